@@ -1,0 +1,299 @@
+// C-ABI entry points of libwushkv: argument checks, arena layout, host-side
+// sequence lengths and kernel launches.  No device memory is allocated here.
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/wushkv.h"
+#include "common.h"
+
+using namespace wkv;
+
+struct wushkv_cache {
+  wushkv_config cfg;
+  wushkv_layout_t lay;
+  uint8_t* arena;
+  std::vector<int32_t> len;  // [n_layers][max_batch]
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+};
+
+static uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+extern "C" wushkv_status wushkv_config_check(const wushkv_config* c) {
+  if (!c) return WUSHKV_EINVAL;
+  if (c->n_layers < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->max_batch < 1 ||
+      c->ctx_cap < 1)
+    return WUSHKV_EINVAL;
+  if (c->n_q_heads % c->n_kv_heads != 0) return WUSHKV_EINVAL;
+  if (c->sink < 0 || c->recent < 0 || c->flush < 1) return WUSHKV_EINVAL;
+  if (!(c->p_lo >= 0.0 && c->p_lo < c->p_hi && c->p_hi <= 1.0)) return WUSHKV_EINVAL;
+  if (c->io_dtype != WUSHKV_IO_FP32 && c->io_dtype != WUSHKV_IO_BF16) return WUSHKV_EINVAL;
+  if (c->head_dim != D) return WUSHKV_EUNSUPPORTED;
+  if (c->bits != 2 && c->bits != 4) return WUSHKV_EUNSUPPORTED;
+  {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return WUSHKV_EUNSUPPORTED;
+  }
+  // The window split scores all sink + ring entries in one workgroup.
+  if ((int64_t)c->sink + c->recent + c->flush - 1 > SPLIT_LEN) return WUSHKV_EUNSUPPORTED;
+  return WUSHKV_OK;
+}
+
+extern "C" wushkv_status wushkv_layout(const wushkv_config* c, wushkv_layout_t* out) {
+  wushkv_status st = wushkv_config_check(c);
+  if (st != WUSHKV_OK) return st;
+  if (!out) return WUSHKV_EINVAL;
+  wushkv_layout_t L;
+  memset(&L, 0, sizeof(L));
+  L.code_bytes = D * c->bits / 8;
+  L.vblock = 128 / c->bits;
+  L.ctx_blocks = (c->ctx_cap + L.vblock - 1) / L.vblock;
+  L.cpos = L.ctx_blocks * L.vblock;
+  L.ring_slots = c->recent + c->flush - 1;
+  L.units = c->n_layers * c->max_batch * c->n_kv_heads;
+  const uint64_t u = (uint64_t)L.units;
+  L.bytes_kcode = u * (uint64_t)L.cpos * L.code_bytes;
+  L.bytes_vcode = u * (uint64_t)L.ctx_blocks * D * 16;
+  L.bytes_ksz = u * (uint64_t)L.cpos * 4;
+  L.bytes_vsz = L.bytes_ksz;
+  L.bytes_ksink = u * (uint64_t)c->sink * D * 2;
+  L.bytes_vsink = L.bytes_ksink;
+  L.bytes_kring = u * (uint64_t)L.ring_slots * D * 2;
+  L.bytes_vring = L.bytes_kring;
+  uint64_t off = 0;
+  L.off_kcode = off; off = align256(off + L.bytes_kcode);
+  L.off_vcode = off; off = align256(off + L.bytes_vcode);
+  L.off_ksz = off;   off = align256(off + L.bytes_ksz);
+  L.off_vsz = off;   off = align256(off + L.bytes_vsz);
+  L.off_ksink = off; off = align256(off + L.bytes_ksink);
+  L.off_vsink = off; off = align256(off + L.bytes_vsink);
+  L.off_kring = off; off = align256(off + L.bytes_kring);
+  L.off_vring = off; off = align256(off + L.bytes_vring);
+  L.total_bytes = off;
+  *out = L;
+  return WUSHKV_OK;
+}
+
+extern "C" wushkv_status wushkv_cache_create(const wushkv_config* cfg, void* arena,
+                                             uint64_t arena_bytes, wushkv_cache** out) {
+  if (!out) return WUSHKV_EINVAL;
+  wushkv_layout_t L;
+  wushkv_status st = wushkv_layout(cfg, &L);
+  if (st != WUSHKV_OK) return st;
+  if (!arena || ((uintptr_t)arena & 255) != 0 || arena_bytes < L.total_bytes) return WUSHKV_EINVAL;
+  wushkv_cache* c = new (std::nothrow) wushkv_cache;
+  if (!c) return WUSHKV_EINVAL;
+  c->cfg = *cfg;
+  c->lay = L;
+  c->arena = (uint8_t*)arena;
+  try {
+    c->len.assign((size_t)cfg->n_layers * cfg->max_batch, 0);
+  } catch (...) {
+    delete c;
+    return WUSHKV_EINVAL;
+  }
+  *out = c;
+  return WUSHKV_OK;
+}
+
+extern "C" void wushkv_cache_destroy(wushkv_cache* c) { delete c; }
+
+extern "C" wushkv_status wushkv_reset_seq(wushkv_cache* c, int32_t slot) {
+  if (!c || slot < 0 || slot >= c->cfg.max_batch) return WUSHKV_EINVAL;
+  for (int l = 0; l < c->cfg.n_layers; ++l) c->len[(size_t)l * c->cfg.max_batch + slot] = 0;
+  return WUSHKV_OK;
+}
+
+extern "C" wushkv_status wushkv_get_len(const wushkv_cache* c, int32_t layer, int32_t slot,
+                                        int32_t* len, int32_t* sq) {
+  if (!c || layer < 0 || layer >= c->cfg.n_layers || slot < 0 || slot >= c->cfg.max_batch)
+    return WUSHKV_EINVAL;
+  int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slot];
+  if (len) *len = L;
+  if (sq) *sq = squant_of(L, c->cfg.sink, c->cfg.recent, c->cfg.flush);
+  return WUSHKV_OK;
+}
+
+static Planes planes_of(const wushkv_cache* c) {
+  Planes p;
+  uint8_t* a = c->arena;
+  p.kcode = a + c->lay.off_kcode;
+  p.vcode = a + c->lay.off_vcode;
+  p.ksz = (uint32_t*)(a + c->lay.off_ksz);
+  p.vsz = (uint32_t*)(a + c->lay.off_vsz);
+  p.ksink = (uint16_t*)(a + c->lay.off_ksink);
+  p.vsink = (uint16_t*)(a + c->lay.off_vsink);
+  p.kring = (uint16_t*)(a + c->lay.off_kring);
+  p.vring = (uint16_t*)(a + c->lay.off_vring);
+  return p;
+}
+
+static Geometry geometry_of(const wushkv_cache* c) {
+  Geometry g;
+  g.n_kv = c->cfg.n_kv_heads;
+  g.n_q = c->cfg.n_q_heads;
+  g.G = g.n_q / g.n_kv;
+  g.bits = c->cfg.bits;
+  g.S = c->cfg.sink;
+  g.R = c->cfg.recent;
+  g.F = c->cfg.flush;
+  g.W = c->lay.ring_slots;
+  g.code_bytes = c->lay.code_bytes;
+  g.vblock = c->lay.vblock;
+  g.ctx_blocks = c->lay.ctx_blocks;
+  g.cpos = c->lay.cpos;
+  g.max_batch = c->cfg.max_batch;
+  g.p_lo = c->cfg.p_lo;
+  g.p_hi = c->cfg.p_hi;
+  return g;
+}
+
+// Distinct, in-range slots.
+static bool slots_ok(const wushkv_cache* c, int32_t n_seq, const int32_t* slots) {
+  std::vector<char> seen((size_t)c->cfg.max_batch, 0);
+  for (int i = 0; i < n_seq; ++i) {
+    int s = slots[i];
+    if (s < 0 || s >= c->cfg.max_batch || seen[s]) return false;
+    seen[s] = 1;
+  }
+  return true;
+}
+
+extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                       const int32_t* slots, const int32_t* n_new, const void* k,
+                                       const void* v, const float* tk, void* stream) {
+  if (!c || !slots || !n_new || layer < 0 || layer >= c->cfg.n_layers || n_seq < 0)
+    return WUSHKV_EINVAL;
+  if (n_seq > MAXSEQ) return WUSHKV_EUNSUPPORTED;
+  if (n_seq == 0) return WUSHKV_OK;
+  if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
+  int64_t total = 0;
+  int max_new = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    if (n_new[i] < 0) return WUSHKV_EINVAL;
+    int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
+    if ((int64_t)L + n_new[i] > c->cfg.ctx_cap) return WUSHKV_ECAPACITY;
+    total += n_new[i];
+    if (n_new[i] > max_new) max_new = n_new[i];
+  }
+  if (total > INT32_MAX) return WUSHKV_EINVAL;
+  if (total > 0 && (!k || !v || !tk)) return WUSHKV_EINVAL;
+  const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;
+  if (total > 0 && (((uintptr_t)k % esz) || ((uintptr_t)v % esz) || ((uintptr_t)tk % 16)))
+    return WUSHKV_EINVAL;
+  if (total == 0) return WUSHKV_OK;
+
+  AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pl = planes_of(c);
+  a.g = geometry_of(c);
+  a.layer = layer;
+  a.k = k;
+  a.v = v;
+  a.tk = tk;
+  int32_t tok = 0;
+  int max_chunks = 1;
+  for (int i = 0; i < n_seq; ++i) {
+    int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
+    a.s.slot[i] = slots[i];
+    a.s.len0[i] = L;
+    a.s.n_new[i] = n_new[i];
+    a.s.tok0[i] = tok;
+    tok += n_new[i];
+    int base = L - L % CHUNK;
+    int chunks = (L + n_new[i] - base + CHUNK - 1) / CHUNK;
+    if (chunks > max_chunks) max_chunks = chunks;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int io_bf16 = c->cfg.io_dtype == WUSHKV_IO_BF16;
+  hipError_t e;
+  if (max_new <= 16) {
+    // Few new positions: one workgroup per (sequence, KV head) quantizes the
+    // entries leaving the ring, then places the new ones.
+    a.mode = APPEND_FUSED;
+    e = launch_append(a, io_bf16, 1, n_seq, st);
+  } else {
+    // Ring entries leaving the window are read before any new entry is
+    // written (a new position may reuse the slot of an evicted one).
+    a.mode = APPEND_EVICT;
+    e = launch_append(a, io_bf16, 1, n_seq, st);
+    if (e == hipSuccess) {
+      a.mode = APPEND_CHUNKED;
+      e = launch_append(a, io_bf16, max_chunks, n_seq, st);
+    }
+  }
+  if (e != hipSuccess) return WUSHKV_EDEVICE;
+  for (int i = 0; i < n_seq; ++i) c->len[(size_t)layer * c->cfg.max_batch + slots[i]] += n_new[i];
+  return WUSHKV_OK;
+}
+
+static int max_splits_of(const wushkv_cache* c) {
+  return (c->lay.cpos + SPLIT_LEN - 1) / SPLIT_LEN;
+}
+
+extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t n_seq) {
+  if (!c || n_seq < 0) return 0;
+  uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
+  uint64_t q = nq * QS * 4;
+  uint64_t p = nq * (uint64_t)(max_splits_of(c) + 1) * PS * 4;
+  return align256(q) + align256(p);
+}
+
+extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                            const int32_t* slots, const void* q, const float* tq,
+                                            float* out, void* ws, uint64_t ws_bytes,
+                                            void* stream) {
+  if (!c || !slots || layer < 0 || layer >= c->cfg.n_layers || n_seq < 0) return WUSHKV_EINVAL;
+  if (n_seq > MAXSEQ) return WUSHKV_EUNSUPPORTED;
+  if (n_seq == 0) return WUSHKV_OK;
+  if (!q || !tq || !out || !ws) return WUSHKV_EINVAL;
+  const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;
+  if (((uintptr_t)q % esz) || ((uintptr_t)tq % 16) || ((uintptr_t)out % 16) ||
+      ((uintptr_t)ws % 16))
+    return WUSHKV_EINVAL;
+  if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
+  if (ws_bytes < wushkv_decode_workspace_bytes(c, n_seq)) return WUSHKV_EWORKSPACE;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pl = planes_of(c);
+  a.g = geometry_of(c);
+  a.layer = layer;
+  a.n_seq = n_seq;
+  a.max_splits = max_splits_of(c);
+  a.q = q;
+  a.tq = tq;
+  a.out = out;
+  uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
+  a.wsq = (float*)ws;
+  a.wsp = (float*)((uint8_t*)ws + align256(nq * QS * 4));
+  for (int i = 0; i < n_seq; ++i) {
+    int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
+    if (L < 1) return WUSHKV_EINVAL;
+    a.s.slot[i] = slots[i];
+    a.s.len[i] = L;
+    a.s.squant[i] = squant_of(L, c->cfg.sink, c->cfg.recent, c->cfg.flush);
+  }
+  hipError_t e = launch_decode(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream,
+                               c->ev_start, c->ev_stop);
+  return e == hipSuccess ? WUSHKV_OK : WUSHKV_EDEVICE;
+}
+
+extern "C" wushkv_status wushkv_set_split_events(wushkv_cache* c, void* ev_start, void* ev_stop) {
+  if (!c || (!ev_start) != (!ev_stop)) return WUSHKV_EINVAL;
+  c->ev_start = (hipEvent_t)ev_start;
+  c->ev_stop = (hipEvent_t)ev_stop;
+  return WUSHKV_OK;
+}
+
+extern "C" const char* wushkv_status_str(wushkv_status s) {
+  switch (s) {
+    case WUSHKV_OK: return "ok";
+    case WUSHKV_EINVAL: return "invalid argument";
+    case WUSHKV_ECAPACITY: return "sequence capacity exceeded";
+    case WUSHKV_EWORKSPACE: return "workspace too small";
+    case WUSHKV_EUNSUPPORTED: return "unsupported configuration";
+    case WUSHKV_EDEVICE: return "HIP launch error";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,89 @@
+// Internal definitions shared by the libwushkv kernels and host code.
+// gfx950 (CDNA4) only: wave64, HIP runtime.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr int D = 128;          // head_dim (the only one built)
+constexpr int MAXSEQ = 128;     // sequences per call (kernel-argument tables)
+constexpr int SPLIT_LEN = 1024; // decode split-K chunk (multiple of every vblock)
+constexpr int CHUNK = 256;      // prefill append: positions per workgroup (multiple of vblock)
+constexpr int QS = 132;         // workspace stride of one compensated query: 128 + sigma + pad
+constexpr int PS = 132;         // workspace stride of one split partial: o[128], m, l, pad
+
+// Base addresses of the cache planes (arena + layout offsets).
+struct Planes {
+  uint8_t* kcode;
+  uint8_t* vcode;
+  uint32_t* ksz;   // {binary16 scale | binary16 zero << 16}
+  uint32_t* vsz;
+  uint16_t* ksink;  // bfloat16 bits
+  uint16_t* vsink;
+  uint16_t* kring;
+  uint16_t* vring;
+};
+
+struct Geometry {
+  int n_kv, n_q, G, bits;
+  int S, R, F, W;  // sink, recent, flush, ring slots
+  int code_bytes, vblock, ctx_blocks, cpos, max_batch;
+  double p_lo, p_hi;
+};
+
+// squant(L): end of the quantized region [S, squant) at length L (section 4.4).
+__host__ __device__ inline int squant_of(int L, int S, int R, int F) {
+  int outside = L - R - S;
+  if (outside < 0) outside = 0;
+  return S + F * (outside / F);
+}
+
+struct AppendSeqs {
+  int32_t slot[MAXSEQ];
+  int32_t len0[MAXSEQ];   // length before this call
+  int32_t n_new[MAXSEQ];
+  int32_t tok0[MAXSEQ];   // first row of this sequence in k / v
+};
+
+enum AppendMode : int { APPEND_FUSED = 0, APPEND_EVICT = 1, APPEND_CHUNKED = 2 };
+
+struct AppendArgs {
+  Planes pl;
+  Geometry g;
+  int layer;
+  int mode;
+  const void* k;
+  const void* v;
+  const float* tk;
+  AppendSeqs s;
+};
+
+struct DecodeSeqs {
+  int32_t slot[MAXSEQ];
+  int32_t len[MAXSEQ];
+  int32_t squant[MAXSEQ];
+};
+
+struct DecodeArgs {
+  Planes pl;
+  Geometry g;
+  int layer;
+  int n_seq;
+  int max_splits;  // quantized splits per sequence; index max_splits is the window split
+  const void* q;
+  const float* tq;
+  float* out;
+  float* wsq;  // [n_seq][n_q][QS]
+  float* wsp;  // [n_seq][n_q][max_splits + 1][PS]
+  DecodeSeqs s;
+};
+
+// Host-side launchers (defined in the .hip files); return hipSuccess or the
+// launch error.
+hipError_t launch_append(const AppendArgs& a, int io_bf16, int grid_x, int n_seq, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
+                         hipEvent_t ev_stop);
+
+}  // namespace wkv

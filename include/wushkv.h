@@ -1,0 +1,190 @@
+/*
+ * wushkv.h -- C ABI of libwushkv: the WUSH-KV transformed low-bit KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms",
+ * paper page) stores, per KV head, one cache column per position (section
+ * 4.1).  Keys arrive after RoPE and are multiplied by a fixed d x d key
+ * transform T_K before caching; queries are compensated by T_K^{-T} (section
+ * 4.2, appendix B.1).  Values arrive already in the value transform's basis,
+ * which is folded into the projection weights (section 4.5), so the
+ * attention output also leaves in that basis.  Cached entries outside a fixed
+ * sink window and a rolling recent window (section 4.4) are quantized per
+ * token with percentile clipping and asymmetric affine scaling (section 5.3;
+ * 2^b equally spaced levels, appendix B.3).
+ *
+ * Two operations carry the method: wushkv_append (transform + window
+ * placement + quantize/pack) and wushkv_decode_attn (query compensation +
+ * split-K decode attention over the mixed cache + merge).  Everything else
+ * here is layout, bookkeeping and error reporting.
+ *
+ * Conventions for every call:
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are ordinary process memory.  Nothing is retained after a call
+ *     returns except by wushkv_cache_create (the arena address).
+ *   - The library never allocates device memory.  The caller owns the arena,
+ *     every input/output buffer and the decode workspace.
+ *   - All argument checks happen before any kernel launch; a call that returns
+ *     an error has changed no state (host lengths, device memory).
+ *   - Kernels are enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and run asynchronously; the library does no host
+ *     synchronisation.  One cache must not be used from two streams at once.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef WUSHKV_H
+#define WUSHKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WUSHKV_OK = 0,
+  WUSHKV_EINVAL = 1,       /* null/misaligned pointer, index out of range, duplicate slot, bad config value */
+  WUSHKV_ECAPACITY = 2,    /* an append would make a sequence longer than ctx_cap */
+  WUSHKV_EWORKSPACE = 3,   /* decode workspace smaller than wushkv_decode_workspace_bytes() */
+  WUSHKV_EUNSUPPORTED = 4, /* valid but not built: head_dim != 128, bits not in {2, 4}, too many sequences per call */
+  WUSHKV_EDEVICE = 5       /* the HIP runtime reported an error when launching */
+} wushkv_status;
+
+enum { WUSHKV_IO_FP32 = 0, WUSHKV_IO_BF16 = 1 };
+
+/* Largest number of sequences one append or decode call may name. */
+#define WUSHKV_MAX_SEQ_PER_CALL 128
+
+/* Fixed at cache creation. */
+typedef struct {
+  int32_t n_layers;     /* attention modules sharing this cache object            */
+  int32_t n_q_heads;    /* query heads; query head j reads KV head j / (n_q/n_kv) */
+  int32_t n_kv_heads;   /* KV heads (n_q_heads % n_kv_heads == 0)                 */
+  int32_t head_dim;     /* d; must be 128                                         */
+  int32_t bits;         /* code width b: 2 or 4                                   */
+  int32_t sink;         /* S_sink >= 0: first positions kept in bfloat16          */
+  int32_t recent;       /* S_keep >= 0: newest positions kept in bfloat16         */
+  int32_t flush;        /* S_flush >= 1: quantize in multiples of this            */
+  double p_lo, p_hi;    /* clip percentiles, 0 <= p_lo < p_hi <= 1 (e.g. .01/.99) */
+  int32_t max_batch;    /* sequence slots                                         */
+  int32_t ctx_cap;      /* positions per slot (>= 1)                              */
+  int32_t io_dtype;     /* WUSHKV_IO_FP32 or WUSHKV_IO_BF16 for k, v, q inputs   */
+} wushkv_config;
+
+/*
+ * Device layout of one cache.  All planes live in one caller-allocated
+ * arena; offsets are bytes from the arena start, each a multiple of 256.
+ * A "unit" is one (layer, slot, KV head): u = (layer * max_batch + slot) *
+ * n_kv_heads + head.  Positions p are absolute (0-based) in the sequence.
+ *
+ *   kcode  uint8  [unit][cpos][code_bytes]         token-major key codes;
+ *                 element i of position p sits in byte (i*bits)/8 at bit
+ *                 (i*bits)%8 of that position's code_bytes = d*bits/8 bytes.
+ *   vcode  uint8  [unit][ctx_blocks][d][16]        value codes, dim-major per
+ *                 block of vblock = 128/bits positions: element i of position
+ *                 p sits in row i of block p/vblock, byte ((p%vblock)*bits)/8,
+ *                 bit ((p%vblock)*bits)%8.
+ *   ksz,vsz uint16[unit][cpos][2]                  binary16 {scale, zero} of
+ *                 the key / value group of each quantized position.
+ *   ksink,vsink bfloat16 [unit][sink][d]           positions [0, sink).
+ *   kring,vring bfloat16 [unit][ring_slots][d]     recent window; position p
+ *                 (p >= sink) lives in slot (p - sink) % ring_slots.
+ *
+ * Keys in the cache are in the transformed basis (T_K k, rounded to bfloat16
+ * before quantization); values are as given (rounded to bfloat16).  After a
+ * sequence reaches length L, positions [sink, squant(L)) are quantized and
+ * [squant(L), L) are in the ring, with squant(L) = sink + flush *
+ * floor(max(0, L - recent - sink) / flush) (section 4.4; S_quant starts at
+ * sink for an empty cache).  Entries of a code plane at positions that are not
+ * quantized hold unspecified bits.
+ */
+typedef struct {
+  uint64_t total_bytes;
+  uint64_t off_kcode, off_vcode, off_ksz, off_vsz, off_ksink, off_vsink, off_kring, off_vring;
+  uint64_t bytes_kcode, bytes_vcode, bytes_ksz, bytes_vsz, bytes_ksink, bytes_vsink,
+      bytes_kring, bytes_vring;
+  int32_t code_bytes;   /* d * bits / 8 per position per K (or V)   */
+  int32_t vblock;       /* positions per value-code block = 128/bits */
+  int32_t ctx_blocks;   /* ceil(ctx_cap / vblock)                    */
+  int32_t cpos;         /* ctx_blocks * vblock                       */
+  int32_t ring_slots;   /* recent + flush - 1                        */
+  int32_t units;        /* n_layers * max_batch * n_kv_heads         */
+} wushkv_layout_t;
+
+typedef struct wushkv_cache wushkv_cache;
+
+/* Check a config.  Host only.  EINVAL / EUNSUPPORTED as described above. */
+wushkv_status wushkv_config_check(const wushkv_config* cfg);
+
+/* Fill *out with the arena layout for cfg (host only, no device calls). */
+wushkv_status wushkv_layout(const wushkv_config* cfg, wushkv_layout_t* out);
+
+/* Bind a cache descriptor to a device arena of at least layout.total_bytes,
+ * 256-byte aligned (EINVAL otherwise).  The arena needs no initialisation.
+ * All sequence lengths start at 0.  *out is owned by the caller and released
+ * with wushkv_cache_destroy; the arena stays the caller's. */
+wushkv_status wushkv_cache_create(const wushkv_config* cfg, void* arena, uint64_t arena_bytes,
+                                  wushkv_cache** out);
+void wushkv_cache_destroy(wushkv_cache* cache);
+
+/* Forget slot's contents in every layer (length 0; S_quant back to sink). */
+wushkv_status wushkv_reset_seq(wushkv_cache* cache, int32_t slot);
+
+/* Host-side length L of (layer, slot) and its quantized-region end squant(L). */
+wushkv_status wushkv_get_len(const wushkv_cache* cache, int32_t layer, int32_t slot,
+                             int32_t* len, int32_t* squant);
+
+/*
+ * Append n_new[i] >= 0 positions to sequence slots[i] (distinct, i < n_seq <=
+ * WUSHKV_MAX_SEQ_PER_CALL) of one layer.  Section 4.4: new entries are first
+ * rounded to bfloat16; positions that leave the recent window (old ring
+ * entries or new ones) are quantized, in the order they become eligible.
+ *
+ *   k   device, io_dtype [sum(n_new)][n_kv_heads][head_dim]: post-RoPE keys,
+ *       the sequences' tokens concatenated in the order of slots[].
+ *   v   device, same shape: values, already in the value transform's basis.
+ *   tk  device, float32 [n_kv_heads][d][d] row-major: k'_i = sum_j tk[i][j] k_j
+ *       (the key transform T_K of this layer).
+ * The transform is evaluated to fp64 accuracy before rounding to bfloat16.
+ * ECAPACITY if any L + n_new > ctx_cap.  Updates the host lengths on success.
+ */
+wushkv_status wushkv_append(wushkv_cache* cache, int32_t layer, int32_t n_seq, const int32_t* slots,
+                            const int32_t* n_new, const void* k, const void* v, const float* tk,
+                            void* stream);
+
+/* Bytes of device workspace wushkv_decode_attn needs for n_seq sequences. */
+uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* cache, int32_t n_seq);
+
+/*
+ * One decode query per query head for each of n_seq sequences (distinct
+ * slots, each with length >= 1) of one layer, attending to all L cached
+ * positions of its sequence (section 4.1, GQA: query head j reads KV head
+ * j / (n_q/n_kv); the newest position is in the cache, so no mask applies).
+ *
+ *   q    device, io_dtype [n_seq][n_q_heads][d]: post-RoPE, uncompensated.
+ *   tq   device, float32 [n_kv_heads][d][d] row-major, = T_K^{-T}:
+ *        q'_i = sum_j tq[i][j] q_j.
+ *   out  device, float32 [n_seq][n_q_heads][d]: softmax(q'.k / sqrt(d)) v over
+ *        the cache, in the value-transform basis (window entries read as
+ *        stored bfloat16, quantized entries as z16 + s16 * code).
+ *   ws   device workspace of ws_bytes >= wushkv_decode_workspace_bytes(),
+ *        16-byte aligned; contents on entry are ignored.
+ */
+wushkv_status wushkv_decode_attn(wushkv_cache* cache, int32_t layer, int32_t n_seq,
+                                 const int32_t* slots, const void* q, const float* tq, float* out,
+                                 void* ws, uint64_t ws_bytes, void* stream);
+
+/* Instrumentation, not part of the method.  When ev_start and ev_stop are
+ * hipEvent_t handles (created by the caller), every later wushkv_decode_attn
+ * call on this cache records ev_start on its stream immediately before the
+ * split-K scan kernel and ev_stop immediately after it, so that a caller can
+ * time that kernel alone.  Pass NULL, NULL to stop.  Host only. */
+wushkv_status wushkv_set_split_events(wushkv_cache* cache, void* ev_start, void* ev_stop);
+
+/* Static string for a status code. */
+const char* wushkv_status_str(wushkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WUSHKV_H */

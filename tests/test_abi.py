@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every function include/wushkv.h declares, configs are validated, the
+arena layout reproduces the pages' footprint arithmetic, and invalid calls
+fail before any launch without changing state."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import decode_attention_wushkv_amd as wk
+from decode_attention_wushkv_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(wk.LIB_PATH):
+        build.build()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "wushkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wushkv_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_header_function():
+    names = header_functions()
+    assert set(names) == set(wk.EXPORTS)
+    lib = ctypes.CDLL(wk.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    base = dict(n_layers=32, n_q_heads=32, n_kv_heads=32, bits=2, sink=4, recent=128, flush=1,
+                p_lo=0.01, p_hi=0.99, max_batch=1, ctx_cap=131072, io_dtype=wk.WUSHKV_IO_BF16)
+    base.update(kw)
+    return wk.make_config(**base)
+
+
+def test_footprint_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "footprint.json")))
+    cfg = _cfg(n_layers=g["n_layers"], n_kv_heads=g["n_kv_heads"], n_q_heads=g["n_kv_heads"],
+               ctx_cap=g["context"])
+    lay = wk.wushkv_layout(cfg)
+    # values per token: 2 (K, V) x layers x KV heads x head_dim
+    vals = 2 * cfg.n_layers * cfg.n_kv_heads * cfg.head_dim
+    assert vals == g["values_per_token"]
+    assert vals * 2 == g["fp16_bytes_per_token"]
+    assert vals * 2 * g["context"] == g["fp16_bytes_per_sequence"]
+    # the 2-bit code planes hold exactly 2 bits per cached value
+    assert lay.bytes_kcode + lay.bytes_vcode == g["two_bit_code_bytes_per_sequence"]
+    # scale/zero overhead, reported separately: 4 B per (token, layer, KV head) per K/V
+    assert lay.bytes_ksz + lay.bytes_vsz == 2 * 4 * cfg.n_layers * cfg.n_kv_heads * g["context"]
+    assert lay.bytes_ksz + lay.bytes_vsz == 1 << 30
+    # windows: bf16 sink + ring per unit
+    units = cfg.n_layers * cfg.n_kv_heads
+    assert lay.bytes_ksink == units * 4 * 128 * 2
+    assert lay.bytes_kring == units * 128 * 128 * 2
+    assert lay.total_bytes % 256 == 0
+    for n in ("kcode", "vcode", "ksz", "vsz", "ksink", "vsink", "kring", "vring"):
+        assert getattr(lay, f"off_{n}") % 256 == 0
+
+
+def test_footprint_4bit():
+    lay = wk.wushkv_layout(_cfg(bits=4))
+    assert lay.bytes_kcode + lay.bytes_vcode == 2 * 8589934592
+    assert lay.vblock == 32 and lay.code_bytes == 64
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), wk.WUSHKV_EUNSUPPORTED),
+    (dict(bits=3), wk.WUSHKV_EUNSUPPORTED),
+    (dict(n_q_heads=30, n_kv_heads=8), wk.WUSHKV_EINVAL),
+    (dict(n_q_heads=24, n_kv_heads=8), wk.WUSHKV_EUNSUPPORTED),
+    (dict(p_lo=0.5, p_hi=0.5), wk.WUSHKV_EINVAL),
+    (dict(p_lo=-0.1), wk.WUSHKV_EINVAL),
+    (dict(flush=0), wk.WUSHKV_EINVAL),
+    (dict(recent=-1), wk.WUSHKV_EINVAL),
+    (dict(ctx_cap=0), wk.WUSHKV_EINVAL),
+    (dict(io_dtype=7), wk.WUSHKV_EINVAL),
+    (dict(recent=1100), wk.WUSHKV_EUNSUPPORTED),
+    (dict(), wk.WUSHKV_OK),
+])
+def test_config_check(kw, status):
+    assert wk.wushkv_config_check(_cfg(**kw)) == status
+
+
+FAKE_ARENA = 1 << 40   # an aligned address that is never dereferenced by these host-only calls
+
+
+def _fake_cache(**kw):
+    cfg = _cfg(n_layers=2, n_q_heads=8, n_kv_heads=2, max_batch=4, ctx_cap=100, **kw)
+    lay = wk.wushkv_layout(cfg)
+    return wk.wushkv_cache_create(cfg, FAKE_ARENA, lay.total_bytes), lay
+
+
+def test_cache_create_checks_arena():
+    cfg = _cfg(n_layers=1, max_batch=1, ctx_cap=100)
+    lay = wk.wushkv_layout(cfg)
+    with pytest.raises(wk.WushkvError):
+        wk.wushkv_cache_create(cfg, FAKE_ARENA + 16, lay.total_bytes)
+    with pytest.raises(wk.WushkvError):
+        wk.wushkv_cache_create(cfg, FAKE_ARENA, lay.total_bytes - 1)
+    h = wk.wushkv_cache_create(cfg, FAKE_ARENA, lay.total_bytes)
+    assert wk.wushkv_get_len(h, 0, 0) == (0, 4)
+    wk.wushkv_cache_destroy(h)
+
+
+def test_append_errors_leave_state_unchanged():
+    h, _ = _fake_cache()
+    P = 1 << 41
+    assert wk.wushkv_append(h, 0, [0, 0], [1, 1], P, P, P, check=False) == wk.WUSHKV_EINVAL  # duplicate
+    assert wk.wushkv_append(h, 0, [5], [1], P, P, P, check=False) == wk.WUSHKV_EINVAL        # slot range
+    assert wk.wushkv_append(h, 2, [0], [1], P, P, P, check=False) == wk.WUSHKV_EINVAL        # layer range
+    assert wk.wushkv_append(h, 0, [0], [-1], P, P, P, check=False) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_append(h, 0, [0, 1], [50, 101], P, P, P, check=False) == wk.WUSHKV_ECAPACITY
+    assert wk.wushkv_append(h, 0, [0], [1], 0, P, P, check=False) == wk.WUSHKV_EINVAL        # null k
+    assert wk.wushkv_append(h, 0, [0], [1], P + 1, P, P, check=False) == wk.WUSHKV_EINVAL    # misaligned
+    assert wk.wushkv_append(h, 0, list(range(4)) * 40, [0] * 160, P, P, P, check=False) == \
+        wk.WUSHKV_EUNSUPPORTED
+    assert wk.wushkv_append(h, 0, [0, 1], [0, 0], P, P, P, check=False) == wk.WUSHKV_OK      # no-op
+    for s in range(4):
+        assert wk.wushkv_get_len(h, 0, s) == (0, 4)
+    wk.wushkv_cache_destroy(h)
+
+
+def test_decode_errors():
+    h, _ = _fake_cache()
+    P = 1 << 41
+    need = wk.wushkv_decode_workspace_bytes(h, 2)
+    assert need > 0
+    # empty sequences cannot be decoded
+    assert wk.wushkv_decode_attn(h, 0, [0], P, P, P, P, need, check=False) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_decode_attn(h, 0, [0, 1], P, P, P, P, need - 1, check=False) == wk.WUSHKV_EWORKSPACE
+    assert wk.wushkv_decode_attn(h, 0, [1, 1], P, P, P, P, need, check=False) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_decode_attn(h, 0, [0], 0, P, P, P, need, check=False) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_decode_attn(h, 0, [0], P, P, P + 4, P, need, check=False) == wk.WUSHKV_EINVAL
+    wk.wushkv_cache_destroy(h)
+
+
+def test_reset_and_status_strings():
+    h, _ = _fake_cache()
+    wk.wushkv_reset_seq(h, 3)
+    with pytest.raises(wk.WushkvError):
+        wk.wushkv_reset_seq(h, 4)
+    wk.wushkv_cache_destroy(h)
+    for s in range(6):
+        assert wk.wushkv_status_str(s)
+    assert wk.wushkv_status_str(99) == "unknown status"

@@ -1,0 +1,292 @@
+"""GPU parity of libwushkv against the fp64 CPU oracle (small and medium sizes).
+
+Stages, each with its own tolerance:
+  T  transformed keys as stored in the bfloat16 windows: bit-exact except where
+     the oracle flags the bfloat16 rounding of T k as undecided by fp64.
+  Q  codes: >= 99.99 % equal and every mismatch one level off with the
+     oracle's code coordinate within 1e-5 of a rounding boundary; binary16
+     scale and zero within 1e-6 relative.
+  A  attention output per (sequence, query head):
+     max_i |o_i - r_i| <= 2e-3 * max_i |r_i|.
+All inputs come from the seeded synthetic generator; nothing the oracle reads
+comes from the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_wushkv_amd import synth
+from decode_attention_wushkv_amd.device_cache import DeviceCache
+
+from cachepack import read_unit, write_unit
+
+pytestmark = pytest.mark.gpu
+
+ATOL_REL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_attention_wushkv_amd import build
+    if build.is_stale():
+        build.build()
+    torch.cuda.set_device(0)
+
+
+def _cache(w: synth.Workload, *, bits=None, S=None, R=None, F=None, max_batch=None, ctx_cap=None,
+           p_lo=None, p_hi=None, n_layers=None):
+    return DeviceCache(n_layers=n_layers or 1, n_q_heads=w.n_q, n_kv_heads=w.n_kv,
+                       bits=bits or w.bits[0], sink=w.sink if S is None else S,
+                       recent=w.recent if R is None else R, flush=F or w.flush,
+                       p_lo=p_lo or w.p_lo, p_hi=p_hi or w.p_hi,
+                       max_batch=max_batch or w.batch, ctx_cap=ctx_cap or max(w.lengths()),
+                       io_dtype=w.torch_io, device="cuda")
+
+
+def _inputs(w, layer, seq, L):
+    k, v = synth.keys_values(w, layer, seq, 0, L)
+    return k, v
+
+
+def _append_all(dc, layer, slots, ks, vs, T, plan):
+    """Append each sequence's tokens following plan = list of chunk sizes
+    (applied to every sequence in the call, clipped to what remains)."""
+    pos = [0] * len(slots)
+    tk = torch.from_numpy(T).cuda()
+    for n in plan:
+        nn = [min(n, ks[i].shape[0] - pos[i]) for i in range(len(slots))]
+        if sum(nn) == 0:
+            continue
+        kk = torch.cat([ks[i][pos[i]:pos[i] + nn[i]] for i in range(len(slots))]).cuda().contiguous()
+        vv = torch.cat([vs[i][pos[i]:pos[i] + nn[i]] for i in range(len(slots))]).cuda().contiguous()
+        dc.append(layer, slots, nn, kk, vv, tk)
+        pos = [p + n_ for p, n_ in zip(pos, nn)]
+    assert all(p == k.shape[0] for p, k in zip(pos, ks))
+
+
+def _oracle_units(w, ks, vs, T, dc):
+    c = dc.cfg
+    units = {}
+    for si, (k, v) in enumerate(zip(ks, vs)):
+        for h in range(w.n_kv):
+            units[(si, h)] = oracle.cache_unit(
+                k[:, h].double().numpy(), v[:, h].double().numpy(), T[h].astype(np.float64),
+                S=c.sink, R=c.recent, F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi)
+    return units
+
+
+def check_windows(gpu, orc):
+    """T stage: bf16 window entries equal the oracle's rounding of T k (and of v)."""
+    L, S, sq = orc["L"], orc["S"], orc["squant"]
+    win = np.r_[np.arange(0, min(S, L)), np.arange(max(sq, S), L)].astype(int)
+    if win.size == 0:
+        return 0
+    amb = orc["k_ambiguous"][win]
+    gk, ok_ = gpu["kwin"][win], orc["k_bf16"][win]
+    assert np.array_equal(gk[~amb], ok_[~amb]), "window keys differ from bf16(T k)"
+    assert np.array_equal(gpu["vwin"][win], orc["v_bf16"][win]), "window values differ"
+    return int(amb.sum())
+
+
+def check_codes(gpu, orc, bits):
+    """Q stage on every quantized position (groups whose transformed keys hold an
+    undecided bf16 rounding are compared on values only)."""
+    q = np.asarray(orc["qpos"], dtype=int)
+    if q.size == 0:
+        return dict(n=0)
+    stats = {}
+    for kind in ("k", "v"):
+        gc = gpu[f"{kind}codes"][q].astype(int)
+        oc = orc[f"{kind}codes"][q].astype(int)
+        u = orc[f"{kind}u"][q]
+        gs, gz = gpu[f"{kind}s16"][q], gpu[f"{kind}z16"][q]
+        os_, oz = orc[f"{kind}s16"][q], orc[f"{kind}z16"][q]
+        if kind == "k":
+            skip = orc["k_ambiguous"][q].any(axis=1)
+        else:
+            skip = np.zeros(q.size, dtype=bool)
+        keep = ~skip
+        rel = lambda a, b: np.abs(a - b) / np.maximum(np.abs(b), 1e-30)
+        assert np.all(rel(gs[keep], os_[keep]) <= 1e-6), f"{kind} scale mismatch"
+        assert np.all(np.abs(gz[keep] - oz[keep]) <= 1e-6 * np.abs(oz[keep])), f"{kind} zero mismatch"
+        mism = (gc != oc) & keep[:, None]
+        frac = mism.sum() / max(1, keep.sum() * 128)
+        assert frac <= 1e-4, f"{kind} code mismatch fraction {frac}"
+        if mism.any():
+            assert np.all(np.abs(gc[mism] - oc[mism]) == 1)
+            uu = u[mism]
+            assert np.all(np.abs(uu - np.floor(uu) - 0.5) <= 1e-5), "mismatch off a boundary"
+        stats[kind] = dict(mismatch=int(mism.sum()), skipped_groups=int(skip.sum()))
+    return stats
+
+
+def check_attention(got, ref):
+    for j in range(ref.shape[0]):
+        err = np.max(np.abs(got[j] - ref[j]))
+        assert err <= ATOL_REL * np.max(np.abs(ref[j])), (j, err, np.max(np.abs(ref[j])))
+
+
+def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None, lengths=None,
+             check_attn=True):
+    lengths = lengths or w.lengths()
+    dc = _cache(w, bits=bits, S=S, R=R, F=F, p_lo=p_lo, p_hi=p_hi, max_batch=len(lengths),
+                ctx_cap=max(lengths))
+    T, Tq = synth.transforms(w, 0)
+    ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
+    slots = list(range(len(lengths)))
+    _append_all(dc, 0, slots, ks, vs, T, plan)
+    torch.cuda.synchronize()
+    units = _oracle_units(w, ks, vs, T, dc)
+    for (si, h), orc in units.items():
+        assert dc.get_len(0, si) == (orc["L"], orc["squant"])
+        gpu = read_unit(dc, 0, si, h, orc["L"])
+        check_windows(gpu, orc)
+        check_codes(gpu, orc, dc.cfg.bits)
+    if not check_attn:
+        return dc
+    q = synth.queries(w, 0, 0, len(lengths))
+    out = dc.decode_attn(0, slots, q.cuda(), torch.from_numpy(Tq).cuda()).cpu().numpy()
+    for si in range(len(lengths)):
+        K = np.stack([oracle.readback(units[(si, h)])[0] for h in range(w.n_kv)])
+        V = np.stack([oracle.readback(units[(si, h)])[1] for h in range(w.n_kv)])
+        qc = np.concatenate([oracle.compensate(T[h].astype(np.float64),
+                                               q[si, h * w.group:(h + 1) * w.group].double().numpy())
+                             for h in range(w.n_kv)])
+        ref = oracle.attention(qc, K, V)
+        check_attention(out[si], ref)
+    return dc
+
+
+# ------------------------------------------------------------------ tests
+
+def test_cfg0_prefill_then_decode_steps():
+    """1 layer, 1 KV head, 4 query heads, fp32 io, 1024 positions: a prefill of
+    1000 positions then 24 one-token appends (ring evictions each step)."""
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [1000] + [1] * 24)
+
+
+def test_cfg0_token_by_token_small():
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [1] * 300, lengths=[300])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_cfg0_bits(bits):
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [700, 5, 300, 19], bits=bits)
+
+
+def test_transform_stage_nothing_quantized():
+    """T stage: with S + R >= L every entry stays in bfloat16."""
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [999, 1], R=1000, lengths=[1000])
+
+
+def test_cfg1_llama_layer_32k():
+    """32 query / 8 KV heads, bf16, 32768 positions: prefill 32767 + one decode
+    append, full parity on all 8 KV heads."""
+    w = synth.WORKLOADS[1]
+    _run_e2e(w, [32767, 1])
+
+
+def test_prefill_equals_token_by_token():
+    """Section 4.4's state depends only on the length: a single prefill and a
+    ragged sequence of appends give bit-identical caches."""
+    w = synth.WORKLOADS[1]
+    L = 1500
+    dc = _cache(w, max_batch=2, ctx_cap=L)
+    T, _ = synth.transforms(w, 0)
+    k, v = _inputs(w, 0, 0, L)
+    tk = torch.from_numpy(T).cuda()
+    dc.append(0, [0], [L], k.cuda(), v.cuda(), tk)
+    pos = 0
+    for n in [1, 3, 17, 300, 1, 1, 64, 600, 1, 2, 255, 129, 130]:
+        n = min(n, L - pos)
+        dc.append(0, [1], [n], k[pos:pos + n].cuda().contiguous(), v[pos:pos + n].cuda().contiguous(), tk)
+        pos += n
+    if pos < L:
+        dc.append(0, [1], [L - pos], k[pos:].cuda().contiguous(), v[pos:].cuda().contiguous(), tk)
+    torch.cuda.synchronize()
+    for h in range(w.n_kv):
+        a = read_unit(dc, 0, 0, h, L)
+        b = read_unit(dc, 0, 1, h, L)
+        sq = a["squant"]
+        for key in ("kcodes", "vcodes"):
+            assert np.array_equal(a[key][4:sq], b[key][4:sq])
+        for key in ("ks16", "kz16", "vs16", "vz16"):
+            assert np.array_equal(a[key][4:sq], b[key][4:sq])
+        for key in ("kwin", "vwin"):
+            assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
+
+
+def test_ragged_batch_gqa():
+    """Three sequences of different lengths in one call; a zero-length append
+    for one of them mid-way."""
+    w = synth.WORKLOADS[1]
+    _run_e2e(w, [700, 3, 1, 1, 600, 1], lengths=[1310, 2, 907])
+
+
+@pytest.mark.parametrize("S,R,F", [(0, 32, 1), (4, 0, 1), (16, 128, 16), (1, 5, 3)])
+def test_window_variants(S, R, F):
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [513, 1, 1, 70, 1], S=S, R=R, F=F, lengths=[586])
+
+
+def test_short_sequences_sink_only():
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [1, 1, 1], lengths=[3])
+
+
+def test_other_percentiles():
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [600], p_lo=0.05, p_hi=0.9, lengths=[600])
+
+
+@pytest.mark.parametrize("bits,G,L", [(2, 1, 3001), (2, 4, 2048), (4, 8, 1500), (4, 2, 5),
+                                      (2, 8, 1027)])
+def test_decode_on_identical_contents(bits, G, L):
+    """Decode attention alone: arbitrary stored contents written into the arena
+    (codes, binary16 scale/zero, bfloat16 windows) are read identically by the
+    GPU and by the oracle."""
+    n_kv = 2
+    w = synth.Workload(9, "decode-only", 1, n_kv * G, n_kv, 1, L, (bits,), 4, 64, 1, 0.01, 0.99, "bf16")
+    dc = _cache(w, ctx_cap=L)
+    T, Tq = synth.transforms(w, 0)
+    k, v = _inputs(w, 0, 0, L)
+    dc.append(0, [0], [L], k.cuda(), v.cuda(), torch.from_numpy(T).cuda())   # sets the length
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + bits + G)
+    K, V = [], []
+    for h in range(n_kv):
+        cont = synth.random_cache_contents(rng, L, bits)
+        write_unit(dc, 0, 0, h, L, cont)
+        sq = dc.get_len(0, 0)[1]
+        Kh = cont["k_bf16"].astype(np.float64).copy()
+        Vh = cont["v_bf16"].astype(np.float64).copy()
+        qp = np.arange(4, sq)
+        Kh[qp] = oracle.dequantize(cont["kcodes"][qp], cont["ks16"][qp], cont["kz16"][qp])
+        Vh[qp] = oracle.dequantize(cont["vcodes"][qp], cont["vs16"][qp], cont["vz16"][qp])
+        K.append(Kh)
+        V.append(Vh)
+    torch.cuda.synchronize()
+    q = synth.queries(w, 0, 0, 1)
+    out = dc.decode_attn(0, [0], q.cuda(), torch.from_numpy(Tq).cuda()).cpu().numpy()
+    qc = np.concatenate([oracle.compensate(T[h].astype(np.float64), q[0, h * G:(h + 1) * G].double().numpy())
+                         for h in range(n_kv)])
+    ref = oracle.attention(qc, np.stack(K), np.stack(V))
+    check_attention(out[0], ref)
+
+
+def test_decode_twice_bitwise_deterministic():
+    w = synth.WORKLOADS[0]
+    dc = _run_e2e(w, [1024], check_attn=False)
+    _, Tq = synth.transforms(w, 0)
+    q = synth.queries(w, 0, 0, 1).cuda()
+    tq = torch.from_numpy(Tq).cuda()
+    a = dc.decode_attn(0, [0], q, tq).clone()
+    b = dc.decode_attn(0, [0], q, tq).clone()
+    assert torch.equal(a, b)
