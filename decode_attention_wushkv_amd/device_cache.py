@@ -22,7 +22,10 @@ class DeviceCache:
                                bits=bits, sink=sink, recent=recent, flush=flush, p_lo=p_lo,
                                p_hi=p_hi, max_batch=max_batch, ctx_cap=ctx_cap, io_dtype=io)
         self.layout = wushkv_layout(self.cfg)
-        self.device = torch.device(device)
+        device = torch.device(device)
+        if device.type == "cuda" and device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = device
         self.arena = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=self.device)
         self.handle = wushkv_cache_create(self.cfg, self.arena.data_ptr(), self.layout.total_bytes)
         self._ws = None

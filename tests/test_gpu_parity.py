@@ -227,7 +227,7 @@ def test_ragged_batch_gqa():
     """Three sequences of different lengths in one call; a zero-length append
     for one of them mid-way."""
     w = synth.WORKLOADS[1]
-    _run_e2e(w, [700, 3, 1, 1, 600, 1], lengths=[1310, 2, 907])
+    _run_e2e(w, [700, 3, 1, 1, 600, 5], lengths=[1310, 2, 907])
 
 
 @pytest.mark.parametrize("S,R,F", [(0, 32, 1), (4, 0, 1), (16, 128, 16), (1, 5, 3)])
