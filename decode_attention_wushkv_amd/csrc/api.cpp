@@ -36,7 +36,7 @@ extern "C" wushkv_status wushkv_config_check(const wushkv_config* c) {
     if (G != 1 && G != 2 && G != 4 && G != 8) return WUSHKV_EUNSUPPORTED;
   }
   // The window split scores all sink + ring entries in one workgroup.
-  if ((int64_t)c->sink + c->recent + c->flush - 1 > SPLIT_LEN) return WUSHKV_EUNSUPPORTED;
+  if ((int64_t)c->sink + c->recent + c->flush - 1 > WINDOW_MAX) return WUSHKV_EUNSUPPORTED;
   return WUSHKV_OK;
 }
 
@@ -228,15 +228,11 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
   return WUSHKV_OK;
 }
 
-static int max_splits_of(const wushkv_cache* c) {
-  return (c->lay.cpos + SPLIT_LEN - 1) / SPLIT_LEN;
-}
-
 extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t n_seq) {
   if (!c || n_seq < 0) return 0;
   uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
   uint64_t q = nq * QS * 4;
-  uint64_t p = nq * (uint64_t)(max_splits_of(c) + 1) * PS * 4;
+  uint64_t p = nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4;
   return align256(q) + align256(p);
 }
 
@@ -260,20 +256,30 @@ extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int3
   a.g = geometry_of(c);
   a.layer = layer;
   a.n_seq = n_seq;
-  a.max_splits = max_splits_of(c);
   a.q = q;
   a.tq = tq;
   a.out = out;
   uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
   a.wsq = (float*)ws;
   a.wsp = (float*)((uint8_t*)ws + align256(nq * QS * 4));
+  const int sl = sub_len(c->cfg.bits);
+  int max_sub = 0;
   for (int i = 0; i < n_seq; ++i) {
     int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
     if (L < 1) return WUSHKV_EINVAL;
     a.s.slot[i] = slots[i];
     a.s.len[i] = L;
     a.s.squant[i] = squant_of(L, c->cfg.sink, c->cfg.recent, c->cfg.flush);
+    const int sq = a.s.squant[i];
+    const int nsub = sq > c->cfg.sink ? (sq + sl - 1) / sl - c->cfg.sink / sl : 0;
+    if (nsub > max_sub) max_sub = nsub;
   }
+  // workgroups per (sequence, KV head): at least one sub-chunk per wave, at
+  // most what fills the GPU once (decided in the launcher), capped by the
+  // workspace bound
+  int cap = max_chunks(n_seq, c->cfg.n_kv_heads);
+  int need = (max_sub + 3) / 4;
+  a.n_splits = need < cap ? need : cap;
   hipError_t e = launch_decode(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream,
                                c->ev_start, c->ev_stop);
   return e == hipSuccess ? WUSHKV_OK : WUSHKV_EDEVICE;

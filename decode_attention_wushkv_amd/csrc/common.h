@@ -9,10 +9,37 @@ namespace wkv {
 
 constexpr int D = 128;          // head_dim (the only one built)
 constexpr int MAXSEQ = 128;     // sequences per call (kernel-argument tables)
-constexpr int SPLIT_LEN = 1024; // decode split-K chunk (multiple of every vblock)
-constexpr int CHUNK = 256;      // prefill append: positions per workgroup (multiple of vblock)
-constexpr int QS = 132;         // workspace stride of one compensated query: 128 + sigma + pad
-constexpr int PS = 132;         // workspace stride of one split partial: o[128], m, l, pad
+constexpr int WINDOW_MAX = 1024; // sink + ring entries scored by one workgroup
+constexpr int CHUNK = 256;       // prefill append: positions per workgroup (multiple of vblock)
+
+// Decode sub-chunk of one wave: 128 positions at 2 bits, 64 at 4 bits (equal
+// code bytes; a multiple of the value-code block).
+__host__ __device__ constexpr int sub_len(int bits) { return 256 / bits; }
+// Upper bound on workgroups per (sequence, KV head) in one decode call (the
+// host picks the actual count from the GPU's occupancy); sizes the workspace.
+__host__ __device__ inline int max_chunks(int n_seq, int n_kv) {
+  int u = n_seq * n_kv;
+  int c = (4096 + u - 1) / u;
+  return c < 64 ? c : 64;
+}
+
+// Fixed-point precision of the decode dot products: the compensated query
+// is held as QDIG signed base-16 digits and the softmax weights of a
+// 128-position sub-chunk as WDIG unsigned ones (16 bits each).
+constexpr int QDIG = 4;
+constexpr int WDIG = 4;
+constexpr int DIGP = 8;  // digit words are padded to 8 per (dimension group) for 16-byte loads
+
+// Workspace record of one compensated query head (32-bit words):
+//   [0, 128)  q' * log2(e) / sqrt(d)            (float)
+//   128       sigma = sum_i q'_i (same scale)   (float)
+//   129       1 / S_q: q'_i ~= qi_i / S_q       (float)
+//   130, 131  sum of qi over dims [0,64), [64,128) (int)
+//   [136, 264) qi in QDIG balanced base-16 digits, packed as signed nibbles
+//             for v_dot8: 16 groups of 8 dimensions x DIGP words
+constexpr int QOFF_SIGMA = 128, QOFF_INVS = 129, QOFF_QSUM = 130, QOFF_LIMB = 136;
+constexpr int QS = QOFF_LIMB + 16 * DIGP;
+constexpr int PS = 132;          // workspace stride of one split partial: o[128], m, l, pad
 
 // Base addresses of the cache planes (arena + layout offsets).
 struct Planes {
@@ -71,19 +98,19 @@ struct DecodeArgs {
   Geometry g;
   int layer;
   int n_seq;
-  int max_splits;  // quantized splits per sequence; index max_splits is the window split
+  int n_splits;  // workgroups over the quantized region; block x == n_splits is the window
   const void* q;
   const float* tq;
   float* out;
-  float* wsq;  // [n_seq][n_q][QS]
-  float* wsp;  // [n_seq][n_q][max_splits + 1][PS]
+  float* wsq;     // [n_seq][n_q][QS]
+  float* wsp;     // [n_seq][n_q][n_splits + 1][PS]
   DecodeSeqs s;
 };
 
 // Host-side launchers (defined in the .hip files); return hipSuccess or the
 // launch error.
 hipError_t launch_append(const AppendArgs& a, int io_bf16, int grid_x, int n_seq, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
+hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 
 }  // namespace wkv
