@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--bits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this size first (hardware-counter "
+                         "calibration: bytes fetched/written by a copy of known size)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path is a per-GPU "
@@ -114,6 +117,15 @@ def main():
     dc = DeviceCache(n_layers=w.n_layers, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits, sink=S,
                      recent=R, flush=F, p_lo=w.p_lo, p_hi=w.p_hi, max_batch=B,
                      ctx_cap=max(targets), io_dtype=w.torch_io, device=dev)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- build the cache through the library (prefill appends), layer by layer
     t_build = time.perf_counter()

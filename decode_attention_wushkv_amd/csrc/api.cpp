@@ -48,8 +48,9 @@ extern "C" wushkv_status wushkv_layout(const wushkv_config* c, wushkv_layout_t* 
   memset(&L, 0, sizeof(L));
   L.code_bytes = D * c->bits / 8;
   L.vblock = 128 / c->bits;
-  L.ctx_blocks = (c->ctx_cap + L.vblock - 1) / L.vblock;
-  L.cpos = L.ctx_blocks * L.vblock;
+  // positions per unit: ctx_cap rounded up to 128 (whole decode sub-chunks)
+  L.cpos = (c->ctx_cap + 127) / 128 * 128;
+  L.ctx_blocks = L.cpos / L.vblock;
   L.ring_slots = c->recent + c->flush - 1;
   L.units = c->n_layers * c->max_batch * c->n_kv_heads;
   const uint64_t u = (uint64_t)L.units;
@@ -231,9 +232,7 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
 extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t n_seq) {
   if (!c || n_seq < 0) return 0;
   uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
-  uint64_t q = nq * QS * 4;
-  uint64_t p = nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4;
-  return align256(q) + align256(p);
+  return align256(nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4);
 }
 
 extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int32_t n_seq,
@@ -259,9 +258,7 @@ extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int3
   a.q = q;
   a.tq = tq;
   a.out = out;
-  uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
-  a.wsq = (float*)ws;
-  a.wsp = (float*)((uint8_t*)ws + align256(nq * QS * 4));
+  a.wsp = (float*)ws;
   const int sl = sub_len(c->cfg.bits);
   int max_sub = 0;
   for (int i = 0; i < n_seq; ++i) {

@@ -28,17 +28,8 @@ __host__ __device__ inline int max_chunks(int n_seq, int n_kv) {
 // 128-position sub-chunk as WDIG unsigned ones (16 bits each).
 constexpr int QDIG = 4;
 constexpr int WDIG = 4;
-constexpr int DIGP = 8;  // digit words are padded to 8 per (dimension group) for 16-byte loads
+constexpr int DIGP = 8;  // query digit words per group of 8 dimensions (padded for 16-byte loads)
 
-// Workspace record of one compensated query head (32-bit words):
-//   [0, 128)  q' * log2(e) / sqrt(d)            (float)
-//   128       sigma = sum_i q'_i (same scale)   (float)
-//   129       1 / S_q: q'_i ~= qi_i / S_q       (float)
-//   130, 131  sum of qi over dims [0,64), [64,128) (int)
-//   [136, 264) qi in QDIG balanced base-16 digits, packed as signed nibbles
-//             for v_dot8: 16 groups of 8 dimensions x DIGP words
-constexpr int QOFF_SIGMA = 128, QOFF_INVS = 129, QOFF_QSUM = 130, QOFF_LIMB = 136;
-constexpr int QS = QOFF_LIMB + 16 * DIGP;
 constexpr int PS = 132;          // workspace stride of one split partial: o[128], m, l, pad
 
 // Base addresses of the cache planes (arena + layout offsets).
@@ -102,7 +93,6 @@ struct DecodeArgs {
   const void* q;
   const float* tq;
   float* out;
-  float* wsq;     // [n_seq][n_q][QS]
   float* wsp;     // [n_seq][n_q][n_splits + 1][PS]
   DecodeSeqs s;
 };

@@ -3,36 +3,35 @@
 // section 4.2 / appendix B.1 for the T_K^{-T} query compensation, section
 // 4.4 for the full-precision windows, appendix D.1 for the 1/sqrt(d) scale).
 //
-// Three launches per call:
-//   qcomp   one workgroup per (sequence, KV head): q' = T_K^{-T} q for its G
-//           query heads, prescaled by log2(e)/sqrt(d); sigma = sum_i q'_i (the
-//           zero point factors out of a score: q'.(z + s c) = z sigma +
-//           s (q'.c)); q' as a fixed-point vector (QDIG signed base-16
-//           digits) for the integer dot products.
-//   split   one workgroup per (sequence, KV head, chunk of the quantized
-//           region) plus one for the bfloat16 sink + recent entries.
-//             quantized chunk: every thread prefetches its share of the chunk's
-//             key codes, value codes and scale/zero words into registers;
-//             scores q'.c come from v_dot8 (4-bit x 4-bit) on the unpacked
-//             codes and the query digits; the chunk max gives exp2 weights
-//             w_t = p_t s_t, quantized to WDIG base-16 digits against the
-//             chunk's largest value scale; o_i = sum_t w_t c_{t,i} is again
-//             v_dot8 over the dim-major value codes and the weight digits;
-//             o += sum_t p_t z_t.
-//             window chunk: fp32 dot products over bfloat16 rows.
-//           Each wave handles a quarter of its workgroup's chunk with its own
-//           max; the workgroup merges the four and writes (o, m, l) per query
-//           head.
+// Two launches per call:
+//   split   workgroups (4 waves) per (sequence, KV head): n_splits over the
+//           quantized region plus one over the bfloat16 sink + recent entries.
+//           Every workgroup first compensates the G query heads of its KV
+//           head: q' = T_K^{-T} q, prescaled by log2(e)/sqrt(d); sigma =
+//           sum_i q'_i (the zero point factors out of a score:
+//           q'.(z + s c) = z sigma + s (q'.c)); q' also as a 16-bit
+//           fixed-point vector in signed base-16 digits for v_dot8.
+//             quantized workgroups: each wave walks 128-position sub-chunks
+//             (64 at 4 bits) with the next sub-chunk's codes in flight.
+//             Scores q'.c come from v_dot8 (4-bit x 4-bit) on unpacked codes
+//             and the query digits; the sub-chunk max gives exp2 weights
+//             w_t = p_t s_t, quantized to 16 bits against the sub-chunk's
+//             largest one and split into base-16 digit words; o_i =
+//             sum_t w_t c_{t,i} is again v_dot8 over the dim-major value rows
+//             (two dimensions per lane); o += sum_t p_t z_t; an online
+//             softmax in float folds the sub-chunks together.
+//             window workgroup: fp32 dot products over bfloat16 rows.
+//           Each workgroup writes (o, m, l) per query head.
 //   combine one workgroup per (sequence, query head): log-sum-exp merge of the
-//           chunk partials into the fp32 output.
+//           partials into the fp32 output.
 #include "common.h"
 
 namespace wkv {
 namespace {
 
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
-// Largest |q_i| representable by QDIG balanced base-16 digits in [-8, 7].
 constexpr int pow16m1(int n) { return n == 0 ? 0 : 16 * pow16m1(n - 1) + 15; }
+// Largest |q_i| representable by QDIG balanced base-16 digits in [-8, 7].
 constexpr int QMAX = 7 * (pow16m1(QDIG) / 15);
 // Largest softmax-weight code: WDIG unsigned base-16 digits.
 constexpr uint32_t WMAX = (uint32_t)pow16m1(WDIG);
@@ -49,8 +48,8 @@ __device__ __forceinline__ float load_io(const void* base, int64_t idx) {
   return ((const float*)base)[idx];
 }
 
-// Wave-wide sum / max: DPP within rows of 16 lanes, then the four row results
-// read into scalars.
+// Wave-wide sum / max: DPP within rows of 16 lanes, then the four row
+// results read into scalars.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -80,124 +79,14 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+// 2^x for x <= 0 straight from v_exp_f32 (results below 2^-126 may flush to 0,
+// which only drops weights too small to matter).
+__device__ __forceinline__ float exp2_nonpos(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Value of the neighbouring lane (lane ^ 1) via DPP quad_perm [1, 0, 3, 2].
 __device__ __forceinline__ int swap_adjacent(int x) {
   return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
 }
-
-// ---------------------------------------------------------------- qcomp
-
-template <int IO_BF16, int BITS>
-__global__ __launch_bounds__(128) void qcomp_kernel(DecodeArgs a) {
-  __shared__ float qv[8][D];
-  __shared__ float red[2][2];
-  __shared__ int8_t dig[QDIG][D];
-  const int h = blockIdx.x, si = blockIdx.y, i = threadIdx.x;
-  const int G = a.g.G, nq = a.g.n_q;
-  const int lane = i & 63, wv = i >> 6;
-  for (int g = 0; g < G; ++g) qv[g][i] = load_io<IO_BF16>(a.q, ((int64_t)si * nq + h * G + g) * D + i);
-  float trow[D];
-  const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D);
-#pragma unroll
-  for (int c = 0; c < D / 4; ++c) {
-    float4 t4 = tp[c];
-    trow[4 * c] = t4.x;
-    trow[4 * c + 1] = t4.y;
-    trow[4 * c + 2] = t4.z;
-    trow[4 * c + 3] = t4.w;
-  }
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < D; ++j) acc = fmaf(trow[j], qv[g][j], acc);
-    acc *= kLog2eOverSqrtD;
-    float* rec = a.wsq + ((int64_t)si * nq + h * G + g) * QS;
-    uint32_t* reci = (uint32_t*)rec;
-    rec[i] = acc;
-    float s = wave_sum(acc);
-    float mx = wave_max(fabsf(acc));
-    if (lane == 0) {
-      red[wv][0] = s;
-      red[wv][1] = mx;
-    }
-    __syncthreads();
-    const float sigma = red[0][0] + red[1][0];
-    const float maxabs = fmaxf(red[0][1], red[1][1]);
-    const float sq = maxabs > 0.f ? (float)QMAX / maxabs : 1.f;
-    int qi = (int)rintf(acc * sq);
-    qi = qi > QMAX ? QMAX : (qi < -QMAX ? -QMAX : qi);
-    const int qsum = wave_sum_i(qi);
-    // balanced base-16 digits d_k in [-8, 7]: qi = sum_k 16^k d_k
-    int r = qi;
-#pragma unroll
-    for (int k = 0; k < QDIG - 1; ++k) {
-      int d = ((r + 8) & 15) - 8;
-      dig[k][i] = (int8_t)d;
-      r = (r - d) >> 4;
-    }
-    dig[QDIG - 1][i] = (int8_t)r;
-    if (lane == 0) reci[QOFF_QSUM + wv] = (uint32_t)qsum;
-    if (i == 0) {
-      rec[QOFF_SIGMA] = sigma;
-      rec[QOFF_INVS] = 1.f / sq;
-    }
-    __syncthreads();
-    {
-      // Word i of the digit block: group i / DIGP of 8 dimensions, digit
-      // k = i % DIGP; nibble n holds that digit of one dimension of the group.
-      //   2 bits: group = half * 8 + w * 2 + parity, dims 64 half + 16 w + 2 n + parity
-      //   4 bits: group = half * 8 + w,              dims 64 half + 8 w + n
-      const int grp16 = i / DIGP, k = i % DIGP, half = grp16 >> 3;
-      int e0, step;
-      if (BITS == 2) {
-        e0 = 64 * half + 16 * ((grp16 >> 1) & 3) + (grp16 & 1);
-        step = 2;
-      } else {
-        e0 = 64 * half + 8 * (grp16 & 7);
-        step = 1;
-      }
-      uint32_t word = 0;
-      if (k < QDIG)
-#pragma unroll
-        for (int n = 0; n < 8; ++n) word |= ((uint32_t)dig[k][e0 + step * n] & 15u) << (4 * n);
-      reci[QOFF_LIMB + i] = word;
-    }
-    __syncthreads();
-  }
-}
-
-
-// ---------------------------------------------------------------- split
-
-template <int BITS, int G>
-struct SplitCfg {
-  static constexpr int TW = sub_len(BITS);     // positions per wave sub-chunk
-  static constexpr int VB = 128 / BITS;        // positions per value-code block
-  static constexpr int NBW = TW / VB;          // value blocks per sub-chunk (2)
-  static constexpr int CB = 16 * BITS;         // key-code bytes per position
-  static constexpr int ROWS = TW / 32;         // positions per lane pair
-  static constexpr int KQ = CB / 32;           // uint4 per lane (half a position)
-  static constexpr int GS = BITS == 2 ? 16 : 8;  // positions per 32-bit value-row word
-  static constexpr int NG = TW / GS;           // value-row words per sub-chunk (8)
-  static constexpr int WGW = BITS == 2 ? 2 * WDIG : WDIG;  // digit words per row word
-  static constexpr int WGP = (WGW + 3) / 4 * 4;            // ... padded to 16 bytes
-  static constexpr bool QREG = G <= 2;         // query digits held in registers
-  // LDS words
-  static constexpr int QLDS = QREG ? 0 : G * 16 * DIGP;
-  static constexpr int WAVE = G * TW + G * NG * WGP;      // weights + digit words, per wave
-  static constexpr int PART = 4 * G * (D + 2);            // wave partials (o, m, l)
-  static constexpr int QUANT = QLDS + 4 * WAVE + PART;
-  static constexpr int WIN = G * D + G * WINDOW_MAX;
-  static constexpr int UNION = QUANT > WIN ? QUANT : WIN;
-  static constexpr int TOTAL = G * D + 64 + UNION;        // obuf + reductions + union
-};
 
 // Block-wide (256 threads) reductions of NV values per thread (all threads get
 // the results).
@@ -218,6 +107,27 @@ __device__ __forceinline__ void block_reduce(float (&v)[NV], float* red) {
   }
 }
 
+// Block-wide sums of v[0, NV) and maxima of v[NV, 2 NV) in one pass.
+template <int NV>
+__device__ __forceinline__ void block_reduce_sum_max(float (&v)[2 * NV], float* red) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    v[k] = wave_sum(v[k]);
+    v[NV + k] = wave_max(v[NV + k]);
+  }
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < 2 * NV; ++k) red[w * 16 + k] = v[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    v[k] = (red[k] + red[16 + k]) + (red[32 + k] + red[48 + k]);
+    v[NV + k] = fmaxf(fmaxf(red[NV + k], red[16 + NV + k]), fmaxf(red[32 + NV + k], red[48 + NV + k]));
+  }
+}
+
 // Orders this wave's LDS accesses before the following ones (lanes of one
 // wave exchange data through LDS without a workgroup barrier).
 __device__ __forceinline__ void wave_sync() {
@@ -226,8 +136,145 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---------------------------------------------------------------- layout
+
+template <int BITS, int G>
+struct SplitCfg {
+  static constexpr int TW = sub_len(BITS);     // positions per wave sub-chunk
+  static constexpr int VB = 128 / BITS;        // positions per value-code block
+  static constexpr int NBW = TW / VB;          // value blocks per sub-chunk (2)
+  static constexpr int CB = 16 * BITS;         // key-code bytes per position
+  static constexpr int ROWS = TW / 32;         // positions per lane pair
+  static constexpr int KQ = CB / 32;           // uint4 per lane (half a position)
+  static constexpr int GS = BITS == 2 ? 16 : 8;  // positions per 32-bit value-row word
+  static constexpr int NG = TW / GS;           // value-row words per sub-chunk (8)
+  static constexpr int WGW = BITS == 2 ? 2 * WDIG : WDIG;  // digit words per row word
+  static constexpr int WGP = (WGW + 3) / 4 * 4;            // ... padded to 16 bytes
+  static constexpr bool QREG = G <= 2;         // query digits held in registers
+  // LDS (32-bit words).  Persistent part:
+  static constexpr int O_OBUF = 0;                          // [G][D] partial o
+  static constexpr int O_RED = O_OBUF + G * D;              // [64] reductions
+  static constexpr int O_QF = O_RED + 64;                   // [G][D] q' (float)
+  static constexpr int O_QSC = O_QF + G * D;                // [G][4] sigma, 1/S_q, qsum0, qsum1
+  static constexpr int O_QD = O_QSC + G * 4;                // [G][16][DIGP] digit words
+  static constexpr int O_UNION = O_QD + G * 16 * DIGP;
+  // Union: query setup | quantized waves | window.
+  static constexpr int SETUP = G * D + 2 * G * D + QDIG * G * D / 4;   // qv, halves, digits (bytes/4)
+  static constexpr int WAVE = G * TW + G * NG * WGP;                    // per wave
+  static constexpr int QUANT = 4 * WAVE + 4 * G * (D + 2);
+  static constexpr int WIN = G * WINDOW_MAX;
+  static constexpr int U1 = SETUP > QUANT ? SETUP : QUANT;
+  static constexpr int UNION = U1 > WIN ? U1 : WIN;
+  static constexpr int TOTAL = O_UNION + UNION;
+};
+
+// ---------------------------------------------------------------- query
+
+// q' = T_K^{-T} q for the G query heads of KV head h (all 256 threads):
+// float copy, sigma, and the digit words for the integer dot products.
+template <int IO_BF16, int BITS, int G>
+__device__ void compensate_query(const DecodeArgs& a, int h, int si, uint32_t* sm) {
+  using C = SplitCfg<BITS, G>;
+  float* qf = (float*)(sm + C::O_QF);
+  float* qsc = (float*)(sm + C::O_QSC);
+  uint32_t* qdw = sm + C::O_QD;
+  float* red = (float*)(sm + C::O_RED);
+  float* qv = (float*)(sm + C::O_UNION);     // [G][D] raw queries
+  float* hsum = qv + G * D;                  // [2][G][D] half-row sums
+  int8_t* dig = (int8_t*)(hsum + 2 * G * D); // [QDIG][G][D]
+  const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
+  const int nq = a.g.n_q;
+  for (int x = tid; x < G * D; x += 256)
+    qv[x] = load_io<IO_BF16>(a.q, ((int64_t)si * nq + h * G) * D + x);
+  // this thread's half row of T_K^{-T}
+  float t[64];
+  const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D + 64 * hf);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const float4 t4 = tp[c];
+    t[4 * c] = t4.x;
+    t[4 * c + 1] = t4.y;
+    t[4 * c + 2] = t4.z;
+    t[4 * c + 3] = t4.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) acc = fmaf(t[j], qv[gg * D + 64 * hf + j], acc);
+    hsum[(hf * G + gg) * D + i] = acc;
+  }
+  __syncthreads();
+  float v[2 * G];
+  float q[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    q[gg] = (hsum[gg * D + i] + hsum[(G + gg) * D + i]) * kLog2eOverSqrtD;
+    v[gg] = hf ? 0.f : q[gg];
+    v[G + gg] = fabsf(q[gg]);
+  }
+  block_reduce_sum_max<G>(v, red);
+  // fixed point: qi = rint(q' S_q), |qi| <= QMAX; balanced base-16 digits
+  float qsum_h[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    const float maxabs = v[G + gg];
+    const float sq = maxabs > 0.f ? (float)QMAX / maxabs : 1.f;
+    int qi = (int)rintf(q[gg] * sq);
+    qi = qi > QMAX ? QMAX : (qi < -QMAX ? -QMAX : qi);
+    if (hf == 0) {
+      qf[gg * D + i] = q[gg];
+      int r = qi;
+#pragma unroll
+      for (int k = 0; k < QDIG - 1; ++k) {
+        const int d = ((r + 8) & 15) - 8;
+        dig[(k * G + gg) * D + i] = (int8_t)d;
+        r = (r - d) >> 4;
+      }
+      dig[((QDIG - 1) * G + gg) * D + i] = (int8_t)r;
+    }
+    // sums of qi over dimensions [0, 64) and [64, 128): waves 0 and 1
+    qsum_h[gg] = hf ? 0.f : (float)qi;
+    qsum_h[gg] = wave_sum(qsum_h[gg]);
+    if (tid == 0) {
+      qsc[gg * 4] = v[gg];
+      qsc[gg * 4 + 1] = 1.f / sq;
+    }
+    if (tid == 0) qsc[gg * 4 + 2] = qsum_h[gg];
+    if (tid == 64) qsc[gg * 4 + 3] = qsum_h[gg];
+  }
+  __syncthreads();
+  // digit words: group x / DIGP of 8 dimensions, digit k = x % DIGP; nibble n
+  // holds that digit of one dimension of the group.
+  //   2 bits: group = half * 8 + w * 2 + parity, dims 64 half + 16 w + 2 n + parity
+  //   4 bits: group = half * 8 + w,              dims 64 half + 8 w + n
+  for (int x = tid; x < G * 16 * DIGP; x += 256) {
+    const int gg = x / (16 * DIGP), rem = x % (16 * DIGP);
+    const int grp16 = rem / DIGP, k = rem % DIGP, half = grp16 >> 3;
+    int e0, step;
+    if (BITS == 2) {
+      e0 = 64 * half + 16 * ((grp16 >> 1) & 3) + (grp16 & 1);
+      step = 2;
+    } else {
+      e0 = 64 * half + 8 * (grp16 & 7);
+      step = 1;
+    }
+    uint32_t word = 0;
+    if (k < QDIG)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) word |= ((uint32_t)dig[(k * G + gg) * D + e0 + step * n] & 15u) << (4 * n);
+    qdw[x] = word;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- quantized
+
 // Registers holding one sub-chunk's codes: key codes (lane pair per
 // position), scale/zero words, value rows of dimensions lane and lane + 64.
+// Loads are unconditional: a sub-chunk never leaves its unit (cpos is a
+// multiple of 128); positions outside [lo, hi) are masked arithmetically.
 template <int BITS, int G>
 struct SubBuf {
   using C = SplitCfg<BITS, G>;
@@ -238,27 +285,25 @@ struct SubBuf {
 
 template <int BITS, int G>
 __device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a, int64_t unit,
-                                         int pbase, int lo, int hi) {
+                                         int pbase) {
   using C = SplitCfg<BITS, G>;
   const Geometry& g = a.g;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
-  const uint8_t* kb = a.pl.kcode + (unit * g.cpos + pbase) * C::CB + half * (C::CB / 2);
+  const uint8_t* kb = a.pl.kcode + (unit * g.cpos + pbase + tq) * C::CB + half * (C::CB / 2);
+  const uint32_t* kz = a.pl.ksz + unit * g.cpos + pbase + tq;
+  const uint32_t* vz = a.pl.vsz + unit * g.cpos + pbase + tq;
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
-    const int p = pbase + 32 * r + tq;
-    const bool ok = p >= lo && p < hi;
 #pragma unroll
-    for (int q = 0; q < C::KQ; ++q)
-      b.kc[r][q] = ok ? ((const uint4*)(kb + (int64_t)(32 * r + tq) * C::CB))[q] : make_uint4(0, 0, 0, 0);
-    b.ksz[r] = ok ? a.pl.ksz[unit * g.cpos + p] : 0u;
-    b.vsz[r] = ok ? a.pl.vsz[unit * g.cpos + p] : 0u;
+    for (int q = 0; q < C::KQ; ++q) b.kc[r][q] = ((const uint4*)(kb + (int64_t)(32 * r) * C::CB))[q];
+    b.ksz[r] = kz[32 * r];
+    b.vsz[r] = vz[32 * r];
   }
   const uint8_t* vb = a.pl.vcode + ((unit * g.ctx_blocks + pbase / C::VB) * D + lane) * 16;
 #pragma unroll
   for (int k = 0; k < C::NBW; ++k) {
-    const bool ok = pbase + k * C::VB < hi && pbase + (k + 1) * C::VB > lo;
-    b.vc[k][0] = ok ? *(const uint4*)(vb + (int64_t)k * D * 16) : make_uint4(0, 0, 0, 0);
-    b.vc[k][1] = ok ? *(const uint4*)(vb + (int64_t)k * D * 16 + 64 * 16) : make_uint4(0, 0, 0, 0);
+    b.vc[k][0] = *(const uint4*)(vb + (int64_t)k * D * 16);
+    b.vc[k][1] = *(const uint4*)(vb + (int64_t)k * D * 16 + 64 * 16);
   }
 }
 
@@ -270,14 +315,15 @@ struct QueryRegs {
 // into the wave's running (M, Lrun, O) (online softmax across sub-chunks).
 template <int BITS, int G>
 __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase, int lo, int hi,
-                                            const uint4 (*qd)[8], const uint32_t* qlds,
+                                            const uint4 (*qd)[8], const uint32_t* qdw,
                                             const QueryRegs* qr, uint32_t* wsm, float* M,
                                             float* Lrun, float (*O)[2]) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
 
-  // ---- scores (log2 domain)
+  // ---- scores (log2 domain); -inf outside [lo, hi)
   float sc[C::ROWS][G];
+  float vs[C::ROWS], vz[C::ROWS];
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
     uint32_t d[4 * C::KQ];
@@ -288,9 +334,11 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
       d[4 * q + 2] = b.kc[r][q].z;
       d[4 * q + 3] = b.kc[r][q].w;
     }
-    const float ks = f16_to_f32(b.ksz[r] & 0xFFFFu), kz = f16_to_f32(b.ksz[r] >> 16);
     const int p = pbase + 32 * r + tq;
     const bool ok = p >= lo && p < hi;
+    const float ks = f16_to_f32(b.ksz[r] & 0xFFFFu), kz = f16_to_f32(b.ksz[r] >> 16);
+    vs[r] = ok ? f16_to_f32(b.vsz[r] & 0xFFFFu) : 0.f;
+    vz[r] = ok ? f16_to_f32(b.vsz[r] >> 16) : 0.f;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       int acc[QDIG];
@@ -298,7 +346,7 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
       for (int k = 0; k < QDIG; ++k) acc[k] = 0;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const uint4 L = C::QREG ? qd[gg][x] : *(const uint4*)(qlds + (gg * 16 + half * 8 + x) * DIGP);
+        const uint4 L = C::QREG ? qd[gg][x] : *(const uint4*)(qdw + (gg * 16 + half * 8 + x) * DIGP);
         const uint32_t Lk[4] = {L.x, L.y, L.z, L.w};
         int X;
         if constexpr (BITS == 2) {
@@ -314,7 +362,7 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
       int dot = acc[QDIG - 1];
 #pragma unroll
       for (int k = QDIG - 2; k >= 0; --k) dot = dot * 16 + acc[k];
-      if (BITS == 4) dot += 8 * (int)qr[gg].qsum;
+      if constexpr (BITS == 4) dot += 8 * (int)qr[gg].qsum;
       dot += swap_adjacent(dot);
       sc[r][gg] = ok ? ks * ((float)dot * qr[gg].inv) + kz * qr[gg].sig : -INFINITY;
     }
@@ -331,27 +379,26 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
     wmax[gg] = 0.f;
 #pragma unroll
     for (int r = 0; r < C::ROWS; ++r) {
-      pw[r][gg] = half ? 0.f : exp2f(sc[r][gg] - m[gg]);
-      wmax[gg] = fmaxf(wmax[gg], pw[r][gg] * f16_to_f32(b.vsz[r] & 0xFFFFu));
+      pw[r][gg] = half ? 0.f : exp2_nonpos(sc[r][gg] - m[gg]);
+      wmax[gg] = fmaxf(wmax[gg], pw[r][gg] * vs[r]);
     }
     wmax[gg] = wave_max(wmax[gg]);
   }
   uint32_t* wq = wsm;                 // [G][TW], positions of a row word grouped by parity
   uint32_t* wl = wsm + G * C::TW;     // [G][NG][WGP] digit words
   float lsum[G], zsum[G];
-  wave_sync();  // previous sub-chunk's reads of wq / wl are done
+  wave_sync();  // the previous sub-chunk's reads of wq / wl are done
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    const float wscale = wmax[gg] > 0.f ? (float)WMAX / wmax[gg] : 0.f;
+    const float wscale = wmax[gg] > 0.f ? (float)WMAX * __builtin_amdgcn_rcpf(wmax[gg]) : 0.f;
     lsum[gg] = zsum[gg] = 0.f;
 #pragma unroll
     for (int r = 0; r < C::ROWS; ++r) {
-      const float vs = f16_to_f32(b.vsz[r] & 0xFFFFu), vz = f16_to_f32(b.vsz[r] >> 16);
       const int t = 32 * r + tq;
       const int slot = BITS == 2 ? ((t & ~15) | ((t & 1) << 3) | ((t & 15) >> 1)) : t;
       lsum[gg] += pw[r][gg];
-      zsum[gg] = fmaf(pw[r][gg], vz, zsum[gg]);
-      if (!half) wq[gg * C::TW + slot] = (uint32_t)rintf(pw[r][gg] * vs * wscale);
+      zsum[gg] = fmaf(pw[r][gg], vz[r], zsum[gg]);
+      if (!half) wq[gg * C::TW + slot] = (uint32_t)fminf(rintf(pw[r][gg] * vs[r] * wscale), (float)WMAX);
     }
     lsum[gg] = wave_sum(lsum[gg]);
     zsum[gg] = wave_sum(zsum[gg]);
@@ -360,24 +407,22 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
 
   // ---- weight digit words: group gi of GS positions, digit k; nibble n holds
   // digit k of position n of the group's (parity) set
-  {
-    constexpr int WPG = C::WGW;
-    for (int x = lane; x < G * C::NG * WPG; x += 64) {
-      const int gg = x / (C::NG * WPG), rem = x % (C::NG * WPG);
-      const int gi = rem / WPG, r2 = rem % WPG;
-      const int par = BITS == 2 ? r2 / WDIG : 0, k = r2 % WDIG;
-      const uint4* src = (const uint4*)(wq + gg * C::TW + gi * C::GS + par * 8);
-      const uint4 s0 = src[0], s1 = src[1];
-      const uint32_t wv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      uint32_t word = 0;
+  for (int x = lane; x < G * C::NG * C::WGW; x += 64) {
+    const int gg = x / (C::NG * C::WGW), rem = x % (C::NG * C::WGW);
+    const int gi = rem / C::WGW, r2 = rem % C::WGW;
+    const int par = BITS == 2 ? r2 / WDIG : 0, k = r2 % WDIG;
+    const uint4* src = (const uint4*)(wq + gg * C::TW + gi * C::GS + par * 8);
+    const uint4 s0 = src[0], s1 = src[1];
+    const uint32_t wv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    uint32_t word = 0;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) word |= ((wv[n] >> (4 * k)) & 15u) << (4 * n);
-      wl[(gg * C::NG + gi) * C::WGP + par * WDIG + k] = word;
-    }
+    for (int n = 0; n < 8; ++n) word |= ((wv[n] >> (4 * k)) & 15u) << (4 * n);
+    wl[(gg * C::NG + gi) * C::WGP + par * WDIG + k] = word;
   }
   wave_sync();
 
-  // ---- o_i = sum_t w_t c_{t,i}: lane = dimensions lane, lane + 64
+  // ---- o_i = sum_t w_t c_{t,i}: lane = dimensions lane, lane + 64.  Value
+  // codes of positions outside [lo, hi) meet zero weights.
   uint32_t pa[G][2][WDIG];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg)
@@ -387,7 +432,6 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
       for (int k = 0; k < WDIG; ++k) pa[gg][e][k] = 0u;
 #pragma unroll
   for (int kb = 0; kb < C::NBW; ++kb) {
-    if (!(pbase + kb * C::VB < hi && pbase + (kb + 1) * C::VB > lo)) continue;
     const uint32_t rw[2][4] = {{b.vc[kb][0].x, b.vc[kb][0].y, b.vc[kb][0].z, b.vc[kb][0].w},
                                {b.vc[kb][1].x, b.vc[kb][1].y, b.vc[kb][1].z, b.vc[kb][1].w}};
 #pragma unroll
@@ -428,8 +472,8 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     const float Mn = fmaxf(M[gg], m[gg]);
-    const float fo = exp2f(M[gg] - Mn), fn = exp2f(m[gg] - Mn);
-    const float back = wmax[gg] / (float)WMAX;
+    const float fo = exp2_nonpos(M[gg] - Mn), fn = exp2_nonpos(m[gg] - Mn);
+    const float back = wmax[gg] * (1.f / (float)WMAX);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       float of = (float)pa[gg][e][WDIG - 1];
@@ -444,24 +488,26 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
 
 // One wave: sub-chunks c0, c0 + stride, ... (< c_end) of the quantized region
 // [lo, hi), two sub-chunks of codes in flight; leaves its partial in po/pm/pl.
+// A already holds sub-chunk c0.
 template <int BITS, int G>
-__device__ void quant_wave(const DecodeArgs& a, int64_t unit, int qbase, int c0, int stride,
-                           int c_end, int lo, int hi, const uint32_t* qlds, uint32_t* wsm, float* po,
-                           float* pm, float* pl) {
+__device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride, int c_end, int lo,
+                           int hi, const uint32_t* sm, uint32_t* wsm, float* po, float* pm,
+                           float* pl, SubBuf<BITS, G>& A) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1;
+  const float* qsc = (const float*)(sm + C::O_QSC);
+  const uint32_t* qdw = sm + C::O_QD;
   uint4 qd[C::QREG ? G : 1][8];
   QueryRegs qr[G];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    const float* rec = a.wsq + (int64_t)(qbase + gg) * QS;
-    qr[gg].sig = rec[QOFF_SIGMA];
-    qr[gg].inv = rec[QOFF_INVS];
-    qr[gg].qsum = (float)(int)__float_as_uint(rec[QOFF_QSUM + half]);
+    qr[gg].sig = qsc[gg * 4];
+    qr[gg].inv = qsc[gg * 4 + 1];
+    qr[gg].qsum = qsc[gg * 4 + 2 + half];
     if (C::QREG)
 #pragma unroll
       for (int x = 0; x < 8; ++x)
-        qd[C::QREG ? gg : 0][x] = *(const uint4*)((const uint32_t*)rec + QOFF_LIMB + (half * 8 + x) * DIGP);
+        qd[C::QREG ? gg : 0][x] = *(const uint4*)(qdw + (gg * 16 + half * 8 + x) * DIGP);
   }
   float M[G], Lrun[G], O[G][2];
 #pragma unroll
@@ -470,18 +516,17 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int qbase, int c0,
     Lrun[gg] = 0.f;
     O[gg][0] = O[gg][1] = 0.f;
   }
-  SubBuf<BITS, G> A, B;
-  int c = c0;
-  if (c < c_end) load_sub<BITS, G>(A, a, unit, c * C::TW, lo, hi);
+  SubBuf<BITS, G> B;
+  int c = c0;  // A holds sub-chunk c0 (loaded by the caller) when c0 < c_end
   while (c < c_end) {
     int cn = c + stride;
-    if (cn < c_end) load_sub<BITS, G>(B, a, unit, cn * C::TW, lo, hi);
-    process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qlds, qr, wsm, M, Lrun, O);
+    if (cn < c_end) load_sub<BITS, G>(B, a, unit, cn * C::TW);
+    process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, O);
     c = cn;
     if (c >= c_end) break;
     cn = c + stride;
-    if (cn < c_end) load_sub<BITS, G>(A, a, unit, cn * C::TW, lo, hi);
-    process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qlds, qr, wsm, M, Lrun, O);
+    if (cn < c_end) load_sub<BITS, G>(A, a, unit, cn * C::TW);
+    process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, O);
     c = cn;
   }
 #pragma unroll
@@ -495,19 +540,21 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int qbase, int c0,
   }
 }
 
-template <int G>
-__device__ void window_chunk(const DecodeArgs& a, int64_t unit, int qbase, int Lq, int sq,
-                             uint32_t* sm, float* obuf, float* red, float (&m_out)[G],
-                             float (&l_out)[G]) {
+// ---------------------------------------------------------------- window
+
+template <int BITS, int G>
+__device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, uint32_t* sm,
+                             float (&m_out)[G], float (&l_out)[G]) {
+  using C = SplitCfg<BITS, G>;
   const Geometry& g = a.g;
   const int tid = threadIdx.x, half = tid & 1;
   const int i = tid & (D - 1), grp = tid >> 7;
-  float* qs = (float*)sm;        // [G][D]
-  float* scw = qs + G * D;       // [G][WINDOW_MAX]
+  const float* qs = (const float*)(sm + C::O_QF);
+  float* obuf = (float*)(sm + C::O_OBUF);
+  float* red = (float*)(sm + C::O_RED);
+  float* scw = (float*)(sm + C::O_UNION);  // [G][WINDOW_MAX]
   const int ns = Lq < g.S ? Lq : g.S;
   const int ntok = ns + (Lq > sq ? Lq - sq : 0);
-  for (int x = tid; x < G * D; x += 256) qs[x] = a.wsq[(int64_t)(qbase + x / D) * QS + (x % D)];
-  __syncthreads();
   for (int tok = tid >> 1; tok < ntok; tok += 128) {
     const int p = tok < ns ? tok : sq + (tok - ns);
     const uint16_t* src = tok < ns ? a.pl.ksink + (unit * g.S + p) * D
@@ -529,7 +576,7 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int qbase, int L
     }
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      const float d2 = dot[gg] + __shfl_xor(dot[gg], 1);
+      const float d2 = dot[gg] + __int_as_float(swap_adjacent(__float_as_int(dot[gg])));
       if (!half) scw[gg * WINDOW_MAX + tok] = d2;
     }
   }
@@ -578,14 +625,14 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int qbase, int L
   }
 }
 
-template <int BITS, int G>
+// ---------------------------------------------------------------- kernels
+
+template <int IO_BF16, int BITS, int G>
 __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
-  uint32_t* smem = (uint32_t*)smem4;
-  float* obuf = (float*)smem;             // [G][D] workgroup partial o
-  float* red = obuf + G * D;              // [64] reductions
-  uint32_t* un = (uint32_t*)(red + 64);   // union
+  uint32_t* sm = (uint32_t*)smem4;
+  float* obuf = (float*)(sm + C::O_OBUF);
 
   const Geometry& g = a.g;
   const int j = blockIdx.x, h = blockIdx.y, si = blockIdx.z, tid = threadIdx.x;
@@ -594,32 +641,35 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
   const int qbase = si * g.n_q + h * G;
   const int nsp = gridDim.x;
 
-  float m[G], l[G];
+  // the quantized region [S, sq) in sub-chunks of TW positions; this
+  // workgroup's waves take every (4 n_splits)-th one starting at 4 j + wave
+  const int lo = g.S, hi = sq;
+  const int c_first = lo / C::TW;
+  const int c_end = hi > lo ? (hi + C::TW - 1) / C::TW : c_first;
   bool empty;
   if (j == a.n_splits) {
     const int ns = Lq < g.S ? Lq : g.S;
     empty = ns + (Lq > sq ? Lq - sq : 0) == 0;
-    if (!empty) window_chunk<G>(a, unit, qbase, Lq, sq, un, obuf, red, m, l);
   } else {
-    // sub-chunks of TW positions covering [S, sq); this workgroup's waves take
-    // every (4 n_splits)-th one starting at 4 j + wave
-    const int lo = g.S, hi = sq;
-    const int c_first = lo / C::TW;
-    const int c_end = hi > lo ? (hi + C::TW - 1) / C::TW : c_first;
     empty = c_first + 4 * j >= c_end;
-    if (!empty) {
-      uint32_t* qlds = un;
-      float* part = (float*)(qlds + C::QLDS + 4 * C::WAVE);  // [4][G][D + 2]
-      if (!C::QREG) {
-        for (int x = tid; x < G * 16 * DIGP; x += 256)
-          qlds[x] = ((const uint32_t*)(a.wsq + (int64_t)(qbase + x / (16 * DIGP)) * QS))
-              [QOFF_LIMB + x % (16 * DIGP)];
-        __syncthreads();
-      }
+  }
+  float m[G], l[G];
+  if (!empty) {
+    if (j == a.n_splits) {
+      compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
+      window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
+    } else {
       const int w = tid >> 6;
+      const int c0 = c_first + 4 * j + w;
+      // first sub-chunk's codes in flight while the query is compensated
+      SubBuf<BITS, G> A;
+      if (c0 < c_end) load_sub<BITS, G>(A, a, unit, c0 * C::TW);
+      compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
+      uint32_t* wbase = sm + C::O_UNION;
+      float* part = (float*)(wbase + 4 * C::WAVE);  // [4][G][D + 2]
       float* pw = part + w * G * (D + 2);
-      quant_wave<BITS, G>(a, unit, qbase, c_first + 4 * j + w, 4 * a.n_splits, c_end, lo, hi, qlds,
-                          qlds + C::QLDS + w * C::WAVE, pw, pw + G * D, pw + G * D + G);
+      quant_wave<BITS, G>(a, unit, c0, 4 * a.n_splits, c_end, lo, hi, sm, wbase + w * C::WAVE, pw,
+                          pw + G * D, pw + G * D + G, A);
       __syncthreads();
       // merge the four wave partials (a wave without sub-chunks has l = 0)
       const int i = tid & (D - 1), hf = tid >> 7;
@@ -659,8 +709,8 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
   }
 }
 
-// One workgroup per (sequence, query head): log-sum-exp merge of the chunk
-// partials.  Thread = (4 dimensions, chunk residue mod 8).
+// One workgroup per (sequence, query head): log-sum-exp merge of the
+// partials.  Thread = (4 dimensions, partial residue mod 8).
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   __shared__ float scal[256];
   __shared__ __align__(16) float racc[8][D];
@@ -711,7 +761,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 // Workgroups per (sequence, KV head) so that the grid (plus the window
 // workgroups) fits the GPU's resident capacity once; never more than the host
 // bound in a.n_splits.
-template <int BITS, int G>
+template <int IO_BF16, int BITS, int G>
 hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
   static int slots = 0;
   const size_t lds = (size_t)SplitCfg<BITS, G>::TOTAL * 4;
@@ -720,7 +770,7 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<BITS, G>, 256, lds);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<IO_BF16, BITS, G>, 256, lds);
     if (e != hipSuccess) return e;
     slots = cus * (per > 0 ? per : 1);
   }
@@ -731,36 +781,30 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     if (a.n_splits > fill) a.n_splits = fill;
   }
   dim3 gs(a.n_splits + 1, a.g.n_kv, a.n_seq);
-  hipLaunchKernelGGL((split_kernel<BITS, G>), gs, dim3(256), lds, st, a);
+  hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G>), gs, dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+template <int IO_BF16, int BITS>
+hipError_t launch_split_g(DecodeArgs& a, hipStream_t st) {
+  switch (a.g.G) {
+    case 1: return launch_split<IO_BF16, BITS, 1>(a, st);
+    case 2: return launch_split<IO_BF16, BITS, 2>(a, st);
+    case 4: return launch_split<IO_BF16, BITS, 4>(a, st);
+    default: return launch_split<IO_BF16, BITS, 8>(a, st);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop) {
-  dim3 gq(a.g.n_kv, a.n_seq);
-  if (io_bf16) {
-    if (a.g.bits == 2)
-      hipLaunchKernelGGL((qcomp_kernel<1, 2>), gq, dim3(128), 0, st, a);
-    else
-      hipLaunchKernelGGL((qcomp_kernel<1, 4>), gq, dim3(128), 0, st, a);
-  } else {
-    if (a.g.bits == 2)
-      hipLaunchKernelGGL((qcomp_kernel<0, 2>), gq, dim3(128), 0, st, a);
-    else
-      hipLaunchKernelGGL((qcomp_kernel<0, 4>), gq, dim3(128), 0, st, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   if (ev_start && (e = hipEventRecord(ev_start, st)) != hipSuccess) return e;
-  const int G = a.g.G;
-  if (a.g.bits == 2)
-    e = G == 1 ? launch_split<2, 1>(a, st) : G == 2 ? launch_split<2, 2>(a, st)
-      : G == 4 ? launch_split<2, 4>(a, st) : launch_split<2, 8>(a, st);
+  if (io_bf16)
+    e = a.g.bits == 2 ? launch_split_g<1, 2>(a, st) : launch_split_g<1, 4>(a, st);
   else
-    e = G == 1 ? launch_split<4, 1>(a, st) : G == 2 ? launch_split<4, 2>(a, st)
-      : G == 4 ? launch_split<4, 4>(a, st) : launch_split<4, 8>(a, st);
+    e = a.g.bits == 2 ? launch_split_g<0, 2>(a, st) : launch_split_g<0, 4>(a, st);
   if (e != hipSuccess) return e;
   if (ev_stop && (e = hipEventRecord(ev_stop, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.g.n_q, a.n_seq), dim3(256), 0, st, a);

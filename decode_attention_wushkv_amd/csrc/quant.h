@@ -1,0 +1,216 @@
+// Device-side helpers of the quantizer shared by the append kernels and the
+// fused decode step: exact number-format conversions and the per-token
+// percentile-clipped affine quantizer (WUSH-KV paper page, section 5.3;
+// appendix B.3 for the level grid).
+//
+// Numerics: order statistics come from an exact rank sort of the 128 bfloat16
+// values; the linear-interpolation percentile, the scale (hi - lo)/(2^b - 1),
+// its binary16 rounding and the code coordinate (x - z16)/s16 are fp64 with no
+// fused multiply-add, rounded half to even, so every integer decision matches
+// an fp64 evaluation of the definitions.
+#pragma once
+
+#include "common.h"
+
+namespace wkv {
+
+// ---------------------------------------------------------------- formats
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Round m / 2^s to nearest, ties to even (1 <= s <= 63).
+__device__ __forceinline__ uint64_t shift_rne(uint64_t m, int s) {
+  uint64_t q = m >> s;
+  uint64_t rem = m & ((1ull << s) - 1);
+  uint64_t half = 1ull << (s - 1);
+  if (rem > half || (rem == half && (q & 1))) q += 1;
+  return q;
+}
+
+// fp64 -> bfloat16 bits, round to nearest even, gradual underflow, overflow to inf.
+__device__ uint16_t f64_to_bf16(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
+  int ef = (int)((b >> 52) & 0x7FF);
+  uint64_t mant = b & 0xFFFFFFFFFFFFFull;
+  if (ef == 0x7FF) return sign | (mant ? 0x7FC0 : 0x7F80);
+  if (ef == 0) return sign;  // fp64 subnormals lie far below bf16's smallest step
+  int e = ef - 1023;
+  uint64_t m = mant | (1ull << 52);
+  if (e >= -126) {
+    uint64_t r = shift_rne(m, 45);  // keep 8 significant bits
+    if (r == 256) { r = 128; e += 1; }
+    if (e > 127) return sign | 0x7F80;
+    return sign | (uint16_t)((e + 127) << 7) | (uint16_t)(r & 0x7F);
+  }
+  int s = -(e + 81);  // value in units of 2^-133 is m * 2^(e + 81)
+  if (s > 63) return sign;
+  return sign | (uint16_t)shift_rne(m, s);  // r <= 128; 128 encodes 2^-126
+}
+
+// fp32 -> bfloat16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> binary16 bits, round to nearest even, saturating at +-65504.
+__device__ uint16_t f64_to_f16_sat(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
+  int ef = (int)((b >> 52) & 0x7FF);
+  uint64_t mant = b & 0xFFFFFFFFFFFFFull;
+  if (ef == 0x7FF) return mant ? (uint16_t)0x7E00 : (uint16_t)(sign | 0x7BFF);
+  if (ef == 0) return sign;
+  int e = ef - 1023;
+  uint64_t m = mant | (1ull << 52);
+  if (e >= -14) {
+    uint64_t r = shift_rne(m, 42);  // keep 11 significant bits
+    if (r == 2048) { r = 1024; e += 1; }
+    if (e > 15) return sign | 0x7BFF;
+    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r & 0x3FF);
+  }
+  int s = 28 - e;  // value in units of 2^-24 is m * 2^(e - 28)
+  if (s > 63) return sign;
+  return sign | (uint16_t)shift_rne(m, s);  // r <= 1024; 1024 encodes 2^-14
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return (double)(float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---------------------------------------------------------------- quantizer
+
+// LDS scratch of the quantizer for up to two groups of 128 threads.
+struct QLds {
+  float vals[2][D];
+  float sorted[2][D];
+  int codes[2][D];
+};
+
+// Linear-interpolation percentile of the sorted group (fp64, no FMA).
+__device__ double percentile_sorted(const float* sorted, double p) {
+#pragma clang fp contract(off)
+  double h = p * (double)(D - 1);
+  double jf = floor(h);
+  int j = (int)jf;
+  double f = h - jf;
+  if (j >= D - 1) return (double)sorted[D - 1];
+  double a = (double)sorted[j];
+  double b = (double)sorted[j + 1];
+  return a + f * (b - a);
+}
+
+// Quantize groups of 128 values: thread t holds element t % 128 of group
+// t / 128 (x).  Returns this thread's code; *sz gets {s16 | z16 << 16} of its
+// group.  Every thread of the workgroup must call it (it uses barriers).
+__device__ int quantize_group(float x, QLds& L, double p_lo, double p_hi, int bits, uint32_t* sz) {
+#pragma clang fp contract(off)
+  const int i = threadIdx.x & (D - 1), grp = threadIdx.x >> 7;
+  float* vals = L.vals[grp];
+  float* sorted = L.sorted[grp];
+  vals[i] = x;
+  __syncthreads();
+  int rank = 0;
+#pragma unroll 8
+  for (int j = 0; j < D; ++j) {
+    float y = vals[j];
+    rank += (y < x) || (y == x && j < i);
+  }
+  sorted[rank] = x;
+  __syncthreads();
+  const double lo = percentile_sorted(sorted, p_lo);
+  const double hi = percentile_sorted(sorted, p_hi);
+  const double levels = (double)((1 << bits) - 1);
+  const double s = (hi - lo) / levels;
+  const uint16_t s16 = f64_to_f16_sat(s);
+  const uint16_t z16 = f64_to_f16_sat(lo);
+  const double sd = f16_bits_to_f64(s16);
+  const double zd = f16_bits_to_f64(z16);
+  int c = 0;
+  if (sd != 0.0) {
+    double u = ((double)x - zd) / sd;
+    double r = rint(u);
+    r = r < 0.0 ? 0.0 : r;
+    r = r > levels ? levels : r;
+    c = (int)r;
+  }
+  *sz = (uint32_t)s16 | ((uint32_t)z16 << 16);
+  __syncthreads();  // vals / sorted may be reused by the next call
+  return c;
+}
+
+// Accumulates value-code bits of one dimension row for consecutive positions
+// and writes each 16-byte row once (read-modify-write keeps other positions).
+struct VRow {
+  int blk;
+  uint32_t buf[4];
+  uint32_t msk[4];
+};
+
+__device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl, int64_t unit, const Geometry& g) {
+  if (r.blk < 0) return;
+  uint4* p = (uint4*)(pl.vcode + ((unit * g.ctx_blocks + r.blk) * D + (threadIdx.x & (D - 1))) * 16);
+  uint4 old = *p;
+  old.x = (old.x & ~r.msk[0]) | r.buf[0];
+  old.y = (old.y & ~r.msk[1]) | r.buf[1];
+  old.z = (old.z & ~r.msk[2]) | r.buf[2];
+  old.w = (old.w & ~r.msk[3]) | r.buf[3];
+  *p = old;
+  r.blk = -1;
+}
+
+__device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes& pl, int64_t unit,
+                                         const Geometry& g) {
+  int blk = p / g.vblock;
+  if (blk != r.blk) {
+    vrow_flush(r, pl, unit, g);
+    r.blk = blk;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r.buf[w] = r.msk[w] = 0u;
+  }
+  int bit = (p % g.vblock) * g.bits;
+  uint32_t m = (1u << g.bits) - 1u;
+  r.buf[bit >> 5] |= (uint32_t)code << (bit & 31);
+  r.msk[bit >> 5] |= m << (bit & 31);
+}
+
+// Quantize key and value entries of position p and store codes and
+// scale/zero.  128-thread workgroups: thread i holds dimension i of both (kx,
+// vx) and the two groups run one after the other.  256-thread workgroups:
+// threads 0..127 hold the key entry (kx), threads 128..255 the value entry
+// (vx) and both groups run at once.
+__device__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, const Planes& pl,
+                                int64_t unit, const Geometry& g) {
+  const int i = threadIdx.x & (D - 1);
+  const bool two = blockDim.x == 2 * D;
+  const bool is_v = two && threadIdx.x >= D;
+  uint32_t ksz = 0, vsz = 0;
+  int kc = 0, vc = 0;
+  if (two) {
+    const int c = quantize_group(is_v ? vx : kx, L, g.p_lo, g.p_hi, g.bits, is_v ? &vsz : &ksz);
+    (is_v ? vc : kc) = c;
+  } else {
+    kc = quantize_group(kx, L, g.p_lo, g.p_hi, g.bits, &ksz);
+    vc = quantize_group(vx, L, g.p_lo, g.p_hi, g.bits, &vsz);
+  }
+  if (!is_v) L.codes[0][i] = kc;
+  __syncthreads();
+  const int words = g.code_bytes / 4;  // 8 (2-bit) or 16 (4-bit)
+  if (threadIdx.x < words) {
+    const int per = 32 / g.bits;
+    uint32_t w = 0;
+    for (int e = 0; e < per; ++e) w |= (uint32_t)L.codes[0][threadIdx.x * per + e] << (e * g.bits);
+    ((uint32_t*)(pl.kcode + (unit * g.cpos + p) * g.code_bytes))[threadIdx.x] = w;
+  }
+  if (threadIdx.x == 0) pl.ksz[unit * g.cpos + p] = ksz;
+  if (threadIdx.x == (two ? D : 0)) pl.vsz[unit * g.cpos + p] = vsz;
+  if (!two || is_v) vrow_add(vr, p, vc, pl, unit, g);
+  __syncthreads();  // codes[] reuse
+}
+
+}  // namespace wkv

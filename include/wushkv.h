@@ -105,8 +105,8 @@ typedef struct {
       bytes_kring, bytes_vring;
   int32_t code_bytes;   /* d * bits / 8 per position per K (or V)   */
   int32_t vblock;       /* positions per value-code block = 128/bits */
-  int32_t ctx_blocks;   /* ceil(ctx_cap / vblock)                    */
-  int32_t cpos;         /* ctx_blocks * vblock                       */
+  int32_t ctx_blocks;   /* cpos / vblock                             */
+  int32_t cpos;         /* positions per unit: ctx_cap rounded up to 128 */
   int32_t ring_slots;   /* recent + flush - 1                        */
   int32_t units;        /* n_layers * max_batch * n_kv_heads         */
 } wushkv_layout_t;
