@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the WUSH-KV 2-bit transformed KV cache on one MI355X.
 
-A step is one pass of the whole hot path over one batch: for every layer, a
-one-token wushkv_append per sequence (key transform, window placement, ring
-eviction, percentile clip, quantize, pack) followed by wushkv_decode_attn
-(query compensation, split-K scan over the packed codes and the bfloat16
-windows, log-sum-exp merge).  The cache is built beforehand through the same
+A step is one pass of the whole hot path over one batch: for every layer, one
+wushkv_decode_step call per batch (key transform of the new position, query
+compensation, split-K scan over the packed codes and the bfloat16 windows with
+the new entry included, then the flush of the ring entry that leaves the
+window: percentile clip, quantize, pack -- and the log-sum-exp merge).  With
+--path append+attn the same step runs as wushkv_append followed by
+wushkv_decode_attn (three launches per layer instead of two; the flush then
+precedes the attention).  The cache is built beforehand through the same
 library (prefill appends) from seeded synthetic inputs and is resident in HBM
 when the timed region starts.
 
@@ -13,7 +16,7 @@ Default workload: 32 layers x 32 KV heads x head_dim 128 (MHA, 32 query heads),
 batch 1, context 131072, 2-bit, sink 4, recent 128 -- the cache whose 2-bit
 footprint is ~8 GiB of codes (+1 GiB of fp16 scale/zero).
 
-Prints one JSON line.  value = cache bytes the decode steps read (algorithmic:
+Prints one JSON line.  value = cache bytes the attention reads (algorithmic:
 72 B per quantized token-head, 512 B per bfloat16 window token-head) per second
 of whole-step time (appends included).
 """
@@ -36,9 +39,11 @@ def squant(L, S, R, F):
     return S + F * (max(0, L - R - S) // F)
 
 
-def unit_bytes(L, S, R, F, bits):
-    """Algorithmic bytes one decode reads for one (sequence, KV head) at length L."""
-    sq = squant(L, S, R, F)
+def unit_bytes(L, S, R, F, bits, step=True):
+    """Algorithmic bytes the attention reads for one (sequence, KV head) at
+    length L (new position included).  A fused step attends before the flush:
+    its quantized boundary is that of length L - 1."""
+    sq = squant(L - 1 if step else L, S, R, F)
     quant = max(0, sq - S)
     window = min(S, L) + max(0, L - sq)
     return quant * (2 * (128 * bits // 8) + 8) + window * 512
@@ -70,7 +75,7 @@ def cpu_baseline(w, bits, seconds, max_units):
         oracle.attention(q, K[None], V[None])
         elapsed += time.perf_counter() - t0
         done += 1
-    gbs = done * unit_bytes(L, S, R, F, bits) / elapsed / 1e9
+    gbs = done * unit_bytes(L, S, R, F, bits, step=False) / elapsed / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} (layer, KV head) units of {w.group} query head(s) at context {L}, "
                       f"dequantize + fp64 softmax attention, {elapsed:.1f} s"}
@@ -83,6 +88,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3, help="workload id in synth.WORKLOADS")
     ap.add_argument("--bits", type=int, default=None)
+    ap.add_argument("--path", choices=("step", "append+attn"), default="step",
+                    help="fused wushkv_decode_step, or wushkv_append then wushkv_decode_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -171,10 +178,13 @@ def main():
 
     ev_pairs = []
 
+    fused = args.path == "step"
+
     def step(st, timed):
         for layer in range(w.n_layers):
             k1, v1, q = steps_in[st][layer]
-            dc.append(layer, slots, [1] * B, k1, v1, tks[layer])
+            if not fused:
+                dc.append(layer, slots, [1] * B, k1, v1, tks[layer])
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -182,7 +192,10 @@ def main():
                 e1.record(stream)
                 wk.wushkv_set_split_events(dc.handle, e0.cuda_event, e1.cuda_event)
                 ev_pairs.append((e0, e1))
-            dc.decode_attn(layer, slots, q, tqs[layer], out)
+            if fused:
+                dc.decode_step(layer, slots, k1, v1, tks[layer], q, tqs[layer], out)
+            else:
+                dc.decode_attn(layer, slots, q, tqs[layer], out)
             if timed:
                 wk.wushkv_set_split_events(dc.handle, None, None)
 
@@ -205,7 +218,7 @@ def main():
     for st in range(W, W + K):
         for s in range(B):
             Lnow = L0[s] + st + 1
-            bytes_total += w.n_layers * w.n_kv * unit_bytes(Lnow, S, R, F, bits)
+            bytes_total += w.n_layers * w.n_kv * unit_bytes(Lnow, S, R, F, bits, fused)
     bytes_per_step = bytes_total / K
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     bytes_per_launch = bytes_per_step / w.n_layers
@@ -232,11 +245,13 @@ def main():
                    "bits": bits, "sink": S, "recent": R, "flush": F,
                    "p_lo": w.p_lo, "p_hi": w.p_hi, "io": w.io},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "path": args.path,
         "append": {"tokens_per_s": round(append_tok_s, 1),
                    "note": "one-token appends per (sequence, layer) inside the timed steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "split_kernel (split-K scan over codes + windows)",
+                     "kernel": "split_kernel (split-K scan over codes + windows"
+                               + (", fused one-token append)" if fused else ")"),
                      "bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(split_avg_ms, 5), "launches": len(split_ms)},
         "cache_build_s": round(build_s, 2),

@@ -24,7 +24,7 @@ WUSHKV_MAX_SEQ_PER_CALL = 128
 EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_append", "wushkv_decode_workspace_bytes",
-    "wushkv_decode_attn", "wushkv_set_split_events", "wushkv_status_str",
+    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events", "wushkv_status_str",
 )
 
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_decode_workspace_bytes.argtypes = [P, i32]
     L.wushkv_decode_attn.restype = ctypes.c_int
     L.wushkv_decode_attn.argtypes = [P, i32, i32, i32p, P, P, P, P, _U64, P]
+    L.wushkv_decode_step.restype = ctypes.c_int
+    L.wushkv_decode_step.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P, _U64, P]
     L.wushkv_set_split_events.restype = ctypes.c_int
     L.wushkv_set_split_events.argtypes = [P, P, P]
     L.wushkv_status_str.restype = ctypes.c_char_p
@@ -175,6 +177,19 @@ def wushkv_decode_attn(cache: int, layer: int, slots, q_ptr: int, tq_ptr: int, o
                                   ctypes.c_void_p(ws_ptr), int(ws_bytes), ctypes.c_void_p(stream))
     if check:
         _check(st, "wushkv_decode_attn")
+    return st
+
+
+def wushkv_decode_step(cache: int, layer: int, slots, k_ptr: int, v_ptr: int, tk_ptr: int,
+                       q_ptr: int, tq_ptr: int, out_ptr: int, ws_ptr: int, ws_bytes: int,
+                       stream: int = 0, *, check: bool = True) -> int:
+    s, n = _i32_array(slots)
+    vp = ctypes.c_void_p
+    st = lib().wushkv_decode_step(vp(cache), int(layer), n, s, vp(k_ptr), vp(v_ptr), vp(tk_ptr),
+                                  vp(q_ptr), vp(tq_ptr), vp(out_ptr), vp(ws_ptr), int(ws_bytes),
+                                  vp(stream))
+    if check:
+        _check(st, "wushkv_decode_step")
     return st
 
 

@@ -8,7 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libwushkv.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "append.hip", "decode.hip")]
-HEADERS = [os.path.join(HERE, "csrc", "common.h"), os.path.join(ROOT, "include", "wushkv.h")]
+HEADERS = [os.path.join(HERE, "csrc", h) for h in ("common.h", "quant.h")] + [
+    os.path.join(ROOT, "include", "wushkv.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -235,17 +235,24 @@ extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t
   return align256(nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4);
 }
 
-extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int32_t n_seq,
-                                            const int32_t* slots, const void* q, const float* tq,
-                                            float* out, void* ws, uint64_t ws_bytes,
-                                            void* stream) {
+// Shared by decode_attn and decode_step: validation of the attention
+// arguments, then the per-sequence plan and the launch.  step = 1 adds the
+// fused one-token append (k, v, tk non-null).
+static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                   const int32_t* slots, const void* k, const void* v,
+                                   const float* tk, const void* q, const float* tq, float* out,
+                                   void* ws, uint64_t ws_bytes, void* stream, bool step) {
   if (!c || !slots || layer < 0 || layer >= c->cfg.n_layers || n_seq < 0) return WUSHKV_EINVAL;
   if (n_seq > MAXSEQ) return WUSHKV_EUNSUPPORTED;
+  if (step && c->cfg.sink + c->cfg.recent + c->cfg.flush > WINDOW_MAX) return WUSHKV_EUNSUPPORTED;
   if (n_seq == 0) return WUSHKV_OK;
   if (!q || !tq || !out || !ws) return WUSHKV_EINVAL;
+  if (step && (!k || !v || !tk)) return WUSHKV_EINVAL;
   const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;
   if (((uintptr_t)q % esz) || ((uintptr_t)tq % 16) || ((uintptr_t)out % 16) ||
       ((uintptr_t)ws % 16))
+    return WUSHKV_EINVAL;
+  if (step && (((uintptr_t)k % esz) || ((uintptr_t)v % esz) || ((uintptr_t)tk % 16)))
     return WUSHKV_EINVAL;
   if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
   if (ws_bytes < wushkv_decode_workspace_bytes(c, n_seq)) return WUSHKV_EWORKSPACE;
@@ -259,13 +266,19 @@ extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int3
   a.tq = tq;
   a.out = out;
   a.wsp = (float*)ws;
+  if (step) {
+    a.k_new = k;
+    a.v_new = v;
+    a.tk = tk;
+  }
   const int sl = sub_len(c->cfg.bits);
   int max_sub = 0;
   for (int i = 0; i < n_seq; ++i) {
-    int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
-    if (L < 1) return WUSHKV_EINVAL;
+    const int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
+    if (step ? L + 1 > c->cfg.ctx_cap : L < 1) return step ? WUSHKV_ECAPACITY : WUSHKV_EINVAL;
     a.s.slot[i] = slots[i];
-    a.s.len[i] = L;
+    // a step attends at length L + 1 with the boundary of length L (flush after)
+    a.s.len[i] = step ? L + 1 : L;
     a.s.squant[i] = squant_of(L, c->cfg.sink, c->cfg.recent, c->cfg.flush);
     const int sq = a.s.squant[i];
     const int nsub = sq > c->cfg.sink ? (sq + sl - 1) / sl - c->cfg.sink / sl : 0;
@@ -279,7 +292,26 @@ extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int3
   a.n_splits = need < cap ? need : cap;
   hipError_t e = launch_decode(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream,
                                c->ev_start, c->ev_stop);
-  return e == hipSuccess ? WUSHKV_OK : WUSHKV_EDEVICE;
+  if (e != hipSuccess) return WUSHKV_EDEVICE;
+  if (step)
+    for (int i = 0; i < n_seq; ++i) c->len[(size_t)layer * c->cfg.max_batch + slots[i]] += 1;
+  return WUSHKV_OK;
+}
+
+extern "C" wushkv_status wushkv_decode_attn(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                            const int32_t* slots, const void* q, const float* tq,
+                                            float* out, void* ws, uint64_t ws_bytes,
+                                            void* stream) {
+  return decode_common(c, layer, n_seq, slots, nullptr, nullptr, nullptr, q, tq, out, ws,
+                       ws_bytes, stream, false);
+}
+
+extern "C" wushkv_status wushkv_decode_step(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                            const int32_t* slots, const void* k, const void* v,
+                                            const float* tk, const void* q, const float* tq,
+                                            float* out, void* ws, uint64_t ws_bytes,
+                                            void* stream) {
+  return decode_common(c, layer, n_seq, slots, k, v, tk, q, tq, out, ws, ws_bytes, stream, true);
 }
 
 extern "C" wushkv_status wushkv_set_split_events(wushkv_cache* c, void* ev_start, void* ev_stop) {

@@ -94,6 +94,14 @@ struct DecodeArgs {
   const float* tq;
   float* out;
   float* wsp;     // [n_seq][n_q][n_splits + 1][PS]
+  // Decode step (fused one-token append): the new key and value rows
+  // [n_seq][n_kv][D] in the io dtype and T_K [n_kv][D][D].  Null k_new means
+  // attention only.  In a step, s.len is the length with the new position and
+  // s.squant the quantized boundary before it (the window holds the new entry
+  // in full precision; the flush follows the attention).
+  const void* k_new;
+  const void* v_new;
+  const float* tk;
   DecodeSeqs s;
 };
 

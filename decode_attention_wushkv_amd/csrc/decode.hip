@@ -24,7 +24,15 @@
 //           Each workgroup writes (o, m, l) per query head.
 //   combine one workgroup per (sequence, query head): log-sum-exp merge of the
 //           partials into the fp32 output.
-#include "common.h"
+//
+// Decode step (attention fused with the one-token append, in the order of
+// section 4.4: the new entry is attended in full precision, then the window
+// is flushed): the window workgroup also transforms the new key, includes the
+// new position in its window, and after writing its partial quantizes the
+// ring entries that leave the recent window and stores the new entry.  The
+// quantized workgroups read positions below the old boundary only, so the
+// codes it writes (at or above that boundary) never race with them.
+#include "quant.h"
 
 namespace wkv {
 namespace {
@@ -162,7 +170,11 @@ struct SplitCfg {
   static constexpr int SETUP = G * D + 2 * G * D + QDIG * G * D / 4;   // qv, halves, digits (bytes/4)
   static constexpr int WAVE = G * TW + G * NG * WGP;                    // per wave
   static constexpr int QUANT = 4 * WAVE + 4 * G * (D + 2);
-  static constexpr int WIN = G * WINDOW_MAX;
+  // window workgroup, in the union: scores [G][WINDOW_MAX], the decode-step
+  // new key and value (bfloat16, D words), per-wave PV partials [4][G][D]
+  static constexpr int O_NEW = G * WINDOW_MAX;
+  static constexpr int O_WPART = O_NEW + D;
+  static constexpr int WIN = O_WPART + 4 * G * D;
   static constexpr int U1 = SETUP > QUANT ? SETUP : QUANT;
   static constexpr int UNION = U1 > WIN ? U1 : WIN;
   static constexpr int TOTAL = O_UNION + UNION;
@@ -540,6 +552,92 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride
   }
 }
 
+// ---------------------------------------------------------------- decode step
+
+template <int IO_BF16>
+__device__ __forceinline__ uint16_t io_to_bf16(const void* base, int64_t idx) {
+  if (IO_BF16) return ((const uint16_t*)base)[idx];
+  return f32_to_bf16(((const float*)base)[idx]);
+}
+
+// The new position's entries as bfloat16 bits in LDS: k' = T_K k with fp64
+// FMAs in dimension order and one rounding (the same arithmetic as the append
+// kernel, so both paths store identical bits), and v rounded to bfloat16.
+template <int IO_BF16, int BITS, int G>
+__device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
+  using C = SplitCfg<BITS, G>;
+  float* kin = (float*)(sm + C::O_UNION);
+  uint16_t* knew = (uint16_t*)(sm + C::O_UNION + C::O_NEW);
+  uint16_t* vnew = knew + D;
+  const int tid = threadIdx.x;
+  const int64_t row = ((int64_t)si * a.g.n_kv + h) * D;
+  if (tid < D)
+    kin[tid] = load_io<IO_BF16>(a.k_new, row + tid);
+  else
+    vnew[tid - D] = io_to_bf16<IO_BF16>(a.v_new, row + tid - D);
+  __syncthreads();
+  if (tid < D) {
+    const float4* tp = (const float4*)(a.tk + ((int64_t)h * D + tid) * D);
+    double acc = 0.0;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {  // half a row of T_K in flight at a time
+      float4 t4[D / 8];
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) t4[c] = tp[hb * (D / 8) + c];
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const float* kx = kin + 4 * (hb * (D / 8) + c);
+        acc = fma((double)t4[c].x, (double)kx[0], acc);
+        acc = fma((double)t4[c].y, (double)kx[1], acc);
+        acc = fma((double)t4[c].z, (double)kx[2], acc);
+        acc = fma((double)t4[c].w, (double)kx[3], acc);
+      }
+    }
+    knew[tid] = f64_to_bf16(acc);
+  }
+  __syncthreads();
+}
+
+// After the window partial is written: quantize the ring entries leaving the
+// recent window at length Lq ([sq, squant(Lq)) minus the new position), then
+// store the new entry in the sink, the ring or, when the window has no room
+// for it, as codes.  Threads 0..127 handle key dimensions, 128..255 value
+// dimensions.
+template <int BITS, int G>
+__device__ void step_append(const DecodeArgs& a, int64_t unit, int Lq, int sq, uint32_t* sm) {
+  using C = SplitCfg<BITS, G>;
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x, i = tid & (D - 1);
+  const bool is_v = tid >= D;
+  const int L0 = Lq - 1;
+  const int sq1 = squant_of(Lq, g.S, g.R, g.F);
+  QLds& ql = *(QLds*)(sm + C::O_UNION);
+  const uint16_t* knew = (const uint16_t*)(sm + C::O_UNION + C::O_NEW);
+  const uint16_t* vnew = knew + D;
+  VRow vr;
+  vr.blk = -1;
+  __syncthreads();  // window scores in the union are dead
+  const int e1 = sq1 < L0 ? sq1 : L0;
+  for (int p = sq; p < e1; ++p) {
+    const int64_t row = (unit * g.W + (p - g.S) % g.W) * D + i;
+    const float x = bf16_bits_to_f32(is_v ? a.pl.vring[row] : a.pl.kring[row]);
+    store_quantized(p, x, x, ql, vr, a.pl, unit, g);
+  }
+  __syncthreads();  // ring reads above complete before the ring write below
+  const uint16_t nb = is_v ? vnew[i] : knew[i];
+  if (L0 < g.S) {
+    const int64_t o = (unit * g.S + L0) * D + i;
+    (is_v ? a.pl.vsink : a.pl.ksink)[o] = nb;
+  } else if (L0 >= sq1) {
+    const int64_t o = (unit * g.W + (L0 - g.S) % g.W) * D + i;
+    (is_v ? a.pl.vring : a.pl.kring)[o] = nb;
+  } else {
+    const float x = bf16_bits_to_f32(nb);
+    store_quantized(L0, x, x, ql, vr, a.pl, unit, g);
+  }
+  vrow_flush(vr, a.pl, unit, g);
+}
+
 // ---------------------------------------------------------------- window
 
 template <int BITS, int G>
@@ -547,37 +645,63 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
                              float (&m_out)[G], float (&l_out)[G]) {
   using C = SplitCfg<BITS, G>;
   const Geometry& g = a.g;
-  const int tid = threadIdx.x, half = tid & 1;
-  const int i = tid & (D - 1), grp = tid >> 7;
+  const int tid = threadIdx.x, half = tid & 1, lane = tid & 63, wv = tid >> 6;
   const float* qs = (const float*)(sm + C::O_QF);
   float* obuf = (float*)(sm + C::O_OBUF);
   float* red = (float*)(sm + C::O_RED);
   float* scw = (float*)(sm + C::O_UNION);  // [G][WINDOW_MAX]
+  const uint16_t* knew = (const uint16_t*)(sm + C::O_UNION + C::O_NEW);
+  const uint16_t* vnew = knew + D;
+  float* part = (float*)(sm + C::O_UNION + C::O_WPART);  // [4 waves][G][D]
   const int ns = Lq < g.S ? Lq : g.S;
   const int ntok = ns + (Lq > sq ? Lq - sq : 0);
-  for (int tok = tid >> 1; tok < ntok; tok += 128) {
+  // decode step: the newest position is read from LDS
+  const int pnew = a.k_new ? Lq - 1 : -1;
+  auto row_of = [&](int tok, const uint16_t* sink, const uint16_t* ring,
+                    const uint16_t* nw) -> const uint16_t* {
     const int p = tok < ns ? tok : sq + (tok - ns);
-    const uint16_t* src = tok < ns ? a.pl.ksink + (unit * g.S + p) * D
-                                   : a.pl.kring + (unit * g.W + (p - g.S) % g.W) * D;
-    const uint4* s4 = (const uint4*)(src + half * 64);
-    float dot[G];
+    return p == pnew ? nw
+           : tok < ns ? sink + (unit * g.S + p) * D
+                      : ring + (unit * g.W + (p - g.S) % g.W) * D;
+  };
+
+  // ---- scores: a lane pair per token (64 dimensions each), two tokens per
+  // pair with all their loads in flight together
+  for (int base = 0; base < ntok; base += 256) {
+    uint4 kb[2][8];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) dot[gg] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const int tok = base + 128 * u + (tid >> 1);
+      if (tok < ntok) {
+        const uint4* s4 = (const uint4*)(row_of(tok, a.pl.ksink, a.pl.kring, knew) + half * 64);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 w = s4[c];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = bf16_to_f32((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) dot[gg] = fmaf(qs[gg * D + half * 64 + c * 8 + e], x, dot[gg]);
+        for (int c = 0; c < 8; ++c) kb[u][c] = s4[c];
       }
     }
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float d2 = dot[gg] + __int_as_float(swap_adjacent(__float_as_int(dot[gg])));
-      if (!half) scw[gg * WINDOW_MAX + tok] = d2;
+    for (int u = 0; u < 2; ++u) {
+      const int tok = base + 128 * u + (tid >> 1);
+      if (tok < ntok) {  // uniform within a lane pair
+        float dot[G];
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) dot[gg] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t ww[4] = {kb[u][c].x, kb[u][c].y, kb[u][c].z, kb[u][c].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = bf16_to_f32((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg)
+              dot[gg] = fmaf(qs[gg * D + half * 64 + c * 8 + e], x, dot[gg]);
+          }
+        }
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float d2 = dot[gg] + __int_as_float(swap_adjacent(__float_as_int(dot[gg])));
+          if (!half) scw[gg * WINDOW_MAX + tok] = d2;
+        }
+      }
     }
   }
   __syncthreads();
@@ -598,26 +722,58 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
       scw[gg * WINDOW_MAX + t] = p;
     }
   }
-  block_reduce<G, false>(ls, red);
-  __syncthreads();
-  float acc[G];
+  block_reduce<G, false>(ls, red);  // its barriers also publish the weights
+
+  // ---- o = sum_t p_t v_t: thread = (8 dimensions, token lane of 16); eight
+  // rows per thread in flight per round of 128 tokens
+  const int dg = tid & 15, tl = tid >> 4;
+  float acc[G][8];
 #pragma unroll
-  for (int gg = 0; gg < G; ++gg) acc[gg] = 0.f;
-  for (int tok = grp; tok < ntok; tok += 2) {
-    const int p = tok < ns ? tok : sq + (tok - ns);
-    const uint16_t* src = tok < ns ? a.pl.vsink + (unit * g.S + p) * D
-                                   : a.pl.vring + (unit * g.W + (p - g.S) % g.W) * D;
-    const float x = bf16_to_f32(src[i]);
+  for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) acc[gg] = fmaf(scw[gg * WINDOW_MAX + tok], x, acc[gg]);
+    for (int e = 0; e < 8; ++e) acc[gg][e] = 0.f;
+  for (int base = 0; base < ntok; base += 128) {
+    uint4 vb[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tok = base + 16 * r + tl;
+      vb[r] = tok < ntok ? ((const uint4*)row_of(tok, a.pl.vsink, a.pl.vring, vnew))[dg]
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tok = base + 16 * r + tl;
+      if (tok < ntok) {
+        const uint32_t ww[4] = {vb[r].x, vb[r].y, vb[r].z, vb[r].w};
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float pw = scw[gg * WINDOW_MAX + tok];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[gg][e] = fmaf(pw, bf16_to_f32((uint16_t)(ww[e >> 1] >> ((e & 1) * 16))), acc[gg][e]);
+        }
+      }
+    }
   }
-  if (grp == 1)
+  // the four token lanes of a wave are 16 lanes apart
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) obuf[gg * D + i] = acc[gg];
+  for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[gg][e] += __shfl_xor(acc[gg][e], 16);
+      acc[gg][e] += __shfl_xor(acc[gg][e], 32);
+    }
+  if (lane < 16)
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[(wv * G + gg) * D + dg * 8 + e] = acc[gg][e];
   __syncthreads();
-  if (grp == 0)
+  if (tid < D)
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) obuf[gg * D + i] += acc[gg];
+    for (int gg = 0; gg < G; ++gg)
+      obuf[gg * D + tid] = (part[gg * D + tid] + part[(G + gg) * D + tid]) +
+                           (part[(2 * G + gg) * D + tid] + part[(3 * G + gg) * D + tid]);
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     m_out[gg] = mx[gg];
@@ -656,6 +812,7 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
   float m[G], l[G];
   if (!empty) {
     if (j == a.n_splits) {
+      if (a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
     } else {
@@ -707,6 +864,7 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
       }
     }
   }
+  if (a.k_new && j == a.n_splits) step_append<BITS, G>(a, unit, Lq, sq, sm);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the

@@ -13,6 +13,7 @@
 #include "common.h"
 
 namespace wkv {
+namespace {
 
 // ---------------------------------------------------------------- formats
 
@@ -30,7 +31,7 @@ __device__ __forceinline__ uint64_t shift_rne(uint64_t m, int s) {
 }
 
 // fp64 -> bfloat16 bits, round to nearest even, gradual underflow, overflow to inf.
-__device__ uint16_t f64_to_bf16(double x) {
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   uint64_t b = (uint64_t)__double_as_longlong(x);
   uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
   int ef = (int)((b >> 52) & 0x7FF);
@@ -59,7 +60,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // fp64 -> binary16 bits, round to nearest even, saturating at +-65504.
-__device__ uint16_t f64_to_f16_sat(double x) {
+__device__ __forceinline__ uint16_t f64_to_f16_sat(double x) {
   uint64_t b = (uint64_t)__double_as_longlong(x);
   uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
   int ef = (int)((b >> 52) & 0x7FF);
@@ -93,7 +94,7 @@ struct QLds {
 };
 
 // Linear-interpolation percentile of the sorted group (fp64, no FMA).
-__device__ double percentile_sorted(const float* sorted, double p) {
+__device__ __forceinline__ double percentile_sorted(const float* sorted, double p) {
 #pragma clang fp contract(off)
   double h = p * (double)(D - 1);
   double jf = floor(h);
@@ -108,7 +109,7 @@ __device__ double percentile_sorted(const float* sorted, double p) {
 // Quantize groups of 128 values: thread t holds element t % 128 of group
 // t / 128 (x).  Returns this thread's code; *sz gets {s16 | z16 << 16} of its
 // group.  Every thread of the workgroup must call it (it uses barriers).
-__device__ int quantize_group(float x, QLds& L, double p_lo, double p_hi, int bits, uint32_t* sz) {
+__device__ __forceinline__ int quantize_group(float x, QLds& L, double p_lo, double p_hi, int bits, uint32_t* sz) {
 #pragma clang fp contract(off)
   const int i = threadIdx.x & (D - 1), grp = threadIdx.x >> 7;
   float* vals = L.vals[grp];
@@ -146,37 +147,45 @@ __device__ int quantize_group(float x, QLds& L, double p_lo, double p_hi, int bi
 
 // Accumulates value-code bits of one dimension row for consecutive positions
 // and writes each 16-byte row once (read-modify-write keeps other positions).
+// Named fields rather than arrays keep the row in registers.
 struct VRow {
   int blk;
-  uint32_t buf[4];
-  uint32_t msk[4];
+  uint32_t b0, b1, b2, b3;  // code bits
+  uint32_t m0, m1, m2, m3;  // which bits are set
 };
 
 __device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl, int64_t unit, const Geometry& g) {
   if (r.blk < 0) return;
   uint4* p = (uint4*)(pl.vcode + ((unit * g.ctx_blocks + r.blk) * D + (threadIdx.x & (D - 1))) * 16);
   uint4 old = *p;
-  old.x = (old.x & ~r.msk[0]) | r.buf[0];
-  old.y = (old.y & ~r.msk[1]) | r.buf[1];
-  old.z = (old.z & ~r.msk[2]) | r.buf[2];
-  old.w = (old.w & ~r.msk[3]) | r.buf[3];
+  old.x = (old.x & ~r.m0) | r.b0;
+  old.y = (old.y & ~r.m1) | r.b1;
+  old.z = (old.z & ~r.m2) | r.b2;
+  old.w = (old.w & ~r.m3) | r.b3;
   *p = old;
   r.blk = -1;
 }
 
 __device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes& pl, int64_t unit,
                                          const Geometry& g) {
-  int blk = p / g.vblock;
+  const int blk = p / g.vblock;
   if (blk != r.blk) {
     vrow_flush(r, pl, unit, g);
     r.blk = blk;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) r.buf[w] = r.msk[w] = 0u;
+    r.b0 = r.b1 = r.b2 = r.b3 = r.m0 = r.m1 = r.m2 = r.m3 = 0u;
   }
-  int bit = (p % g.vblock) * g.bits;
-  uint32_t m = (1u << g.bits) - 1u;
-  r.buf[bit >> 5] |= (uint32_t)code << (bit & 31);
-  r.msk[bit >> 5] |= m << (bit & 31);
+  const int bit = (p % g.vblock) * g.bits;
+  const int w = bit >> 5;
+  const uint32_t cv = (uint32_t)code << (bit & 31);
+  const uint32_t mv = ((1u << g.bits) - 1u) << (bit & 31);
+  r.b0 |= w == 0 ? cv : 0u;
+  r.b1 |= w == 1 ? cv : 0u;
+  r.b2 |= w == 2 ? cv : 0u;
+  r.b3 |= w == 3 ? cv : 0u;
+  r.m0 |= w == 0 ? mv : 0u;
+  r.m1 |= w == 1 ? mv : 0u;
+  r.m2 |= w == 2 ? mv : 0u;
+  r.m3 |= w == 3 ? mv : 0u;
 }
 
 // Quantize key and value entries of position p and store codes and
@@ -184,7 +193,7 @@ __device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes&
 // vx) and the two groups run one after the other.  256-thread workgroups:
 // threads 0..127 hold the key entry (kx), threads 128..255 the value entry
 // (vx) and both groups run at once.
-__device__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, const Planes& pl,
+__device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, const Planes& pl,
                                 int64_t unit, const Geometry& g) {
   const int i = threadIdx.x & (D - 1);
   const bool two = blockDim.x == 2 * D;
@@ -192,8 +201,10 @@ __device__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, co
   uint32_t ksz = 0, vsz = 0;
   int kc = 0, vc = 0;
   if (two) {
-    const int c = quantize_group(is_v ? vx : kx, L, g.p_lo, g.p_hi, g.bits, is_v ? &vsz : &ksz);
-    (is_v ? vc : kc) = c;
+    uint32_t sz = 0;
+    const int c = quantize_group(is_v ? vx : kx, L, g.p_lo, g.p_hi, g.bits, &sz);
+    kc = vc = c;
+    ksz = vsz = sz;
   } else {
     kc = quantize_group(kx, L, g.p_lo, g.p_hi, g.bits, &ksz);
     vc = quantize_group(vx, L, g.p_lo, g.p_hi, g.bits, &vsz);
@@ -213,4 +224,5 @@ __device__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, co
   __syncthreads();  // codes[] reuse
 }
 
+}  // namespace
 }  // namespace wkv

@@ -6,8 +6,8 @@ from __future__ import annotations
 import torch
 
 from . import (WUSHKV_IO_BF16, WUSHKV_IO_FP32, make_config, wushkv_append, wushkv_cache_create,
-               wushkv_cache_destroy, wushkv_decode_attn, wushkv_decode_workspace_bytes,
-               wushkv_get_len, wushkv_layout, wushkv_reset_seq)
+               wushkv_cache_destroy, wushkv_decode_attn, wushkv_decode_step,
+               wushkv_decode_workspace_bytes, wushkv_get_len, wushkv_layout, wushkv_reset_seq)
 
 
 class DeviceCache:
@@ -79,4 +79,22 @@ class DeviceCache:
         ws = self.workspace(n_seq)
         wushkv_decode_attn(self.handle, layer, slots, q.data_ptr(), tq.data_ptr(), out.data_ptr(),
                            ws.data_ptr(), ws.numel(), self._stream())
+        return out
+
+    def decode_step(self, layer: int, slots, k: torch.Tensor, v: torch.Tensor, tk: torch.Tensor,
+                    q: torch.Tensor, tq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Append one position per sequence and attend to all positions (new one
+        included, flush after the attention); k, v are [n_seq][n_kv][128]."""
+        for t in (k, v, q):
+            assert t.dtype == self.io_dtype and t.is_contiguous() and t.device == self.device
+        for t in (tk, tq):
+            assert t.dtype == torch.float32 and t.is_contiguous() and t.device == self.device
+        n_seq = len(slots)
+        if out is None:
+            out = torch.empty((n_seq, self.cfg.n_q_heads, 128), dtype=torch.float32,
+                              device=self.device)
+        ws = self.workspace(n_seq)
+        wushkv_decode_step(self.handle, layer, slots, k.data_ptr(), v.data_ptr(), tk.data_ptr(),
+                           q.data_ptr(), tq.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                           self._stream())
         return out

@@ -174,9 +174,34 @@ wushkv_status wushkv_decode_attn(wushkv_cache* cache, int32_t layer, int32_t n_s
                                  const int32_t* slots, const void* q, const float* tq, float* out,
                                  void* ws, uint64_t ws_bytes, void* stream);
 
+/*
+ * One decode step of one layer for n_seq sequences (distinct slots, each with
+ * length L >= 0 and L + 1 <= ctx_cap): append one new position per sequence
+ * and attend the queries to all L + 1 positions, in the order of section 4.4
+ * -- the new entry is attended in full precision together with the recent
+ * window, and the window is flushed afterwards.  The attention therefore sees
+ * squant(L) as its quantized boundary (L + 1 - squant(L) <= recent + flush
+ * bfloat16 window entries plus the sink), and the cache left behind is the
+ * one wushkv_append with n_new = 1 would leave (boundary squant(L + 1)).
+ * Equivalent to wushkv_append with recent + 1 followed by wushkv_decode_attn,
+ * in two kernel launches.
+ *
+ *   k, v  device, io_dtype [n_seq][n_kv_heads][d]: the new position's
+ *         post-RoPE key and its value (as in wushkv_append).
+ *   tk    device, float32 [n_kv_heads][d][d] = T_K (as in wushkv_append).
+ *   q, tq, out, ws  as in wushkv_decode_attn.
+ * EUNSUPPORTED if sink + recent + flush > 1024 (the window one workgroup
+ * holds); ECAPACITY if any L + 1 > ctx_cap.  Updates the host lengths on
+ * success; a failing call changes nothing.
+ */
+wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_seq,
+                                 const int32_t* slots, const void* k, const void* v,
+                                 const float* tk, const void* q, const float* tq, float* out,
+                                 void* ws, uint64_t ws_bytes, void* stream);
+
 /* Instrumentation, not part of the method.  When ev_start and ev_stop are
  * hipEvent_t handles (created by the caller), every later wushkv_decode_attn
- * call on this cache records ev_start on its stream immediately before the
+ * or wushkv_decode_step call on this cache records ev_start on its stream immediately before the
  * split-K scan kernel and ev_stop immediately after it, so that a caller can
  * time that kernel alone.  Pass NULL, NULL to stop.  Host only. */
 wushkv_status wushkv_set_split_events(wushkv_cache* cache, void* ev_start, void* ev_stop);

@@ -144,6 +144,30 @@ def test_decode_errors():
     wk.wushkv_cache_destroy(h)
 
 
+def test_decode_step_errors():
+    h, _ = _fake_cache()
+    P = 1 << 41
+    need = wk.wushkv_decode_workspace_bytes(h, 2)
+    step = lambda slots, k=P, tk=P, out=P, ws=need: wk.wushkv_decode_step(
+        h, 0, slots, k, P, tk, P, P, out, P, ws, check=False)
+    assert step([0, 1], ws=need - 1) == wk.WUSHKV_EWORKSPACE
+    assert step([1, 1]) == wk.WUSHKV_EINVAL                  # duplicate slot
+    assert step([0], k=0) == wk.WUSHKV_EINVAL                # null key
+    assert step([0], tk=P + 4) == wk.WUSHKV_EINVAL           # misaligned T_K
+    assert step([0], out=P + 4) == wk.WUSHKV_EINVAL          # misaligned output
+    assert wk.wushkv_decode_step(h, 2, [0], P, P, P, P, P, P, P, need, check=False) == \
+        wk.WUSHKV_EINVAL                                     # layer range
+    for s in range(4):
+        assert wk.wushkv_get_len(h, 0, s) == (0, 4)
+    wk.wushkv_cache_destroy(h)
+    # a window of sink + recent + flush = 1025 entries passes the config check
+    # (the append path needs one fewer) but not the fused step
+    h, _ = _fake_cache(recent=1020)
+    assert wk.wushkv_decode_step(h, 0, [0], P, P, P, P, P, P, P, need, check=False) == \
+        wk.WUSHKV_EUNSUPPORTED
+    wk.wushkv_cache_destroy(h)
+
+
 def test_reset_and_status_strings():
     h, _ = _fake_cache()
     wk.wushkv_reset_seq(h, 3)

@@ -129,6 +129,28 @@ def check_attention(got, ref):
         assert err <= ATOL_REL * np.max(np.abs(ref[j])), (j, err, np.max(np.abs(ref[j])))
 
 
+def _check_state(dc, w, ks, vs, T):
+    """T and Q stages for every (sequence, KV head) of layer 0 against the
+    oracle's cache at the sequences' full lengths; returns the oracle units."""
+    units = _oracle_units(w, ks, vs, T, dc)
+    for (si, h), orc in units.items():
+        assert dc.get_len(0, si) == (orc["L"], orc["squant"])
+        gpu = read_unit(dc, 0, si, h, orc["L"])
+        check_windows(gpu, orc)
+        check_codes(gpu, orc, dc.cfg.bits)
+    return units
+
+
+def _reference_attention(w, T, q_seq, units_of_head):
+    """Oracle attention of one sequence's G*n_kv query heads over oracle units."""
+    K = np.stack([oracle.readback(units_of_head[h])[0] for h in range(w.n_kv)])
+    V = np.stack([oracle.readback(units_of_head[h])[1] for h in range(w.n_kv)])
+    qc = np.concatenate([oracle.compensate(T[h].astype(np.float64),
+                                           q_seq[h * w.group:(h + 1) * w.group].double().numpy())
+                         for h in range(w.n_kv)])
+    return oracle.attention(qc, K, V)
+
+
 def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None, lengths=None,
              check_attn=True):
     lengths = lengths or w.lengths()
@@ -139,23 +161,13 @@ def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None
     slots = list(range(len(lengths)))
     _append_all(dc, 0, slots, ks, vs, T, plan)
     torch.cuda.synchronize()
-    units = _oracle_units(w, ks, vs, T, dc)
-    for (si, h), orc in units.items():
-        assert dc.get_len(0, si) == (orc["L"], orc["squant"])
-        gpu = read_unit(dc, 0, si, h, orc["L"])
-        check_windows(gpu, orc)
-        check_codes(gpu, orc, dc.cfg.bits)
+    units = _check_state(dc, w, ks, vs, T)
     if not check_attn:
         return dc
     q = synth.queries(w, 0, 0, len(lengths))
     out = dc.decode_attn(0, slots, q.cuda(), torch.from_numpy(Tq).cuda()).cpu().numpy()
     for si in range(len(lengths)):
-        K = np.stack([oracle.readback(units[(si, h)])[0] for h in range(w.n_kv)])
-        V = np.stack([oracle.readback(units[(si, h)])[1] for h in range(w.n_kv)])
-        qc = np.concatenate([oracle.compensate(T[h].astype(np.float64),
-                                               q[si, h * w.group:(h + 1) * w.group].double().numpy())
-                             for h in range(w.n_kv)])
-        ref = oracle.attention(qc, K, V)
+        ref = _reference_attention(w, T, q[si], {h: units[(si, h)] for h in range(w.n_kv)})
         check_attention(out[si], ref)
     return dc
 
@@ -290,3 +302,98 @@ def test_decode_twice_bitwise_deterministic():
     a = dc.decode_attn(0, [0], q, tq).clone()
     b = dc.decode_attn(0, [0], q, tq).clone()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ decode step
+
+def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_every=1):
+    """Prefill L0s[i] positions per sequence with wushkv_append, then n_steps
+    fused decode steps.  Each step's output is checked against the oracle's
+    attention over the state before the flush (section 4.4: the new entry
+    joins the bfloat16 window, flushed after the attention) -- the oracle cache
+    at length L + 1 with recent + 1 -- and the final cache against the oracle
+    cache at its length."""
+    lengths = [L0 + n_steps for L0 in L0s]
+    dc = _cache(w, bits=bits, S=S, R=R, F=F, max_batch=len(lengths), ctx_cap=max(lengths))
+    c = dc.cfg
+    T, Tq = synth.transforms(w, 0)
+    ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
+    slots = list(range(len(lengths)))
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    if any(L0s):
+        kk = torch.cat([ks[i][:L0s[i]] for i in slots]).cuda().contiguous()
+        vv = torch.cat([vs[i][:L0s[i]] for i in slots]).cuda().contiguous()
+        dc.append(0, slots, list(L0s), kk, vv, tk)
+    for st in range(n_steps):
+        pos = [L0 + st for L0 in L0s]
+        k1 = torch.stack([ks[i][pos[i]] for i in slots]).cuda().contiguous()
+        v1 = torch.stack([vs[i][pos[i]] for i in slots]).cuda().contiguous()
+        q = synth.queries(w, 0, st, len(slots))
+        out = dc.decode_step(0, slots, k1, v1, tk, q.cuda(), tq)
+        if st % check_every and st != n_steps - 1:
+            continue
+        out = out.cpu().numpy()
+        for si in slots:
+            Lq = pos[si] + 1
+            units = {h: oracle.cache_unit(ks[si][:Lq, h].double().numpy(),
+                                          vs[si][:Lq, h].double().numpy(),
+                                          T[h].astype(np.float64), S=c.sink, R=c.recent + 1,
+                                          F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi)
+                     for h in range(w.n_kv)}
+            check_attention(out[si], _reference_attention(w, T, q[si], units))
+    torch.cuda.synchronize()
+    _check_state(dc, w, ks, vs, T)
+    return dc
+
+
+def test_decode_step_cfg0_after_prefill():
+    """fp32 io, 4 query heads on 1 KV head: prefill 900, then 24 steps (one
+    ring entry quantized after each attention)."""
+    _run_steps(synth.WORKLOADS[0], [900], 24)
+
+
+@pytest.mark.parametrize("S,R,F", [(4, 8, 1), (0, 6, 1), (4, 0, 1), (2, 5, 3), (16, 32, 16)])
+def test_decode_step_from_empty(S, R, F):
+    """Steps from an empty sequence through the sink, the ring filling, and the
+    first flushes (batched for flush > 1; the new entry itself quantized right
+    after its attention when recent = 0)."""
+    _run_steps(synth.WORKLOADS[0], [0], 60, S=S, R=R, F=F)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_decode_step_gqa_ragged(bits):
+    """bf16 io, 32 query / 8 KV heads, three sequences of different lengths
+    (one starting empty) in each call."""
+    _run_steps(synth.WORKLOADS[1], [1500, 0, 777], 5, bits=bits, check_every=2)
+
+
+def test_decode_step_same_cache_as_append():
+    """The cache a decode step leaves equals the one wushkv_append (n_new = 1)
+    leaves, bit for bit, over steps that quantize and steps that do not."""
+    w = synth.WORKLOADS[1]
+    L0, n = 400, 40
+    dc = _cache(w, S=4, R=16, F=4, max_batch=2, ctx_cap=L0 + n)
+    T, Tq = synth.transforms(w, 0)
+    k, v = _inputs(w, 0, 0, L0 + n)
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    dc.append(0, [0, 1], [L0, L0], torch.cat([k[:L0], k[:L0]]).cuda(),
+              torch.cat([v[:L0], v[:L0]]).cuda(), tk)
+    for st in range(n):
+        p = L0 + st
+        k1 = k[p:p + 1].cuda().contiguous()
+        v1 = v[p:p + 1].cuda().contiguous()
+        q = synth.queries(w, 0, st, 1).cuda()
+        dc.decode_step(0, [0], k1, v1, tk, q, tq)
+        dc.append(0, [1], [1], k1, v1, tk)
+        dc.decode_attn(0, [1], q, tq)
+    torch.cuda.synchronize()
+    L = L0 + n
+    assert dc.get_len(0, 0) == dc.get_len(0, 1)
+    for h in range(w.n_kv):
+        a = read_unit(dc, 0, 0, h, L)
+        b = read_unit(dc, 0, 1, h, L)
+        sq = a["squant"]
+        for key in ("kcodes", "vcodes", "ks16", "kz16", "vs16", "vz16"):
+            assert np.array_equal(a[key][4:sq], b[key][4:sq]), key
+        for key in ("kwin", "vwin"):
+            assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
