@@ -33,6 +33,103 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+# sources of the split kernel: a traffic figure measured on other sources is not reported
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_wushkv_amd", "csrc", f)
+                  for f in ("decode.hip", "common.h", "quant.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str, path: str) -> str:
+    return os.path.join(PROFILES, f"split_kernel_{workload}_{path}_hbm_traffic.txt")
+
+
+def stored_traffic(workload: str, path: str):
+    """Calibrated HBM bytes per split launch from the counter summary, or None
+    when there is none or it was measured on other kernel sources."""
+    f = traffic_file(workload, path)
+    if not os.path.exists(f):
+        return None
+    kv = {}
+    for line in open(f):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def _counter_rows(csv_path):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib, workload, path, commands, algo_bytes):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    into the calibrated per-launch traffic of the split kernel.  The copy
+    kernel of copy_mib MiB (read copy_mib, write copy_mib) gives the scale of
+    each counter."""
+    import statistics
+    out = {}
+    for name, csv_path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = _counter_rows(csv_path)
+        copy = max(v for (d, n), v in per.items() if "copyBuffer" in n)
+        split = [v for (d, n), v in per.items() if "split_kernel" in n]
+        factor = copy_mib * 1024.0 / copy
+        out[name] = dict(copy_kib=copy, factor=factor, split_kib=statistics.median(split),
+                         n=len(split))
+    traffic = sum(o["split_kib"] * o["factor"] * 1024 for o in out.values())
+    lines = [
+        f"# HBM traffic of the split kernel, workload {workload}, path {path}",
+        "# rocprofv3 counters per dispatch (KiB), median over the split launches, scaled by",
+        f"# what the same counter reads for a device copy of {copy_mib} MiB",
+        "# commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
+    ] + [f"#   {c}" for c in commands] + [
+        f"FETCH_SIZE_copy_kib: {out['FETCH_SIZE']['copy_kib']:.0f}",
+        f"FETCH_SIZE_factor: {out['FETCH_SIZE']['factor']:.4f}",
+        f"FETCH_SIZE_split_median_kib: {out['FETCH_SIZE']['split_kib']:.0f}",
+        f"WRITE_SIZE_copy_kib: {out['WRITE_SIZE']['copy_kib']:.0f}",
+        f"WRITE_SIZE_factor: {out['WRITE_SIZE']['factor']:.4f}",
+        f"WRITE_SIZE_split_median_kib: {out['WRITE_SIZE']['split_kib']:.0f}",
+        f"split_launches_counted: {out['FETCH_SIZE']['n']}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"algorithmic_bytes_per_launch: {algo_bytes:.0f}",
+        f"traffic_over_algorithmic: {traffic / algo_bytes:.4f}",
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(stats_csv, commands, top=8):
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# rocprofv3 --kernel-trace --stats summary (durations in microseconds)",
+             "# command (run from /tmp with TMPDIR=/tmp; R = repository root):"]
+    lines += [f"#   {c}" for c in commands]
+    lines.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>9} {'max_us':>10} {'pct':>6}  kernel")
+    # this library's kernels first, then the largest others (input generation)
+    rows = [r for r in rows if "wkv::" in r["Name"]] + [r for r in rows if "wkv::" not in r["Name"]][:3]
+    for r in rows[:top]:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        name = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}  {name}")
+    lines.append(f"kernel_source_sha256_16: {kernel_source_hash()}")
+    return "\n".join(lines) + "\n"
 
 
 def squant(L, S, R, F):
@@ -95,7 +192,31 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (hardware-counter "
                          "calibration: bytes fetched/written by a copy of known size)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV",
+                    help="write the kernel-trace summary from rocprofv3 --stats output and exit")
+    ap.add_argument("--commands", nargs="*", default=[], help="profiling commands to record")
     args = ap.parse_args()
+    if args.summarize_pmc or args.summarize_trace:
+        from decode_attention_wushkv_amd import synth
+        w = synth.WORKLOADS[args.workload]
+        bits = args.bits or w.bits[0]
+        if args.summarize_trace:
+            out = os.path.join(PROFILES, f"decode_{args.path}_{w.name}_kernel_stats.txt")
+            text = summarize_trace(args.summarize_trace, args.commands)
+        else:
+            L = max(w.lengths())
+            algo = sum(w.n_kv * unit_bytes(t, w.sink, w.recent, w.flush, bits, args.path == "step")
+                       for t in w.lengths())
+            out = traffic_file(w.name, args.path)
+            text = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                                 args.copy_calibration_mib, w.name, args.path, args.commands, algo)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(out, "w") as fh:
+            fh.write(text)
+        print(out)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path is a per-GPU "
                                    "kernel (head or context sharding across GPUs is not built)",
@@ -243,6 +364,9 @@ def main():
     achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
     append_tok_s = B * w.n_layers * K / (total_ms * 1e-3)
 
+    traffic = stored_traffic(w.name, args.path)
+    if traffic is not None:
+        traffic = int(traffic)
     res = {
         "metric": "2-bit KV decode attn: cache GB/s & % HBM peak; append tokens/s",
         "value": round(value, 2),
@@ -266,7 +390,7 @@ def main():
         "append": {"tokens_per_s": round(append_tok_s, 1),
                    "note": "one-token appends per (sequence, layer) inside the timed steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "split_kernel (split-K scan over codes + windows"
                                + (", fused one-token append)" if fused else ")"),
                      "bytes_per_launch": int(bytes_per_launch),

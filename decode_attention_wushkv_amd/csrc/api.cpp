@@ -266,6 +266,8 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   a.tq = tq;
   a.out = out;
   a.wsp = (float*)ws;
+  a.xcd_map = 1;  // used when the unit count is a multiple of 8
+  a.contig = 0;
   if (step) {
     a.k_new = k;
     a.v_new = v;

@@ -791,21 +791,36 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
   float* obuf = (float*)(sm + C::O_OBUF);
 
   const Geometry& g = a.g;
-  const int j = blockIdx.x, h = blockIdx.y, si = blockIdx.z, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int nsp = a.n_splits + 1;  // workgroups per (sequence, KV head)
+  int j, u;
+  if (a.xcd_map) {
+    const int r = blockIdx.x >> 3;
+    u = (blockIdx.x & 7) + 8 * (r / nsp);
+    j = r % nsp;
+  } else {
+    u = blockIdx.x / nsp;
+    j = blockIdx.x % nsp;
+  }
+  const int h = u % g.n_kv, si = u / g.n_kv;
   const int slot = a.s.slot[si], Lq = a.s.len[si], sq = a.s.squant[si];
   const int64_t unit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
   const int qbase = si * g.n_q + h * G;
-  const int nsp = gridDim.x;
 
-  // the quantized region [S, sq) in sub-chunks of TW positions; this
-  // workgroup's waves take every (4 n_splits)-th one starting at 4 j + wave
+  // the quantized region [S, sq) in sub-chunks of TW positions, spread over
+  // the 4 n_splits waves of this (sequence, KV head): interleaved (wave k
+  // takes k, k + nw, ...) or one contiguous run per wave
   const int lo = g.S, hi = sq;
   const int c_first = lo / C::TW;
   const int c_end = hi > lo ? (hi + C::TW - 1) / C::TW : c_first;
+  const int nw = 4 * a.n_splits;
+  const int64_t nsub = c_end - c_first;
   bool empty;
   if (j == a.n_splits) {
     const int ns = Lq < g.S ? Lq : g.S;
     empty = ns + (Lq > sq ? Lq - sq : 0) == 0;
+  } else if (a.contig) {
+    empty = (nsub * (4 * j + 4)) / nw == (nsub * 4 * j) / nw;
   } else {
     empty = c_first + 4 * j >= c_end;
   }
@@ -816,16 +831,25 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
     } else {
-      const int w = tid >> 6;
-      const int c0 = c_first + 4 * j + w;
+      const int w = tid >> 6, wi = 4 * j + w;
+      int c0, cstride, cend;
+      if (a.contig) {
+        c0 = c_first + (int)((nsub * wi) / nw);
+        cend = c_first + (int)((nsub * (wi + 1)) / nw);
+        cstride = 1;
+      } else {
+        c0 = c_first + wi;
+        cend = c_end;
+        cstride = nw;
+      }
       // first sub-chunk's codes in flight while the query is compensated
       SubBuf<BITS, G> A;
-      if (c0 < c_end) load_sub<BITS, G>(A, a, unit, c0 * C::TW);
+      if (c0 < cend) load_sub<BITS, G>(A, a, unit, c0 * C::TW);
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       uint32_t* wbase = sm + C::O_UNION;
       float* part = (float*)(wbase + 4 * C::WAVE);  // [4][G][D + 2]
       float* pw = part + w * G * (D + 2);
-      quant_wave<BITS, G>(a, unit, c0, 4 * a.n_splits, c_end, lo, hi, sm, wbase + w * C::WAVE, pw,
+      quant_wave<BITS, G>(a, unit, c0, cstride, cend, lo, hi, sm, wbase + w * C::WAVE, pw,
                           pw + G * D, pw + G * D + G, A);
       __syncthreads();
       // merge the four wave partials (a wave without sub-chunks has l = 0)
@@ -938,8 +962,10 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     if (fill < 1) fill = 1;
     if (a.n_splits > fill) a.n_splits = fill;
   }
-  dim3 gs(a.n_splits + 1, a.g.n_kv, a.n_seq);
-  hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G>), gs, dim3(256), lds, st, a);
+  const int units = a.n_seq * a.g.n_kv;
+  a.xcd_map = a.xcd_map && units % 8 == 0;
+  hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G>), dim3((a.n_splits + 1) * units), dim3(256), lds,
+                     st, a);
   return hipGetLastError();
 }
 
