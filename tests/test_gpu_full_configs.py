@@ -1,0 +1,127 @@
+"""Parity at the full sizes of the three large workloads, on sampled units, in
+the launch configuration the benchmark times:
+
+  * qwen3-8b-36L-b32-ragged4k-16k  36 layers, 32 sequences of lengths
+    U[4096, 16384], 32 query / 8 KV heads, 2-bit;
+  * mha-32L-32kv-128k              32 layers x 32 KV heads, 131072 positions;
+  * qwen3-32b-64L-b8-prefill64k    64 layers, 8 sequences x 65536 prefill
+    positions, 64 query / 8 KV heads, at 2 and 4 bits.
+
+Each test allocates the whole cache (every layer, full batch and capacity) and
+fills the sampled layers through the library: one prefill wushkv_append of all
+sequences at their full lengths (inputs drawn on the device by the seeded
+generator), then one fused wushkv_decode_step.  Sampled (layer, sequence, KV
+head) units are then checked completely against the oracle: every window
+entry, every code and binary16 scale/zero after the step (the state at L + 1,
+flushed entry included), and the attention output of the unit's G query heads
+against the oracle's attention over its own cache before the flush (section
+4.4 of the paper page: the new entry is attended in full precision).  Layers
+that are not sampled stay empty: each layer is an independent launch of the
+same geometry, and the last layer, the one at the largest arena offsets, is
+always sampled.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_wushkv_amd import synth
+from decode_attention_wushkv_amd.device_cache import DeviceCache
+
+from cachepack import read_unit
+from gpu_checks import check_attention, check_codes, check_windows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_attention_wushkv_amd import build
+    if build.is_stale():
+        build.build()
+    torch.cuda.set_device(0)
+
+
+def _run(wid, bits, layers, units_per_layer, seed):
+    w = synth.WORKLOADS[wid]
+    lengths = w.lengths()
+    B = len(lengths)
+    slots = list(range(B))
+    dc = DeviceCache(n_layers=w.n_layers, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits,
+                     sink=w.sink, recent=w.recent, flush=w.flush, p_lo=w.p_lo, p_hi=w.p_hi,
+                     max_batch=B, ctx_cap=max(lengths) + 1, io_dtype=w.torch_io, device="cuda")
+    rng = np.random.default_rng(seed)
+    G, S, R, F = w.group, w.sink, w.recent, w.flush
+    for layer in layers:
+        sample = [(int(rng.integers(B)), int(rng.integers(w.n_kv))) for _ in range(units_per_layer)]
+        print(f"[full] {w.name} {bits}-bit layer {layer} units {sample}", flush=True)
+        T, Tq = synth.transforms(w, layer)
+        tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+        scales = synth.channel_scales(w, layer)
+        host = {}
+        parts_k, parts_v = [], []
+        for si in slots:
+            k, v = synth.keys_values(w, layer, si, 0, lengths[si], device="cuda", scales=scales)
+            k1, v1 = synth.keys_values(w, layer, si, lengths[si], 1, device="cuda", scales=scales)
+            for (s2, h) in sample:
+                if s2 == si:
+                    host[(si, h)] = (torch.cat([k[:, h], k1[:, h]]).double().cpu().numpy(),
+                                     torch.cat([v[:, h], v1[:, h]]).double().cpu().numpy())
+            parts_k.append(k)
+            parts_v.append(v)
+        kk, vv = torch.cat(parts_k), torch.cat(parts_v)
+        del parts_k, parts_v
+        dc.append(layer, slots, lengths, kk, vv, tk)
+        del kk, vv
+        new = [synth.keys_values(w, layer, si, lengths[si], 1, device="cuda", scales=scales)
+               for si in slots]
+        k1 = torch.cat([x[0] for x in new]).contiguous()
+        v1 = torch.cat([x[1] for x in new]).contiguous()
+        q = synth.queries(w, layer, 0, B, device="cuda")
+        out = dc.decode_step(layer, slots, k1, v1, tk, q, tq).cpu().numpy()
+        torch.cuda.synchronize()
+        qh = q.double().cpu().numpy()
+        for (si, h) in sample:
+            keys, values = host[(si, h)]
+            L1 = lengths[si] + 1
+            assert dc.get_len(layer, si)[0] == L1
+            # cache after the step: the oracle state at L + 1
+            orc = oracle.cache_unit(keys, values, T[h].astype(np.float64), S=S, R=R, F=F,
+                                    bits=bits, p_lo=w.p_lo, p_hi=w.p_hi)
+            gpu = read_unit(dc, layer, si, h, L1)
+            check_windows(gpu, orc)
+            check_codes(gpu, orc, bits)
+            # attention before the flush: boundary squant(L), new entry in bf16
+            sq0 = oracle.squant(L1 - 1, S, R, F)
+            K = orc["k_bf16"].copy()
+            V = orc["v_bf16"].copy()
+            qp = np.arange(S, sq0)
+            K[qp] = oracle.dequantize(orc["kcodes"][qp], orc["ks16"][qp], orc["kz16"][qp])
+            V[qp] = oracle.dequantize(orc["vcodes"][qp], orc["vs16"][qp], orc["vz16"][qp])
+            qc = oracle.compensate(T[h].astype(np.float64), qh[si, h * G:(h + 1) * G])
+            ref = oracle.attention(qc, K[None], V[None])
+            check_attention(out[si, h * G:(h + 1) * G], ref)
+    del dc
+    torch.cuda.empty_cache()
+
+
+def test_full_ragged_batch_36_layers():
+    """Ragged batch of 32 at 4K-16K: two layers, four sampled units each."""
+    w = synth.WORKLOADS[2]
+    _run(2, 2, [5, w.n_layers - 1], 4, seed=21)
+
+
+def test_full_mha_128k():
+    """32 KV heads at 131072 positions: two layers, two sampled units each."""
+    w = synth.WORKLOADS[3]
+    _run(3, 2, [0, w.n_layers - 1], 2, seed=31)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_full_prefill_64k(bits):
+    """8 sequences x 65536 prefill positions, G = 8: one layer (the last),
+    three sampled units."""
+    w = synth.WORKLOADS[4]
+    _run(4, bits, [w.n_layers - 1], 3, seed=41 + bits)

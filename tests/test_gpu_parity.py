@@ -20,10 +20,9 @@ from decode_attention_wushkv_amd import synth
 from decode_attention_wushkv_amd.device_cache import DeviceCache
 
 from cachepack import read_unit, write_unit
+from gpu_checks import ATOL_REL, check_attention, check_codes, check_windows, reference_attention
 
 pytestmark = pytest.mark.gpu
-
-ATOL_REL = 2e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -78,57 +77,6 @@ def _oracle_units(w, ks, vs, T, dc):
     return units
 
 
-def check_windows(gpu, orc):
-    """T stage: bf16 window entries equal the oracle's rounding of T k (and of v)."""
-    L, S, sq = orc["L"], orc["S"], orc["squant"]
-    win = np.r_[np.arange(0, min(S, L)), np.arange(max(sq, S), L)].astype(int)
-    if win.size == 0:
-        return 0
-    amb = orc["k_ambiguous"][win]
-    gk, ok_ = gpu["kwin"][win], orc["k_bf16"][win]
-    assert np.array_equal(gk[~amb], ok_[~amb]), "window keys differ from bf16(T k)"
-    assert np.array_equal(gpu["vwin"][win], orc["v_bf16"][win]), "window values differ"
-    return int(amb.sum())
-
-
-def check_codes(gpu, orc, bits):
-    """Q stage on every quantized position (groups whose transformed keys hold an
-    undecided bf16 rounding are compared on values only)."""
-    q = np.asarray(orc["qpos"], dtype=int)
-    if q.size == 0:
-        return dict(n=0)
-    stats = {}
-    for kind in ("k", "v"):
-        gc = gpu[f"{kind}codes"][q].astype(int)
-        oc = orc[f"{kind}codes"][q].astype(int)
-        u = orc[f"{kind}u"][q]
-        gs, gz = gpu[f"{kind}s16"][q], gpu[f"{kind}z16"][q]
-        os_, oz = orc[f"{kind}s16"][q], orc[f"{kind}z16"][q]
-        if kind == "k":
-            skip = orc["k_ambiguous"][q].any(axis=1)
-        else:
-            skip = np.zeros(q.size, dtype=bool)
-        keep = ~skip
-        rel = lambda a, b: np.abs(a - b) / np.maximum(np.abs(b), 1e-30)
-        assert np.all(rel(gs[keep], os_[keep]) <= 1e-6), f"{kind} scale mismatch"
-        assert np.all(np.abs(gz[keep] - oz[keep]) <= 1e-6 * np.abs(oz[keep])), f"{kind} zero mismatch"
-        mism = (gc != oc) & keep[:, None]
-        frac = mism.sum() / max(1, keep.sum() * 128)
-        assert frac <= 1e-4, f"{kind} code mismatch fraction {frac}"
-        if mism.any():
-            assert np.all(np.abs(gc[mism] - oc[mism]) == 1)
-            uu = u[mism]
-            assert np.all(np.abs(uu - np.floor(uu) - 0.5) <= 1e-5), "mismatch off a boundary"
-        stats[kind] = dict(mismatch=int(mism.sum()), skipped_groups=int(skip.sum()))
-    return stats
-
-
-def check_attention(got, ref):
-    for j in range(ref.shape[0]):
-        err = np.max(np.abs(got[j] - ref[j]))
-        assert err <= ATOL_REL * np.max(np.abs(ref[j])), (j, err, np.max(np.abs(ref[j])))
-
-
 def _check_state(dc, w, ks, vs, T):
     """T and Q stages for every (sequence, KV head) of layer 0 against the
     oracle's cache at the sequences' full lengths; returns the oracle units."""
@@ -139,16 +87,6 @@ def _check_state(dc, w, ks, vs, T):
         check_windows(gpu, orc)
         check_codes(gpu, orc, dc.cfg.bits)
     return units
-
-
-def _reference_attention(w, T, q_seq, units_of_head):
-    """Oracle attention of one sequence's G*n_kv query heads over oracle units."""
-    K = np.stack([oracle.readback(units_of_head[h])[0] for h in range(w.n_kv)])
-    V = np.stack([oracle.readback(units_of_head[h])[1] for h in range(w.n_kv)])
-    qc = np.concatenate([oracle.compensate(T[h].astype(np.float64),
-                                           q_seq[h * w.group:(h + 1) * w.group].double().numpy())
-                         for h in range(w.n_kv)])
-    return oracle.attention(qc, K, V)
 
 
 def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None, lengths=None,
@@ -167,7 +105,7 @@ def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None
     q = synth.queries(w, 0, 0, len(lengths))
     out = dc.decode_attn(0, slots, q.cuda(), torch.from_numpy(Tq).cuda()).cpu().numpy()
     for si in range(len(lengths)):
-        ref = _reference_attention(w, T, q[si], {h: units[(si, h)] for h in range(w.n_kv)})
+        ref = reference_attention(w, T, q[si], {h: units[(si, h)] for h in range(w.n_kv)})
         check_attention(out[si], ref)
     return dc
 
@@ -340,7 +278,7 @@ def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_ever
                                           T[h].astype(np.float64), S=c.sink, R=c.recent + 1,
                                           F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi)
                      for h in range(w.n_kv)}
-            check_attention(out[si], _reference_attention(w, T, q[si], units))
+            check_attention(out[si], reference_attention(w, T, q[si], units))
     torch.cuda.synchronize()
     _check_state(dc, w, ks, vs, T)
     return dc
