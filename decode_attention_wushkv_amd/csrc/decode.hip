@@ -329,7 +329,7 @@ template <int BITS, int G>
 __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase, int lo, int hi,
                                             const uint4 (*qd)[8], const uint32_t* qdw,
                                             const QueryRegs* qr, uint32_t* wsm, float* M,
-                                            float* Lrun, float (*O)[2]) {
+                                            float* Lrun, float* Zrun, float (*O)[2]) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
 
@@ -349,8 +349,9 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
     const int p = pbase + 32 * r + tq;
     const bool ok = p >= lo && p < hi;
     const float ks = f16_to_f32(b.ksz[r] & 0xFFFFu), kz = f16_to_f32(b.ksz[r] >> 16);
-    vs[r] = ok ? f16_to_f32(b.vsz[r] & 0xFFFFu) : 0.f;
-    vz[r] = ok ? f16_to_f32(b.vsz[r] >> 16) : 0.f;
+    const uint32_t vszr = ok ? b.vsz[r] : 0u;  // masked positions: scale and zero 0
+    vs[r] = f16_to_f32(vszr & 0xFFFFu);
+    vz[r] = f16_to_f32(vszr >> 16);
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       int acc[QDIG];
@@ -412,8 +413,7 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
       zsum[gg] = fmaf(pw[r][gg], vz[r], zsum[gg]);
       if (!half) wq[gg * C::TW + slot] = (uint32_t)fminf(rintf(pw[r][gg] * vs[r] * wscale), (float)WMAX);
     }
-    lsum[gg] = wave_sum(lsum[gg]);
-    zsum[gg] = wave_sum(zsum[gg]);
+    // lsum, zsum stay per-lane partials; the wave sums them once at its end
   }
   wave_sync();
 
@@ -491,9 +491,10 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
       float of = (float)pa[gg][e][WDIG - 1];
 #pragma unroll
       for (int k = WDIG - 2; k >= 0; --k) of = fmaf(of, 16.f, (float)pa[gg][e][k]);
-      O[gg][e] = fmaf(O[gg][e], fo, fmaf(of, back, zsum[gg]) * fn);
+      O[gg][e] = fmaf(O[gg][e], fo, of * back * fn);
     }
-    Lrun[gg] = fmaf(Lrun[gg], fo, lsum[gg] * fn);
+    Lrun[gg] = fmaf(Lrun[gg], fo, lsum[gg] * fn);  // per-lane partial
+    Zrun[gg] = fmaf(Zrun[gg], fo, zsum[gg] * fn);  // per-lane partial of sum p z
     M[gg] = Mn;
   }
 }
@@ -521,11 +522,13 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride
       for (int x = 0; x < 8; ++x)
         qd[C::QREG ? gg : 0][x] = *(const uint4*)(qdw + (gg * 16 + half * 8 + x) * DIGP);
   }
-  float M[G], Lrun[G], O[G][2];
+  // running softmax state: M wave-uniform; Lrun and Zrun (sum of p z) per-lane
+  // partials, O per dimension
+  float M[G], Lrun[G], Zrun[G], O[G][2];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     M[gg] = -INFINITY;
-    Lrun[gg] = 0.f;
+    Lrun[gg] = Zrun[gg] = 0.f;
     O[gg][0] = O[gg][1] = 0.f;
   }
   SubBuf<BITS, G> B;
@@ -533,21 +536,23 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride
   while (c < c_end) {
     int cn = c + stride;
     if (cn < c_end) load_sub<BITS, G>(B, a, unit, cn * C::TW);
-    process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, O);
+    process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
     if (c >= c_end) break;
     cn = c + stride;
     if (cn < c_end) load_sub<BITS, G>(A, a, unit, cn * C::TW);
-    process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, O);
+    process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
   }
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    po[gg * D + lane] = O[gg][0];
-    po[gg * D + lane + 64] = O[gg][1];
+    const float Lw = wave_sum(Lrun[gg]);
+    const float Zw = wave_sum(Zrun[gg]);  // zero-point term, the same for every dimension
+    po[gg * D + lane] = O[gg][0] + Zw;
+    po[gg * D + lane + 64] = O[gg][1] + Zw;
     if (lane == 0) {
       pm[gg] = M[gg];
-      pl[gg] = Lrun[gg];
+      pl[gg] = Lw;
     }
   }
 }
