@@ -220,8 +220,19 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
     a.mode = APPEND_EVICT;
     e = launch_append(a, io_bf16, 1, n_seq, st);
     if (e == hipSuccess) {
-      a.mode = APPEND_CHUNKED;
-      e = launch_append(a, io_bf16, max_chunks, n_seq, st);
+      if (io_bf16 && prefill_supported(c->cfg.p_lo, c->cfg.p_hi)) {
+        // key transform on the matrix cores, selection-based percentiles
+        int spans = 1;
+        for (int i = 0; i < n_seq; ++i) {
+          const int base = a.s.len0[i] - a.s.len0[i] % PREFILL_TILE;
+          const int x = (a.s.len0[i] + a.s.n_new[i] - base + PREFILL_SPAN - 1) / PREFILL_SPAN;
+          if (x > spans) spans = x;
+        }
+        e = launch_prefill(a, spans, n_seq, st);
+      } else {
+        a.mode = APPEND_CHUNKED;
+        e = launch_append(a, io_bf16, max_chunks, n_seq, st);
+      }
     }
   }
   if (e != hipSuccess) return WUSHKV_EDEVICE;

@@ -115,6 +115,14 @@ struct DecodeArgs {
 // Host-side launchers (defined in the .hip files); return hipSuccess or the
 // launch error.
 hipError_t launch_append(const AppendArgs& a, int io_bf16, int grid_x, int n_seq, hipStream_t st);
+// Prefill kernel (bfloat16 inputs): workgroups of PREFILL_SPAN positions per
+// (sequence, KV head), in tiles aligned to PREFILL_TILE; grid_x covers the
+// longest run of new positions.  prefill_supported() tells whether the clip
+// percentiles need only the three smallest and three largest values.
+constexpr int PREFILL_TILE = 64;
+constexpr int PREFILL_SPAN = 1024;
+hipError_t launch_prefill(const AppendArgs& a, int grid_x, int n_seq, hipStream_t st);
+bool prefill_supported(double p_lo, double p_hi);
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 

@@ -3,11 +3,11 @@
 // percentile-clipped affine quantizer (WUSH-KV paper page, section 5.3;
 // appendix B.3 for the level grid).
 //
-// Numerics: order statistics come from an exact rank sort of the 128 bfloat16
-// values; the linear-interpolation percentile, the scale (hi - lo)/(2^b - 1),
-// its binary16 rounding and the code coordinate (x - z16)/s16 are fp64 with no
-// fused multiply-add, rounded half to even, so every integer decision matches
-// an fp64 evaluation of the definitions.
+// Numerics: order statistics are exact (rank sort or selection of the 128
+// bfloat16 values); the linear-interpolation percentile, the scale
+// (hi - lo)/(2^b - 1) and its binary16 rounding are fp64 with no fused
+// multiply-add; levels are round-half-to-even of the exact (x - z16)/s16,
+// decided by exact comparisons with the level boundaries.
 #pragma once
 
 #include "common.h"
@@ -106,6 +106,42 @@ __device__ __forceinline__ double percentile_sorted(const float* sorted, double 
   return a + f * (b - a);
 }
 
+// Level assignment.  The boundary between levels c and c + 1 is
+// z16 + (c + 1/2) s16, exact in fp64 (both factors have at most 11
+// significant bits).  A value takes a level above c when it lies above that
+// boundary; a value exactly on it rounds to the even level, so the test is
+// strict for even c.  This is round-half-to-even of the exact (x - z16) / s16,
+// clamped to [0, levels], computed without a division.
+__device__ __forceinline__ bool above_boundary(double x, double zd, double sd, int c) {
+#pragma clang fp contract(off)
+  const double t = zd + ((double)c + 0.5) * sd;
+  return (c & 1) ? x >= t : x > t;
+}
+
+__device__ __forceinline__ int level_of(double x, double zd, double sd, int levels) {
+  if (sd == 0.0) return 0;
+  int c = 0;
+  for (int k = 0; k < levels; ++k) c += above_boundary(x, zd, sd, k) ? 1 : 0;
+  return c;
+}
+
+// Linear-interpolation percentile from the two order statistics around
+// h = p (n - 1): x_j + f (x_{j+1} - x_j), f = h - floor(h) (fp64, no FMA).
+__device__ __forceinline__ double interp(double xj, double xj1, double f) {
+#pragma clang fp contract(off)
+  return xj + f * (xj1 - xj);
+}
+
+// Scale and zero of a group with clip ends lo, hi: s = (hi - lo)/(2^b - 1),
+// z = lo, both rounded to binary16 (saturating).
+__device__ __forceinline__ void scale_zero(double lo, double hi, int bits, uint16_t* s16,
+                                           uint16_t* z16) {
+#pragma clang fp contract(off)
+  const double levels = (double)((1 << bits) - 1);
+  *s16 = f64_to_f16_sat((hi - lo) / levels);
+  *z16 = f64_to_f16_sat(lo);
+}
+
 // Quantize groups of 128 values: thread t holds element t % 128 of group
 // t / 128 (x).  Returns this thread's code; *sz gets {s16 | z16 << 16} of its
 // group.  Every thread of the workgroup must call it (it uses barriers).
@@ -126,20 +162,9 @@ __device__ __forceinline__ int quantize_group(float x, QLds& L, double p_lo, dou
   __syncthreads();
   const double lo = percentile_sorted(sorted, p_lo);
   const double hi = percentile_sorted(sorted, p_hi);
-  const double levels = (double)((1 << bits) - 1);
-  const double s = (hi - lo) / levels;
-  const uint16_t s16 = f64_to_f16_sat(s);
-  const uint16_t z16 = f64_to_f16_sat(lo);
-  const double sd = f16_bits_to_f64(s16);
-  const double zd = f16_bits_to_f64(z16);
-  int c = 0;
-  if (sd != 0.0) {
-    double u = ((double)x - zd) / sd;
-    double r = rint(u);
-    r = r < 0.0 ? 0.0 : r;
-    r = r > levels ? levels : r;
-    c = (int)r;
-  }
+  uint16_t s16, z16;
+  scale_zero(lo, hi, bits, &s16, &z16);
+  const int c = level_of((double)x, f16_bits_to_f64(z16), f16_bits_to_f64(s16), (1 << bits) - 1);
   *sz = (uint32_t)s16 | ((uint32_t)z16 << 16);
   __syncthreads();  // vals / sorted may be reused by the next call
   return c;

@@ -186,6 +186,34 @@ def test_window_variants(S, R, F):
     _run_e2e(w, [513, 1, 1, 70, 1], S=S, R=R, F=F, lengths=[586])
 
 
+def _bf16_workload(L, *, bits=2, S=4, R=128, F=1, p_lo=0.01, p_hi=0.99, n_kv=2, G=4):
+    return synth.Workload(11, "prefill-bf16", 1, n_kv * G, n_kv, 1, L, (bits,), S, R, F, p_lo, p_hi,
+                          "bf16")
+
+
+@pytest.mark.parametrize("S,R,F", [(0, 32, 1), (4, 0, 1), (16, 128, 16), (1, 5, 3)])
+def test_prefill_bf16_window_variants(S, R, F):
+    """bfloat16 inputs take the matrix-core prefill kernel: tiles that start
+    and end mid-block, sink and ring positions inside tiles, flush > 1."""
+    w = _bf16_workload(2900, S=S, R=R, F=F)
+    _run_e2e(w, [37, 2000, 1, 700, 150, 1, 11])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_prefill_bf16_bits(bits):
+    w = _bf16_workload(3000, bits=bits)
+    _run_e2e(w, [1100, 1900])
+
+
+@pytest.mark.parametrize("p_lo,p_hi", [(0.0, 1.0), (0.0157, 0.985), (0.01, 0.995), (0.05, 0.9)])
+def test_prefill_bf16_percentiles(p_lo, p_hi):
+    """Clip percentiles at the ends of what the selection kernel covers (min and
+    max; interpolation between the 2nd and 3rd smallest / 3rd and 2nd largest),
+    and one that falls back to the rank-sort kernel (0.05 / 0.9)."""
+    w = _bf16_workload(1500, p_lo=p_lo, p_hi=p_hi)
+    _run_e2e(w, [1500])
+
+
 def test_short_sequences_sink_only():
     w = synth.WORKLOADS[0]
     _run_e2e(w, [1, 1, 1], lengths=[3])
