@@ -178,6 +178,60 @@ def cpu_baseline(w, bits, seconds, max_units):
                       f"dequantize + fp64 softmax attention, {elapsed:.1f} s"}
 
 
+def prefill_rate(wid, bits, dev, reps=3):
+    """wushkv_append of one full-size layer of a prefill workload (every
+    sequence of the batch at its full length, all KV heads), timed with HIP
+    events: tokens/s and the three ceilings of the kernel."""
+    import numpy as np
+    import torch
+
+    from decode_attention_wushkv_amd import synth
+    from decode_attention_wushkv_amd.device_cache import DeviceCache
+
+    w = synth.WORKLOADS[wid]
+    L = w.lengths()
+    B = len(L)
+    slots = list(range(B))
+    dc = DeviceCache(n_layers=1, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits, sink=w.sink,
+                     recent=w.recent, flush=w.flush, p_lo=w.p_lo, p_hi=w.p_hi, max_batch=B,
+                     ctx_cap=max(L), io_dtype=w.torch_io, device=dev)
+    T, _ = synth.transforms(w, 0)
+    tk = torch.from_numpy(T).to(dev)
+    scales = synth.channel_scales(w, 0)
+    parts = [synth.keys_values(w, 0, s, 0, L[s], device=dev, scales=scales) for s in slots]
+    kk = torch.cat([p[0] for p in parts])
+    vv = torch.cat([p[1] for p in parts])
+    del parts
+    times = []
+    for _ in range(reps + 1):
+        for s in slots:
+            dc.reset_seq(s)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dc.append(0, slots, L, kk, vv, tk)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times[1:]))
+    tokens = sum(L)
+    th = tokens * w.n_kv
+    hbm = th * (512 + 2 * (16 * bits) + 8)      # bf16 k, v in; codes and scale/zero out
+    mac = th * 128 * 128                          # T_K products per layer
+    del dc, kk, vv
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "bits": bits, "layer_ms": round(ms, 4),
+            "tokens_per_s_per_layer": round(tokens / (ms * 1e-3), 1),
+            "tokens_per_s_all_layers": round(tokens / (ms * 1e-3) / w.n_layers, 1),
+            "token_heads_per_s": round(th / (ms * 1e-3), 1),
+            "hbm_gbs": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "transform_tflops": round(2 * mac / (ms * 1e-3) / 1e12, 2),
+            "note": "one layer: every sequence at its full length, all KV heads; bound: VALU "
+                    "(selection and quantization), not HBM or MFMA"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +242,8 @@ def main():
     ap.add_argument("--path", choices=("step", "append+attn"), default="step",
                     help="fused wushkv_decode_step, or wushkv_append then wushkv_decode_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-append measurement")
+    ap.add_argument("--prefill-workload", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (hardware-counter "
@@ -399,6 +455,10 @@ def main():
                                f"{K} steps ({round(total_b_ms / K, 4)} ms/step with the events)"},
         "cache_build_s": round(build_s, 2),
     }
+    if not args.no_prefill:
+        del dc, steps_in, out
+        torch.cuda.empty_cache()
+        res["prefill"] = prefill_rate(args.prefill_workload, bits, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_seconds, max_units=400)
     print(json.dumps(res), flush=True)

@@ -5,9 +5,8 @@
 // One workgroup of 128 threads handles one (sequence, KV head) and a run of
 // positions; thread i owns dimension i of every entry it touches.
 //
-// Numerics: k'_i = sum_j T[i][j] k_j accumulated with fp64 FMAs (fp32 T,
-// fp32/bf16 k: every product is exact in fp64), rounded once to bfloat16
-// (RNE); the quantizer is in quant.h.
+// Numerics: k'_i = sum_j T[i][j] k_j in fp64 (transform_entry in quant.h),
+// rounded once to bfloat16 (RNE); the quantizer is in quant.h.
 #include "quant.h"
 
 namespace wkv {
@@ -93,9 +92,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
     kvec[i] = load_io<IO_BF16>(a.k, row * D + i);
     const uint16_t vb = io_to_bf16<IO_BF16>(a.v, row * D + i);
     __syncthreads();
-    double acc = 0.0;
-#pragma unroll
-    for (int j = 0; j < D; ++j) acc = fma((double)trow[j], (double)kvec[j], acc);
+    const double acc = transform_entry([&](int j) { return trow[j]; }, [&](int j) { return kvec[j]; });
     const uint16_t kb = f64_to_bf16(acc);
     if (p < g.S) {
       const int64_t o = (unit * g.S + p) * D + i;

@@ -565,9 +565,9 @@ __device__ __forceinline__ uint16_t io_to_bf16(const void* base, int64_t idx) {
   return f32_to_bf16(((const float*)base)[idx]);
 }
 
-// The new position's entries as bfloat16 bits in LDS: k' = T_K k with fp64
-// FMAs in dimension order and one rounding (the same arithmetic as the append
-// kernel, so both paths store identical bits), and v rounded to bfloat16.
+// The new position's entries as bfloat16 bits in LDS: k' = T_K k in fp64
+// (transform_entry, the arithmetic of every append path, so all store
+// identical bits) with one rounding, and v rounded to bfloat16.
 template <int IO_BF16, int BITS, int G>
 __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
   using C = SplitCfg<BITS, G>;
@@ -582,22 +582,8 @@ __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
     vnew[tid - D] = io_to_bf16<IO_BF16>(a.v_new, row + tid - D);
   __syncthreads();
   if (tid < D) {
-    const float4* tp = (const float4*)(a.tk + ((int64_t)h * D + tid) * D);
-    double acc = 0.0;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {  // half a row of T_K in flight at a time
-      float4 t4[D / 8];
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) t4[c] = tp[hb * (D / 8) + c];
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const float* kx = kin + 4 * (hb * (D / 8) + c);
-        acc = fma((double)t4[c].x, (double)kx[0], acc);
-        acc = fma((double)t4[c].y, (double)kx[1], acc);
-        acc = fma((double)t4[c].z, (double)kx[2], acc);
-        acc = fma((double)t4[c].w, (double)kx[3], acc);
-      }
-    }
+    const float* tp = a.tk + ((int64_t)h * D + tid) * D;
+    const double acc = transform_entry([&](int j) { return tp[j]; }, [&](int j) { return kin[j]; });
     knew[tid] = f64_to_bf16(acc);
   }
   __syncthreads();

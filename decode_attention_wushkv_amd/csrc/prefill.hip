@@ -10,12 +10,12 @@
 // T = T1 + T2 + T3 (8 + 8 + 8 significant bits), held as MFMA operands in
 // registers for the whole workgroup; bfloat16 keys times bfloat16 parts are
 // exact products, summed by v_mfma_f32_32x32x16_bf16 in fp32: T1 products in
-// four chains of 32, T2 + T3 products in one chain.  A fifth product with
-// |k| and |T| rounded up gives A = sum_j |k_j| |T_ij|, which bounds the fp32
-// error of the sum by 2^-17 A.  An entry whose fp32 value lies within that
-// bound of a bfloat16 rounding boundary is recomputed with the fp64 FMAs, in
-// dimension order, of the one-position path (a few per cent of the entries),
-// so the stored bfloat16 keys are identical to that path's.
+// eight MFMAs of 16 folded into one fp32 sum, T2 and T3 products in one chain
+// each.  A product of |k| and |T1| bounds A = sum_j |k_j| |T_ij|, and 2^-18 A
+// bounds the fp32 error of the sum.  An entry whose fp32 value lies within that bound of
+// a bfloat16 rounding boundary is recomputed in fp64 with the arithmetic of
+// the one-position paths (transform_entry; a few per cent of the entries), so
+// the stored bfloat16 keys are identical to theirs.
 //
 // Quantization.  Each group (one position's 128 key or value entries) is
 // split over a lane pair.  A lane scans its 64 entries keeping the three
@@ -39,10 +39,12 @@ constexpr int PCH = PREFILL_SPAN; // positions per workgroup
 constexpr int RS = 136;           // LDS row stride (bf16 elements) of the key / value tiles
 constexpr int TS = 132;           // LDS row stride (floats) of T_K
 constexpr int FIXMAX = PT * D;    // recomputation list capacity (every entry of a tile)
-// fp32 summation error bound of the transform relative to sum_j |k_j| |T_ij|:
-// 32 products per T1 chain, T2 + T3 below 2^-7 of T, three final additions,
-// one ulp per operation; 2^-17 keeps a margin above the resulting 2^-17.4.
-constexpr float kTransformErr = 7.62939453125e-06f;  // 2^-17
+// fp32 summation error bound of the transform relative to sum_j |k_j| |T_ij|,
+// counting one ulp (2^-23) per rounding: 15 roundings inside each 16-product
+// T1 MFMA, 7 from folding the eight results together, the T2 chain below 2^-8
+// of T (about half an ulp overall), the final additions; 24 ulp = 2^-18.4,
+// and 2^-18 keeps a margin.
+constexpr float kTransformErr = 3.814697265625e-06f;  // 2^-18
 
 struct __align__(16) PLds {
   float t[D * TS];        // T_K rows (fp32)
@@ -60,11 +62,10 @@ __device__ __forceinline__ __bf16 bf16_of_bits(uint32_t b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// bfloat16 bits of |t| rounded up (never below |t|)
-__device__ __forceinline__ uint32_t bf16_abs_up(float t) {
-  uint32_t b = __float_as_uint(t) & 0x7FFFFFFFu;
-  if (b & 0xFFFFu) b += 0x10000u;
-  return b >> 16;
+__device__ __forceinline__ bf16x8 abs_bf16x8(bf16x8 x) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  return as_bf16x8(make_uint4(u.x & 0x7FFF7FFFu, u.y & 0x7FFF7FFFu, u.z & 0x7FFF7FFFu,
+                              u.w & 0x7FFF7FFFu));
 }
 
 // float rounded down / up from a double (exact bounds for comparisons of
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
   __syncthreads();
   // lane: output dim i, k-slice 8 (lane / 32) .. + 8 of each 16-step
   const int i_out = 32 * w + (lane & 31);
-  bf16x8 b1[8], b2[8], b3[8], bab[8];
+  bf16x8 b1[8], b2[8], b3[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
@@ -143,7 +144,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
       b1[ks][e] = bf16_of_bits(t1);
       b2[ks][e] = bf16_of_bits(t2);
       b3[ks][e] = bf16_of_bits(t3);
-      bab[ks][e] = bf16_of_bits(bf16_abs_up(t));
     }
   }
 
@@ -183,33 +183,36 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
     // ---- transform on the matrix cores; flag entries near a rounding boundary
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      f32x16 acc1[4], c23, cab;
+      uint4 av[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc1[q] = f32x16{};
-      c23 = f32x16{};
-      cab = f32x16{};
+      for (int ks = 0; ks < 8; ++ks)
+        av[ks] = *(const uint4*)(L.k + (32 * rb + (lane & 31)) * RS + 16 * ks + 8 * (lane >> 5));
+      // T1 products: one MFMA per 16-step from zero, folded into s1 in fp32
+      f32x16 s1 = f32x16{}, c2 = f32x16{}, c3 = f32x16{}, cab = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const uint4 av = *(const uint4*)(L.k + (32 * rb + (lane & 31)) * RS + 16 * ks + 8 * (lane >> 5));
-        const bf16x8 A = as_bf16x8(av);
-        const bf16x8 Aab = as_bf16x8(make_uint4(av.x & 0x7FFF7FFFu, av.y & 0x7FFF7FFFu,
-                                                av.z & 0x7FFF7FFFu, av.w & 0x7FFF7FFFu));
-        acc1[ks >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b1[ks], acc1[ks >> 1], 0, 0, 0);
-        c23 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b2[ks], c23, 0, 0, 0);
-        c23 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b3[ks], c23, 0, 0, 0);
-        cab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aab, bab[ks], cab, 0, 0, 0);
+        const bf16x8 A = as_bf16x8(av[ks]);
+        const bf16x8 Aab = as_bf16x8(make_uint4(av[ks].x & 0x7FFF7FFFu, av[ks].y & 0x7FFF7FFFu,
+                                                av[ks].z & 0x7FFF7FFFu, av[ks].w & 0x7FFF7FFFu));
+        const f32x16 p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b1[ks], f32x16{}, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b2[ks], c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, b3[ks], c3, 0, 0, 0);
+        cab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aab, abs_bf16x8(b1[ks]), cab, 0, 0, 0);
+        s1 = ks == 0 ? p1 : s1 + p1;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * rb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const float y = ((acc1[0][r] + acc1[1][r]) + (acc1[2][r] + acc1[3][r])) + c23[r];
+        const float y = s1[r] + (c2[r] + c3[r]);
         const uint32_t bits = __float_as_uint(y);
         L.kq[t * RS + i_out] = (uint16_t)((bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16);
         // distance of y to the rounding boundary of its bfloat16 cell
         const int e = (int)((bits >> 23) & 0xFFu);
         const float ulp = __builtin_amdgcn_ldexpf(1.0f, (e > 0 ? e : 1) - 150);
         const float dist = fabsf((float)((int)(bits & 0xFFFFu) - 0x8000)) * ulp;
-        const float err = kTransformErr * cab[r] * 1.0001f;
+        // |T| <= |T1| (1 + 2^-8): cab (1 + 2^-7) bounds sum_j |k_j| |T_ij| with
+        // room for the rounding of cab itself
+        const float err = kTransformErr * cab[r] * 1.0079f;
         const bool near = dist <= err || err >= 16384.0f * ulp;
         if (near && p0 + t >= c0 && p0 + t < c1) {
           const int slot = atomicAdd(&L.nfix, 1);
@@ -224,19 +227,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
       const int nf = L.nfix;
       for (int x = tid; x < nf; x += 256) {
         const int t = L.fix[x] >> 7, i = L.fix[x] & (D - 1);
-        double acc = 0.0;
-        for (int c = 0; c < D / 8; ++c) {
-          const uint4 kk = *(const uint4*)(L.k + t * RS + 8 * c);
-          const float4 ta = *(const float4*)(L.t + i * TS + 8 * c);
-          const float4 tb = *(const float4*)(L.t + i * TS + 8 * c + 4);
-          const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-          const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float kx = bf16_bits_to_f32((uint16_t)(kw[e >> 1] >> (16 * (e & 1))));
-            acc = fma((double)tv[e], (double)kx, acc);
-          }
-        }
+        const uint16_t* kr = L.k + t * RS;
+        const float* tr = L.t + i * TS;
+        const double acc = transform_entry([&](int j) { return tr[j]; },
+                                           [&](int j) { return bf16_bits_to_f32(kr[j]); });
         L.kq[t * RS + i] = f64_to_bf16(acc);
       }
     }

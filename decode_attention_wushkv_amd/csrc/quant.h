@@ -84,6 +84,24 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
   return (double)(float)__builtin_bit_cast(_Float16, h);
 }
 
+// ---------------------------------------------------------------- transform
+
+// k'_i = sum_j T_ij k_j to fp64 accuracy (every fp32 x fp32 product is exact
+// in fp64), in one fixed order shared by every path that stores a transformed
+// key: four partial sums over dimensions [32 q, 32 q + 32), each a chain of
+// fp64 FMAs in dimension order, added as (s0 + s1) + (s2 + s3).  t(j) and
+// k(j) return T_ij and k_j.
+template <typename TF, typename KF>
+__device__ __forceinline__ double transform_entry(TF t, KF k) {
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < D / 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s[q] = fma((double)t(q * (D / 4) + j), (double)k(q * (D / 4) + j), s[q]);
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
 // ---------------------------------------------------------------- quantizer
 
 // LDS scratch of the quantizer for up to two groups of 128 threads.
