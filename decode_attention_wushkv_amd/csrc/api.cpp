@@ -301,7 +301,10 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   // most what fills the GPU once (decided in the launcher), capped by the
   // workspace bound
   int cap = max_chunks(n_seq, c->cfg.n_kv_heads);
-  int need = (max_sub + 3) / 4;
+  // G <= 2: four waves per workgroup on different sub-chunks; G >= 4: the
+  // waves of a workgroup share sub-chunks and split the query heads
+  const int G = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  int need = G >= 4 ? max_sub : (max_sub + 3) / 4;
   a.n_splits = need < cap ? need : cap;
   hipError_t e = launch_decode(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream,
                                c->ev_start, c->ev_stop);

@@ -159,6 +159,10 @@ struct SplitCfg {
   static constexpr int WGW = BITS == 2 ? 2 * WDIG : WDIG;  // digit words per row word
   static constexpr int WGP = (WGW + 3) / 4 * 4;            // ... padded to 16 bytes
   static constexpr bool QREG = G <= 2;         // query digits held in registers
+  // G >= 4: head split (the four waves of a quantized workgroup walk the same
+  // sub-chunks, GW query heads each)
+  static constexpr bool HS = G >= 4;
+  static constexpr int GW = HS ? G / 4 : G;
   // LDS (32-bit words).  Persistent part:
   static constexpr int O_OBUF = 0;                          // [G][D] partial o
   static constexpr int O_RED = O_OBUF + G * D;              // [64] reductions
@@ -499,17 +503,16 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
   }
 }
 
-// One wave: sub-chunks c0, c0 + stride, ... (< c_end) of the quantized region
-// [lo, hi), two sub-chunks of codes in flight; leaves its partial in po/pm/pl.
-// A already holds sub-chunk c0.
+// One wave, G query heads (scales qsc, digit words qdw): sub-chunks c0,
+// c0 + stride, ... (< c_end) of the quantized region [lo, hi), two sub-chunks
+// of codes in flight; leaves the partial (o[D], m, l) of head gg at
+// out + gg * hstride.  A already holds sub-chunk c0.
 template <int BITS, int G>
 __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride, int c_end, int lo,
-                           int hi, const uint32_t* sm, uint32_t* wsm, float* po, float* pm,
-                           float* pl, SubBuf<BITS, G>& A) {
+                           int hi, const float* qsc, const uint32_t* qdw, uint32_t* wsm, float* out,
+                           int64_t hstride, SubBuf<BITS, G>& A) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1;
-  const float* qsc = (const float*)(sm + C::O_QSC);
-  const uint32_t* qdw = sm + C::O_QD;
   uint4 qd[C::QREG ? G : 1][8];
   QueryRegs qr[G];
 #pragma unroll
@@ -548,11 +551,12 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride
   for (int gg = 0; gg < G; ++gg) {
     const float Lw = wave_sum(Lrun[gg]);
     const float Zw = wave_sum(Zrun[gg]);  // zero-point term, the same for every dimension
-    po[gg * D + lane] = O[gg][0] + Zw;
-    po[gg * D + lane + 64] = O[gg][1] + Zw;
+    float* po = out + gg * hstride;       // o[D], m, l of head gg
+    po[lane] = O[gg][0] + Zw;
+    po[lane + 64] = O[gg][1] + Zw;
     if (lane == 0) {
-      pm[gg] = M[gg];
-      pl[gg] = Lw;
+      po[D] = M[gg];
+      po[D + 1] = Lw;
     }
   }
 }
@@ -656,42 +660,66 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
                       : ring + (unit * g.W + (p - g.S) % g.W) * D;
   };
 
-  // ---- scores: a lane pair per token (64 dimensions each), two tokens per
-  // pair with all their loads in flight together
-  for (int base = 0; base < ntok; base += 256) {
-    uint4 kb[2][8];
+  // ---- scores: a lane pair per token (64 dimensions each)
+  if constexpr (G <= 2) {
+    // two tokens per pair with all their loads in flight together
+    for (int base = 0; base < ntok; base += 256) {
+      uint4 kb[2][8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tok = base + 128 * u + (tid >> 1);
-      if (tok < ntok) {
-        const uint4* s4 = (const uint4*)(row_of(tok, a.pl.ksink, a.pl.kring, knew) + half * 64);
+      for (int u = 0; u < 2; ++u) {
+        const int tok = base + 128 * u + (tid >> 1);
+        if (tok < ntok) {
+          const uint4* s4 = (const uint4*)(row_of(tok, a.pl.ksink, a.pl.kring, knew) + half * 64);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) kb[u][c] = s4[c];
+          for (int c = 0; c < 8; ++c) kb[u][c] = s4[c];
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tok = base + 128 * u + (tid >> 1);
-      if (tok < ntok) {  // uniform within a lane pair
-        float dot[G];
+      for (int u = 0; u < 2; ++u) {
+        const int tok = base + 128 * u + (tid >> 1);
+        if (tok < ntok) {  // uniform within a lane pair
+          float dot[G];
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) dot[gg] = 0.f;
+          for (int gg = 0; gg < G; ++gg) dot[gg] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t ww[4] = {kb[u][c].x, kb[u][c].y, kb[u][c].z, kb[u][c].w};
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t ww[4] = {kb[u][c].x, kb[u][c].y, kb[u][c].z, kb[u][c].w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = bf16_to_f32((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+            for (int e = 0; e < 8; ++e) {
+              const float x = bf16_to_f32((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg)
-              dot[gg] = fmaf(qs[gg * D + half * 64 + c * 8 + e], x, dot[gg]);
+              for (int gg = 0; gg < G; ++gg)
+                dot[gg] = fmaf(qs[gg * D + half * 64 + c * 8 + e], x, dot[gg]);
+            }
+          }
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            const float d2 = dot[gg] + __int_as_float(swap_adjacent(__float_as_int(dot[gg])));
+            if (!half) scw[gg * WINDOW_MAX + tok] = d2;
           }
         }
+      }
+    }
+  } else {
+    // many heads: the pair's 64 key values in registers, one head at a time
+    for (int tok = tid >> 1; tok < ntok; tok += 128) {  // uniform within a lane pair
+      const uint4* s4 = (const uint4*)(row_of(tok, a.pl.ksink, a.pl.kring, knew) + half * 64);
+      float xk[64];
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-          const float d2 = dot[gg] + __int_as_float(swap_adjacent(__float_as_int(dot[gg])));
-          if (!half) scw[gg * WINDOW_MAX + tok] = d2;
-        }
+      for (int c = 0; c < 8; ++c) {
+        const uint4 k4 = s4[c];
+        const uint32_t ww[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xk[8 * c + e] = bf16_to_f32((uint16_t)(ww[e >> 1] >> ((e & 1) * 16)));
+      }
+#pragma unroll 1
+      for (int gg = 0; gg < G; ++gg) {
+        const float* qg = qs + gg * D + half * 64;
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) dot = fmaf(qg[j], xk[j], dot);
+        const float d2 = dot + __int_as_float(swap_adjacent(__float_as_int(dot)));
+        if (!half) scw[gg * WINDOW_MAX + tok] = d2;
       }
     }
   }
@@ -775,7 +803,7 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
 // ---------------------------------------------------------------- kernels
 
 template <int IO_BF16, int BITS, int G>
-__global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
   uint32_t* sm = (uint32_t*)smem4;
@@ -810,17 +838,44 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
   if (j == a.n_splits) {
     const int ns = Lq < g.S ? Lq : g.S;
     empty = ns + (Lq > sq ? Lq - sq : 0) == 0;
+  } else if (C::HS) {
+    empty = a.contig ? (nsub * (j + 1)) / a.n_splits == (nsub * j) / a.n_splits
+                     : c_first + j >= c_end;
   } else if (a.contig) {
     empty = (nsub * (4 * j + 4)) / nw == (nsub * 4 * j) / nw;
   } else {
     empty = c_first + 4 * j >= c_end;
   }
   float m[G], l[G];
+  bool direct = false;  // head-split workgroups write their partials themselves
   if (!empty) {
     if (j == a.n_splits) {
       if (a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
+    } else if constexpr (C::HS) {
+      // head split: the four waves walk the same sub-chunks, wave w taking
+      // query heads [w GW, w GW + GW)
+      const int w = tid >> 6;
+      int c0, cstride, cend;
+      if (a.contig) {
+        c0 = c_first + (int)((nsub * j) / a.n_splits);
+        cend = c_first + (int)((nsub * (j + 1)) / a.n_splits);
+        cstride = 1;
+      } else {
+        c0 = c_first + j;
+        cend = c_end;
+        cstride = a.n_splits;
+      }
+      SubBuf<BITS, C::GW> A;
+      if (c0 < cend) load_sub<BITS, C::GW>(A, a, unit, c0 * C::TW);
+      compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
+      float* dst = a.wsp + ((int64_t)(qbase + w * C::GW) * nsp + j) * PS;
+      quant_wave<BITS, C::GW>(a, unit, c0, cstride, cend, lo, hi,
+                              (const float*)(sm + C::O_QSC) + w * C::GW * 4,
+                              sm + C::O_QD + w * C::GW * 16 * DIGP, sm + C::O_UNION + w * C::WAVE,
+                              dst, (int64_t)nsp * PS, A);
+      direct = true;
     } else {
       const int w = tid >> 6, wi = 4 * j + w;
       int c0, cstride, cend;
@@ -838,10 +893,9 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
       if (c0 < cend) load_sub<BITS, G>(A, a, unit, c0 * C::TW);
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       uint32_t* wbase = sm + C::O_UNION;
-      float* part = (float*)(wbase + 4 * C::WAVE);  // [4][G][D + 2]
-      float* pw = part + w * G * (D + 2);
-      quant_wave<BITS, G>(a, unit, c0, cstride, cend, lo, hi, sm, wbase + w * C::WAVE, pw,
-                          pw + G * D, pw + G * D + G, A);
+      float* part = (float*)(wbase + 4 * C::WAVE);  // [4 waves][G][D + 2]
+      quant_wave<BITS, G>(a, unit, c0, cstride, cend, lo, hi, (const float*)(sm + C::O_QSC),
+                          sm + C::O_QD, wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A);
       __syncthreads();
       // merge the four wave partials (a wave without sub-chunks has l = 0)
       const int i = tid & (D - 1), hf = tid >> 7;
@@ -850,16 +904,16 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
         float M = -INFINITY;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float* px = part + x * G * (D + 2);
-          if (px[G * D + G + gg] > 0.f) M = fmaxf(M, px[G * D + gg]);
+          const float* px = part + (x * G + gg) * (D + 2);
+          if (px[D + 1] > 0.f) M = fmaxf(M, px[D]);
         }
         float lsum = 0.f, o = 0.f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float* px = part + x * G * (D + 2);
-          const float f = px[G * D + G + gg] > 0.f ? exp2f(px[G * D + gg] - M) : 0.f;
-          lsum = fmaf(px[G * D + G + gg], f, lsum);
-          o = fmaf(px[gg * D + i], f, o);
+          const float* px = part + (x * G + gg) * (D + 2);
+          const float f = px[D + 1] > 0.f ? exp2f(px[D] - M) : 0.f;
+          lsum = fmaf(px[D + 1], f, lsum);
+          o = fmaf(px[i], f, o);
         }
         if (hf == 0) obuf[gg * D + i] = o;
         m[gg] = M;
@@ -868,7 +922,7 @@ __global__ __launch_bounds__(256, G == 1 ? 3 : (G == 2 ? 2 : 1)) void split_kern
     }
   }
   __syncthreads();
-  if (tid < D) {
+  if (!direct && tid < D) {
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       float* dst = a.wsp + ((int64_t)(qbase + gg) * nsp + j) * PS;
