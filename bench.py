@@ -178,6 +178,87 @@ def cpu_baseline(w, bits, seconds, max_units):
                       f"dequantize + fp64 softmax attention, {elapsed:.1f} s"}
 
 
+def read_ceiling(window_bytes, dev, copies=6):
+    """Practical HBM read ceiling on this GPU: the library's streaming-read
+    kernel over windows of the split launch's size, rotated through `copies`
+    windows so that none is served from the last-level cache; best grid."""
+    import numpy as np
+    import torch
+
+    import decode_attention_wushkv_amd as wk
+
+    win = (int(window_bytes) + 4095) // 4096 * 4096
+    buf = torch.empty(win * copies, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    out = torch.empty(256 * 4096, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    best = 0.0
+    for blocks in (512, 1024, 2048, 4096):
+        for i in range(copies):  # warm
+            wk.wushkv_stream_read_probe(buf.data_ptr() + i * win, win, blocks, out.data_ptr(), stream)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = 4 * copies
+        a.record()
+        for r in range(reps):
+            wk.wushkv_stream_read_probe(buf.data_ptr() + (r % copies) * win, win, blocks,
+                                        out.data_ptr(), stream)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, reps * win / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf, out
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
+def bf16_reference(w, dev, ms_per_step_2bit, layers=4):
+    """Decode attention over a bfloat16 cache of the same shape with plain torch
+    (one query per head: scores = K q, softmax, p V), timed per layer over
+    `layers` distinct layers: the bandwidth the 2-bit cache saves."""
+    import numpy as np
+    import torch
+
+    L = max(w.lengths())
+    B = len(w.lengths())
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    K = [torch.randn((B * w.n_kv, L, 128), generator=g, device=dev, dtype=torch.bfloat16)
+         for _ in range(layers)]
+    V = [torch.randn((B * w.n_kv, L, 128), generator=g, device=dev, dtype=torch.bfloat16)
+         for _ in range(layers)]
+    q = torch.randn((B * w.n_kv, 128, w.group), generator=g, device=dev, dtype=torch.bfloat16)
+
+    def layer(i):
+        sc = torch.bmm(K[i], q).float() * (1.0 / 128 ** 0.5)         # [h, L, G]
+        p = torch.softmax(sc, dim=1).to(torch.bfloat16)
+        pt = p.transpose(1, 2).contiguous()                             # [h, G, L]
+        return torch.bmm(pt, V[i])                                      # [h, G, 128]
+
+    for i in range(layers):
+        layer(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    reps = 3
+    a.record()
+    for r in range(reps):
+        for i in range(layers):
+            layer(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms_layer = a.elapsed_time(b) / (reps * layers)
+    nbytes = 2 * B * w.n_kv * L * 128 * 2
+    del K, V
+    torch.cuda.empty_cache()
+    ms_step = ms_layer * w.n_layers
+    return {"ms_per_layer": round(ms_layer, 4), "ms_per_step": round(ms_step, 3),
+            "cache_bytes_per_step": nbytes * w.n_layers, "gbs": round(nbytes / (ms_layer * 1e-3) / 1e9, 1),
+            "step_speedup_2bit_vs_torch": round(ms_step / ms_per_step_2bit, 2),
+            "note": f"torch bmm/softmax/bmm over bf16 K, V of the same shape, {layers} layers timed, "
+                    "per-layer time x layers"}
+
+
 def prefill_rate(wid, bits, dev, reps=3):
     """wushkv_append of one full-size layer of a prefill workload (every
     sequence of the batch at its full length, all KV heads), timed with HIP
@@ -243,6 +324,8 @@ def main():
                     help="fused wushkv_decode_step, or wushkv_append then wushkv_decode_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-append measurement")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the streaming-read ceiling and the bf16-cache comparison")
     ap.add_argument("--prefill-workload", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -455,9 +538,19 @@ def main():
                                f"{K} steps ({round(total_b_ms / K, 4)} ms/step with the events)"},
         "cache_build_s": round(build_s, 2),
     }
-    if not args.no_prefill:
+    if not args.no_prefill or not args.no_reference:
         del dc, steps_in, out
         torch.cuda.empty_cache()
+    if not args.no_reference:
+        ceil = read_ceiling(bytes_per_launch, dev)
+        res["roofline"]["read_ceiling_gbs"] = ceil
+        res["roofline"]["frac_of_read_ceiling"] = round(achieved / ceil, 4)
+        ref = bf16_reference(w, dev, ms_per_step)
+        # what any kernel needs to read the bf16 cache at the measured ceiling
+        ref["read_bound_ms_per_step"] = round(ref["cache_bytes_per_step"] / (ceil * 1e9) * 1e3, 3)
+        ref["step_speedup_2bit_vs_read_bound"] = round(ref["read_bound_ms_per_step"] / ms_per_step, 2)
+        res["bf16_reference"] = ref
+    if not args.no_prefill:
         res["prefill"] = prefill_rate(args.prefill_workload, bits, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_seconds, max_units=400)

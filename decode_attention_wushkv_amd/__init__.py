@@ -24,7 +24,8 @@ WUSHKV_MAX_SEQ_PER_CALL = 128
 EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_append", "wushkv_decode_workspace_bytes",
-    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events", "wushkv_status_str",
+    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events",
+    "wushkv_stream_read_probe", "wushkv_status_str",
 )
 
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_decode_step.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P, _U64, P]
     L.wushkv_set_split_events.restype = ctypes.c_int
     L.wushkv_set_split_events.argtypes = [P, P, P]
+    L.wushkv_stream_read_probe.restype = ctypes.c_int
+    L.wushkv_stream_read_probe.argtypes = [P, _U64, i32, P, P]
     L.wushkv_status_str.restype = ctypes.c_char_p
     L.wushkv_status_str.argtypes = [ctypes.c_int]
     _lib = L
@@ -191,6 +194,14 @@ def wushkv_decode_step(cache: int, layer: int, slots, k_ptr: int, v_ptr: int, tk
     if check:
         _check(st, "wushkv_decode_step")
     return st
+
+
+def wushkv_stream_read_probe(buf_ptr: int, nbytes: int, blocks: int, out_ptr: int,
+                             stream: int = 0) -> None:
+    """Instrumentation: one grid-stride streaming read of nbytes at buf_ptr."""
+    _check(lib().wushkv_stream_read_probe(ctypes.c_void_p(buf_ptr), int(nbytes), int(blocks),
+                                          ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)),
+           "wushkv_stream_read_probe")
 
 
 def wushkv_set_split_events(cache: int, ev_start: int | None, ev_stop: int | None) -> None:

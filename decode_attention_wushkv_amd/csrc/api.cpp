@@ -337,6 +337,16 @@ extern "C" wushkv_status wushkv_set_split_events(wushkv_cache* c, void* ev_start
   return WUSHKV_OK;
 }
 
+extern "C" wushkv_status wushkv_stream_read_probe(const void* buf, uint64_t bytes, int32_t blocks,
+                                                  void* out, void* stream) {
+  if (!buf || !out || blocks < 1 || bytes < 16 || (bytes % 16) || ((uintptr_t)buf % 16) ||
+      ((uintptr_t)out % 4))
+    return WUSHKV_EINVAL;
+  return launch_stream_read(buf, bytes, blocks, out, (hipStream_t)stream) == hipSuccess
+             ? WUSHKV_OK
+             : WUSHKV_EDEVICE;
+}
+
 extern "C" const char* wushkv_status_str(wushkv_status s) {
   switch (s) {
     case WUSHKV_OK: return "ok";

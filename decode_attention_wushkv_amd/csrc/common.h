@@ -123,6 +123,7 @@ constexpr int PREFILL_TILE = 64;
 constexpr int PREFILL_SPAN = 1024;
 hipError_t launch_prefill(const AppendArgs& a, int grid_x, int n_seq, hipStream_t st);
 bool prefill_supported(double p_lo, double p_hi);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int blocks, void* out, hipStream_t st);
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 

@@ -206,6 +206,14 @@ wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_s
  * time that kernel alone.  Pass NULL, NULL to stop.  Host only. */
 wushkv_status wushkv_set_split_events(wushkv_cache* cache, void* ev_start, void* ev_stop);
 
+/* Instrumentation, not part of the method: read bytes (a multiple of 16) of
+ * the 16-byte-aligned device buffer buf once with a grid-stride kernel of
+ * `blocks` workgroups of 256 threads, writing one word per thread to out
+ * (device, blocks * 256 uint32).  Its bandwidth is the practical HBM read
+ * ceiling the decode kernels are compared with.  Asynchronous on stream. */
+wushkv_status wushkv_stream_read_probe(const void* buf, uint64_t bytes, int32_t blocks, void* out,
+                                       void* stream);
+
 /* Static string for a status code. */
 const char* wushkv_status_str(wushkv_status status);
 
