@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libwushkv.so")
 WUSHKV_OK, WUSHKV_EINVAL, WUSHKV_ECAPACITY, WUSHKV_EWORKSPACE, WUSHKV_EUNSUPPORTED, \
     WUSHKV_EDEVICE = range(6)
 WUSHKV_IO_FP32, WUSHKV_IO_BF16 = 0, 1
+WUSHKV_CODEC_PERCENTILE, WUSHKV_CODEC_RMS = 0, 1
 WUSHKV_MAX_SEQ_PER_CALL = 128
 
 # Symbols the header declares (checked by the test-suite against the .so).
@@ -25,7 +26,7 @@ EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_append", "wushkv_decode_workspace_bytes",
     "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events",
-    "wushkv_stream_read_probe", "wushkv_status_str",
+    "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_status_str",
 )
 
 
@@ -36,6 +37,7 @@ class wushkv_config(ctypes.Structure):
         ("bits", ctypes.c_int32), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
         ("flush", ctypes.c_int32), ("p_lo", ctypes.c_double), ("p_hi", ctypes.c_double),
         ("max_batch", ctypes.c_int32), ("ctx_cap", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("codec", ctypes.c_int32), ("clip_alpha", ctypes.c_double),
     ]
 
 
@@ -93,6 +95,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_decode_step.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P, _U64, P]
     L.wushkv_set_split_events.restype = ctypes.c_int
     L.wushkv_set_split_events.argtypes = [P, P, P]
+    L.wushkv_gaussian_alpha.restype = ctypes.c_double
+    L.wushkv_gaussian_alpha.argtypes = [i32]
     L.wushkv_stream_read_probe.restype = ctypes.c_int
     L.wushkv_stream_read_probe.argtypes = [P, _U64, i32, P, P]
     L.wushkv_status_str.restype = ctypes.c_char_p
@@ -112,9 +116,10 @@ def _i32_array(xs):
 
 
 def make_config(*, n_layers, n_q_heads, n_kv_heads, bits, sink, recent, flush=1, p_lo=0.01,
-                p_hi=0.99, max_batch, ctx_cap, io_dtype, head_dim=128) -> wushkv_config:
+                p_hi=0.99, max_batch, ctx_cap, io_dtype, head_dim=128, codec=WUSHKV_CODEC_PERCENTILE,
+                clip_alpha=0.0) -> wushkv_config:
     return wushkv_config(n_layers, n_q_heads, n_kv_heads, head_dim, bits, sink, recent, flush,
-                         p_lo, p_hi, max_batch, ctx_cap, io_dtype)
+                         p_lo, p_hi, max_batch, ctx_cap, io_dtype, codec, clip_alpha)
 
 
 # ------------------------------------------------------------- C-ABI mirrors
@@ -194,6 +199,10 @@ def wushkv_decode_step(cache: int, layer: int, slots, k_ptr: int, v_ptr: int, tk
     if check:
         _check(st, "wushkv_decode_step")
     return st
+
+
+def wushkv_gaussian_alpha(bits: int) -> float:
+    return float(lib().wushkv_gaussian_alpha(int(bits)))
 
 
 def wushkv_stream_read_probe(buf_ptr: int, nbytes: int, blocks: int, out_ptr: int,

@@ -1,6 +1,7 @@
 // C-ABI entry points of libwushkv: argument checks, arena layout, host-side
 // sequence lengths and kernel launches.  No device memory is allocated here.
 #include <string.h>
+#include <cmath>
 
 #include <new>
 #include <vector>
@@ -20,6 +21,54 @@ struct wushkv_cache {
 
 static uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+// E[(x - Q(x))^2] for x ~ N(0, 1) and Q rounding to the nearest of 2^bits
+// levels -alpha + k delta, delta = 2 alpha / (2^bits - 1).  On a decision
+// interval [a, b] with level y the integral of (x - y)^2 phi(x) is
+// (1 + y^2)(Phi(b) - Phi(a)) - (b phi(b) - a phi(a)) + 2 y (phi(b) - phi(a)).
+static double gaussian_grid_mse(double alpha, int bits) {
+  const int n = 1 << bits;
+  const double delta = 2.0 * alpha / (n - 1);
+  const double inv_sqrt2 = 0.70710678118654752440, inv_sqrt2pi = 0.39894228040143267794;
+  auto Phi = [&](double x) { return 0.5 * std::erfc(-x * inv_sqrt2); };
+  auto phi = [&](double x) { return inv_sqrt2pi * std::exp(-0.5 * x * x); };
+  double total = 0.0;
+  for (int k = 0; k < n; ++k) {
+    const double y = -alpha + delta * k;
+    const bool lo_inf = k == 0, hi_inf = k == n - 1;
+    const double a = y - 0.5 * delta, b = y + 0.5 * delta;
+    const double Pa = lo_inf ? 0.0 : Phi(a), Pb = hi_inf ? 1.0 : Phi(b);
+    const double pa = lo_inf ? 0.0 : phi(a), pb = hi_inf ? 0.0 : phi(b);
+    const double apa = lo_inf ? 0.0 : a * pa, bpb = hi_inf ? 0.0 : b * pb;
+    total += (1.0 + y * y) * (Pb - Pa) - (bpb - apa) + 2.0 * y * (pb - pa);
+  }
+  return total;
+}
+
+extern "C" double wushkv_gaussian_alpha(int32_t bits) {
+  if (bits < 1 || bits > 8) return 0.0;
+  // golden-section search on [0.3, 6]: the error is unimodal in alpha there
+  const double r = 0.61803398874989484820;
+  double lo = 0.3, hi = 6.0;
+  double x1 = hi - r * (hi - lo), x2 = lo + r * (hi - lo);
+  double f1 = gaussian_grid_mse(x1, bits), f2 = gaussian_grid_mse(x2, bits);
+  for (int it = 0; it < 200 && hi - lo > 1e-13; ++it) {
+    if (f1 < f2) {
+      hi = x2;
+      x2 = x1;
+      f2 = f1;
+      x1 = hi - r * (hi - lo);
+      f1 = gaussian_grid_mse(x1, bits);
+    } else {
+      lo = x1;
+      x1 = x2;
+      f1 = f2;
+      x2 = lo + r * (hi - lo);
+      f2 = gaussian_grid_mse(x2, bits);
+    }
+  }
+  return 0.5 * (lo + hi);
+}
+
 extern "C" wushkv_status wushkv_config_check(const wushkv_config* c) {
   if (!c) return WUSHKV_EINVAL;
   if (c->n_layers < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->max_batch < 1 ||
@@ -29,6 +78,8 @@ extern "C" wushkv_status wushkv_config_check(const wushkv_config* c) {
   if (c->sink < 0 || c->recent < 0 || c->flush < 1) return WUSHKV_EINVAL;
   if (!(c->p_lo >= 0.0 && c->p_lo < c->p_hi && c->p_hi <= 1.0)) return WUSHKV_EINVAL;
   if (c->io_dtype != WUSHKV_IO_FP32 && c->io_dtype != WUSHKV_IO_BF16) return WUSHKV_EINVAL;
+  if (c->codec != WUSHKV_CODEC_PERCENTILE && c->codec != WUSHKV_CODEC_RMS) return WUSHKV_EINVAL;
+  if (!(c->clip_alpha >= 0.0 && c->clip_alpha < 1e6)) return WUSHKV_EINVAL;
   if (c->head_dim != D) return WUSHKV_EUNSUPPORTED;
   if (c->bits != 2 && c->bits != 4) return WUSHKV_EUNSUPPORTED;
   {
@@ -147,6 +198,8 @@ static Geometry geometry_of(const wushkv_cache* c) {
   g.max_batch = c->cfg.max_batch;
   g.p_lo = c->cfg.p_lo;
   g.p_hi = c->cfg.p_hi;
+  g.codec = c->cfg.codec;
+  g.alpha = c->cfg.clip_alpha > 0.0 ? c->cfg.clip_alpha : wushkv_gaussian_alpha(c->cfg.bits);
   return g;
 }
 
@@ -220,7 +273,7 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
     a.mode = APPEND_EVICT;
     e = launch_append(a, io_bf16, 1, n_seq, st);
     if (e == hipSuccess) {
-      if (io_bf16 && prefill_supported(c->cfg.p_lo, c->cfg.p_hi)) {
+      if (io_bf16 && prefill_supported(c->cfg.codec, c->cfg.p_lo, c->cfg.p_hi)) {
         // key transform on the matrix cores, selection-based percentiles
         int spans = 1;
         for (int i = 0; i < n_seq; ++i) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/wushkv.h"
+
 namespace wkv {
 
 constexpr int D = 128;          // head_dim (the only one built)
@@ -49,6 +51,8 @@ struct Geometry {
   int S, R, F, W;  // sink, recent, flush, ring slots
   int code_bytes, vblock, ctx_blocks, cpos, max_batch;
   double p_lo, p_hi;
+  int codec;     // WUSHKV_CODEC_PERCENTILE or WUSHKV_CODEC_RMS
+  double alpha;  // RMS codec endpoint (resolved)
 };
 
 // squant(L): end of the quantized region [S, squant) at length L (section 4.4).
@@ -122,7 +126,7 @@ hipError_t launch_append(const AppendArgs& a, int io_bf16, int grid_x, int n_seq
 constexpr int PREFILL_TILE = 64;
 constexpr int PREFILL_SPAN = 1024;
 hipError_t launch_prefill(const AppendArgs& a, int grid_x, int n_seq, hipStream_t st);
-bool prefill_supported(double p_lo, double p_hi);
+bool prefill_supported(int codec, double p_lo, double p_hi);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int blocks, void* out, hipStream_t st);
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);

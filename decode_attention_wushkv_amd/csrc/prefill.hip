@@ -24,7 +24,9 @@
 // percentiles.  This covers clip percentiles whose interpolation needs only
 // the three smallest and three largest values (p_lo (n - 1) < 2 and
 // p_hi (n - 1) >= 125; the host falls back to the rank-sort kernel otherwise).
-// Scale, zero and levels follow quant.h exactly; value-code rows are
+// With the RMS codec the clip ends are -alpha rms, +alpha rms instead (sum of
+// squares per half-group in fp64, as in quant.h).  Scale, zero and levels
+// follow quant.h exactly; value-code rows are
 // assembled in LDS with atomic ORs and written as whole 16-byte rows.
 #include "quant.h"
 
@@ -258,6 +260,30 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
       const int p = p0 + t;
       const bool quant = p >= qlo && p < qhi;
       const uint16_t* row = (isv ? L.v : L.kq) + t * RS + 64 * hh;
+      double lo, hi;
+      if (g.codec == WUSHKV_CODEC_RMS) {
+        // sum of squares of this lane's half in dimension order, then the two
+        // halves in order (quant.h's rms_of_halves)
+        double ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint4 u4 = *(const uint4*)(row + 8 * c);
+          const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double x = (double)__uint_as_float((e & 1) ? (uw[e >> 1] & 0xFFFF0000u)
+                                                            : (uw[e >> 1] << 16));
+            ss = fma(x, x, ss);
+          }
+        }
+        const uint64_t sb = __builtin_bit_cast(uint64_t, ss);
+        const uint64_t pb = (uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)sb, 0xB1, 0xF, 0xF, false) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(sb >> 32), 0xB1, 0xF, 0xF, false) << 32);
+        const double ps = __builtin_bit_cast(double, pb);
+        const double rms = hh == 0 ? rms_of_halves(ss, ps) : rms_of_halves(ps, ss);
+        lo = -g.alpha * rms;
+        hi = g.alpha * rms;
+      } else {
       float a0 = INFINITY, a1 = INFINITY, a2 = INFINITY;
       float bb0 = -INFINITY, bb1 = -INFINITY, bb2 = -INFINITY;
 #pragma unroll
@@ -284,12 +310,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
       }
       // order statistics x(0..2) = a0..a2, x(127..125) = bb0..bb2
       const double lx0 = jlo == 0 ? a0 : a1, lx1 = jlo == 0 ? a1 : a2;
-      const double lo = interp(lx0, lx1, flo);
-      double hi;
+      lo = interp(lx0, lx1, flo);
       if (jhi >= D - 1)
         hi = bb0;
       else
         hi = interp(jhi == D - 2 ? bb1 : bb2, jhi == D - 2 ? bb0 : bb1, fhi);
+      }
       uint16_t s16, z16;
       scale_zero(lo, hi, BITS, &s16, &z16);
       const double sd = f16_bits_to_f64(s16), zd = f16_bits_to_f64(z16);
@@ -398,7 +424,8 @@ hipError_t launch_prefill(const AppendArgs& a, int grid_x, int n_seq, hipStream_
   return hipGetLastError();
 }
 
-bool prefill_supported(double p_lo, double p_hi) {
+bool prefill_supported(int codec, double p_lo, double p_hi) {
+  if (codec == WUSHKV_CODEC_RMS) return true;
   const double hlo = p_lo * (double)(D - 1), hhi = p_hi * (double)(D - 1);
   return (int)floor(hlo) <= 1 && (int)floor(hhi) >= D - 3;
 }

@@ -109,7 +109,16 @@ struct QLds {
   float vals[2][D];
   float sorted[2][D];
   int codes[2][D];
+  double ss[2][2];  // RMS codec: sums of squares of the two halves of each group
 };
+
+// Sum of squares of a group in the order shared by every path: each half
+// [64 h, 64 h + 64) summed in dimension order in fp64 (every square of a
+// bfloat16 value is exact), then half 0 + half 1.  rms = sqrt(sum / 128).
+__device__ __forceinline__ double rms_of_halves(double s0, double s1) {
+#pragma clang fp contract(off)
+  return sqrt((s0 + s1) / (double)D);
+}
 
 // Linear-interpolation percentile of the sorted group (fp64, no FMA).
 __device__ __forceinline__ double percentile_sorted(const float* sorted, double p) {
@@ -160,26 +169,44 @@ __device__ __forceinline__ void scale_zero(double lo, double hi, int bits, uint1
   *z16 = f64_to_f16_sat(lo);
 }
 
-// Quantize groups of 128 values: thread t holds element t % 128 of group
+// Quantize groups of 128 values (clip ends from the percentiles or from the
+// RMS, by the cache's codec): thread t holds element t % 128 of group
 // t / 128 (x).  Returns this thread's code; *sz gets {s16 | z16 << 16} of its
 // group.  Every thread of the workgroup must call it (it uses barriers).
-__device__ __forceinline__ int quantize_group(float x, QLds& L, double p_lo, double p_hi, int bits, uint32_t* sz) {
+__device__ __forceinline__ int quantize_group(float x, QLds& L, const Geometry& g, uint32_t* sz) {
 #pragma clang fp contract(off)
   const int i = threadIdx.x & (D - 1), grp = threadIdx.x >> 7;
+  const int bits = g.bits;
   float* vals = L.vals[grp];
   float* sorted = L.sorted[grp];
   vals[i] = x;
   __syncthreads();
-  int rank = 0;
+  double lo, hi;
+  if (g.codec == WUSHKV_CODEC_RMS) {
+    if ((i & 63) == 0) {
+      double ss = 0.0;
+      for (int j = i; j < i + 64; ++j) {
+        const double v = (double)vals[j];
+        ss = fma(v, v, ss);
+      }
+      L.ss[grp][i >> 6] = ss;
+    }
+    __syncthreads();
+    const double rms = rms_of_halves(L.ss[grp][0], L.ss[grp][1]);
+    lo = -g.alpha * rms;
+    hi = g.alpha * rms;
+  } else {
+    int rank = 0;
 #pragma unroll 8
-  for (int j = 0; j < D; ++j) {
-    float y = vals[j];
-    rank += (y < x) || (y == x && j < i);
+    for (int j = 0; j < D; ++j) {
+      float y = vals[j];
+      rank += (y < x) || (y == x && j < i);
+    }
+    sorted[rank] = x;
+    __syncthreads();
+    lo = percentile_sorted(sorted, g.p_lo);
+    hi = percentile_sorted(sorted, g.p_hi);
   }
-  sorted[rank] = x;
-  __syncthreads();
-  const double lo = percentile_sorted(sorted, p_lo);
-  const double hi = percentile_sorted(sorted, p_hi);
   uint16_t s16, z16;
   scale_zero(lo, hi, bits, &s16, &z16);
   const int c = level_of((double)x, f16_bits_to_f64(z16), f16_bits_to_f64(s16), (1 << bits) - 1);
@@ -245,12 +272,12 @@ __device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds&
   int kc = 0, vc = 0;
   if (two) {
     uint32_t sz = 0;
-    const int c = quantize_group(is_v ? vx : kx, L, g.p_lo, g.p_hi, g.bits, &sz);
+    const int c = quantize_group(is_v ? vx : kx, L, g, &sz);
     kc = vc = c;
     ksz = vsz = sz;
   } else {
-    kc = quantize_group(kx, L, g.p_lo, g.p_hi, g.bits, &ksz);
-    vc = quantize_group(vx, L, g.p_lo, g.p_hi, g.bits, &vsz);
+    kc = quantize_group(kx, L, g, &ksz);
+    vc = quantize_group(vx, L, g, &vsz);
   }
   if (!is_v) L.codes[0][i] = kc;
   __syncthreads();

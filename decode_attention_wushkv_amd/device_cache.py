@@ -13,14 +13,15 @@ from . import (WUSHKV_IO_BF16, WUSHKV_IO_FP32, make_config, wushkv_append, wushk
 class DeviceCache:
     def __init__(self, *, n_layers, n_q_heads, n_kv_heads, bits, sink, recent, flush=1,
                  p_lo=0.01, p_hi=0.99, max_batch, ctx_cap, io_dtype: torch.dtype,
-                 device="cuda"):
+                 device="cuda", codec=0, clip_alpha=0.0):
         io = WUSHKV_IO_BF16 if io_dtype == torch.bfloat16 else WUSHKV_IO_FP32
         if io_dtype not in (torch.bfloat16, torch.float32):
             raise ValueError("io dtype must be bfloat16 or float32")
         self.io_dtype = io_dtype
         self.cfg = make_config(n_layers=n_layers, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                                bits=bits, sink=sink, recent=recent, flush=flush, p_lo=p_lo,
-                               p_hi=p_hi, max_batch=max_batch, ctx_cap=ctx_cap, io_dtype=io)
+                               p_hi=p_hi, max_batch=max_batch, ctx_cap=ctx_cap, io_dtype=io, codec=codec,
+                               clip_alpha=clip_alpha)
         self.layout = wushkv_layout(self.cfg)
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:

@@ -52,6 +52,19 @@ typedef enum {
 
 enum { WUSHKV_IO_FP32 = 0, WUSHKV_IO_BF16 = 1 };
 
+/* Clip ends of a quantization group (one position's 128 key or value
+ * entries):
+ *   PERCENTILE  lo, hi = the p_lo and p_hi linear-interpolation percentiles of
+ *               the group (asymmetric, adaptive zero point; paper section 5.3).
+ *   RMS         lo, hi = -alpha * rms, +alpha * rms with rms the group's root
+ *               mean square: the QuEST-style symmetric grid of 2^b levels from
+ *               -alpha to alpha on the RMS-normalized group (paper appendix
+ *               B.3); alpha defaults to the endpoint minimizing the
+ *               mean-squared error for a standard Gaussian.
+ * Both store s = (hi - lo)/(2^b - 1) and z = lo in binary16 and the level
+ * nearest to (x - z16)/s16, so decoding is the same for both. */
+enum { WUSHKV_CODEC_PERCENTILE = 0, WUSHKV_CODEC_RMS = 1 };
+
 /* Largest number of sequences one append or decode call may name. */
 #define WUSHKV_MAX_SEQ_PER_CALL 128
 
@@ -69,6 +82,8 @@ typedef struct {
   int32_t max_batch;    /* sequence slots                                         */
   int32_t ctx_cap;      /* positions per slot (>= 1)                              */
   int32_t io_dtype;     /* WUSHKV_IO_FP32 or WUSHKV_IO_BF16 for k, v, q inputs   */
+  int32_t codec;        /* WUSHKV_CODEC_PERCENTILE (0) or WUSHKV_CODEC_RMS       */
+  double clip_alpha;    /* RMS codec endpoint; 0 = wushkv_gaussian_alpha(bits)   */
 } wushkv_config;
 
 /*
@@ -112,6 +127,12 @@ typedef struct {
 } wushkv_layout_t;
 
 typedef struct wushkv_cache wushkv_cache;
+
+/* The endpoint alpha minimizing E[(x - Q_alpha(x))^2] for x ~ N(0, 1), with
+ * Q_alpha rounding to the nearest of 2^bits equally spaced levels from -alpha
+ * to alpha (paper appendix B.3's optimal endpoint); computed on the host to
+ * about 1e-12.  0 for bits outside 1..8. */
+double wushkv_gaussian_alpha(int32_t bits);
 
 /* Check a config.  Host only.  EINVAL / EUNSUPPORTED as described above. */
 wushkv_status wushkv_config_check(const wushkv_config* cfg);

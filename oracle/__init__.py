@@ -76,6 +76,9 @@ def _load():
     lib.wko_quantize.restype = ctypes.c_int
     lib.wko_quantize.argtypes = [dp, i64, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_double, ctypes.c_double, u8p, dp, dp, dp]
+    lib.wko_quantize_rms.restype = ctypes.c_int
+    lib.wko_quantize_rms.argtypes = [dp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                     u8p, dp, dp, dp]
     lib.wko_dequantize.argtypes = [u8p, dp, dp, i64, ctypes.c_int, dp]
     lib.wko_squant.restype = i64
     lib.wko_squant.argtypes = [i64, i64, i64, i64]
@@ -174,6 +177,59 @@ def quantize(groups, bits: int, p_lo: float, p_hi: float):
                 z16=z16.reshape(lead), u=u.reshape(g.shape))
 
 
+def quantize_rms(groups, bits: int, alpha: float):
+    """Symmetric quantizer on the RMS-normalized group (appendix B.3's grid of
+    2^b levels from -alpha to alpha, scaled by the group's RMS).  Same outputs
+    as quantize()."""
+    g = _f64(groups)
+    n = g.shape[-1]
+    flat = g.reshape(-1, n)
+    ng = flat.shape[0]
+    codes = np.empty((ng, n), dtype=np.uint8)
+    s16 = np.empty(ng)
+    z16 = np.empty(ng)
+    u = np.empty((ng, n))
+    rc = _load().wko_quantize_rms(_dp(flat), ng, n, int(bits), float(alpha),
+                                  codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                  _dp(s16), _dp(z16), _dp(u))
+    if rc != 0:
+        raise ValueError("wko_quantize_rms: bad arguments")
+    lead = g.shape[:-1]
+    return dict(codes=codes.reshape(g.shape), s16=s16.reshape(lead),
+                z16=z16.reshape(lead), u=u.reshape(g.shape))
+
+
+def gaussian_grid_mse(alpha: float, bits: int) -> float:
+    """E[(zeta - Q_alpha(zeta))^2] for zeta ~ N(0, 1), Q_alpha rounding to the
+    nearest of 2^b equally spaced levels from -alpha to alpha (appendix B.3).
+    Closed form per decision interval [a, b] with level y:
+    (1 + y^2)(Phi(b) - Phi(a)) - (b phi(b) - a phi(a)) + 2 y (phi(b) - phi(a))."""
+    from scipy.stats import norm
+    nlev = 1 << bits
+    delta = 2.0 * alpha / (nlev - 1)
+    levels = -alpha + delta * np.arange(nlev)
+    edges = np.concatenate([[-np.inf], (levels[:-1] + levels[1:]) / 2.0, [np.inf]])
+    total = 0.0
+    for k, y in enumerate(levels):
+        a, b = edges[k], edges[k + 1]
+        Pa, Pb = norm.cdf(a), norm.cdf(b)
+        pa = 0.0 if np.isinf(a) else norm.pdf(a)
+        pb = 0.0 if np.isinf(b) else norm.pdf(b)
+        apa = 0.0 if np.isinf(a) else a * pa
+        bpb = 0.0 if np.isinf(b) else b * pb
+        total += (1.0 + y * y) * (Pb - Pa) - (bpb - apa) + 2.0 * y * (pb - pa)
+    return float(total)
+
+
+def quest_alpha(bits: int) -> float:
+    """The endpoint alpha_b minimizing gaussian_grid_mse (appendix B.3's
+    optimal endpoint), by bounded scalar minimization."""
+    from scipy.optimize import minimize_scalar
+    r = minimize_scalar(lambda a: gaussian_grid_mse(a, bits), bounds=(0.3, 6.0),
+                        method="bounded", options={"xatol": 1e-12, "maxiter": 500})
+    return float(r.x)
+
+
 def dequantize(codes, s16, z16) -> np.ndarray:
     """xhat = z16 + s16 * code."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
@@ -222,7 +278,7 @@ def attention(qc, K, V) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def cache_unit(keys, values, T, *, S: int, R: int, F: int, bits: int,
-               p_lo: float, p_hi: float, positions=None):
+               p_lo: float, p_hi: float, positions=None, alpha=None):
     """State of one (sequence, KV head) cache unit at length L = len(keys).
 
     keys: [L, d] post-RoPE keys; values: [L, d] values already in the value
@@ -234,7 +290,9 @@ def cache_unit(keys, values, T, *, S: int, R: int, F: int, bits: int,
     those bfloat16 values (reading: entries are "first appended in full
     precision").  ``positions`` (optional) restricts the quantizer to a subset
     of the quantized positions (the rest of the arrays are then left as NaN /
-    255) so that large units can be sampled.
+    255) so that large units can be sampled.  ``alpha`` (optional) selects the
+    symmetric RMS-normalized quantizer with that endpoint instead of the
+    percentile clip.
     """
     keys = _f64(keys)
     values = _f64(values)
@@ -254,8 +312,12 @@ def cache_unit(keys, values, T, *, S: int, R: int, F: int, bits: int,
     ku = np.full((L, d), np.nan)
     vu = np.full((L, d), np.nan)
     if qpos.size:
-        qk = quantize(kb[qpos], bits, p_lo, p_hi)
-        qv = quantize(vb[qpos], bits, p_lo, p_hi)
+        if alpha is None:   # percentile clip ends
+            qk = quantize(kb[qpos], bits, p_lo, p_hi)
+            qv = quantize(vb[qpos], bits, p_lo, p_hi)
+        else:               # symmetric, RMS-normalized grid with endpoint alpha
+            qk = quantize_rms(kb[qpos], bits, alpha)
+            qv = quantize_rms(vb[qpos], bits, alpha)
         kcodes[qpos], ks[qpos], kz[qpos], ku[qpos] = qk["codes"], qk["s16"], qk["z16"], qk["u"]
         vcodes[qpos], vs[qpos], vz[qpos], vu[qpos] = qv["codes"], qv["s16"], qv["z16"], qv["u"]
     return dict(L=L, S=S, squant=sq, k_bf16=kb, v_bf16=vb, k_ambiguous=amb,

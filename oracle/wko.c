@@ -142,40 +142,68 @@ double wko_percentile(const double* x, int n, double p, double* scratch) {
 /* [P3 s5.3 quantizer; B.1 one group per column; B.3 level spacing]          */
 /* ------------------------------------------------------------------------ */
 
-/* Quantize n_groups groups of n values each (groups contiguous).
- * Outputs per group: s16, z16 (the stored binary16 scale and zero point),
- * per element: code (0 .. 2^bits - 1) and u = (x - z16) / s16 (the unrounded
- * code coordinate, 0 when s16 == 0; lets callers see rounding boundaries).
- * Returns 0, or -1 on bad arguments. */
+/* One group of n values with clip ends lo <= hi: s = (hi - lo)/(2^b - 1),
+ * z = lo, both rounded to binary16; codes = rint((x - z16)/s16) clamped to
+ * [0, 2^b - 1] (all 0 when s16 == 0); u = the unrounded code coordinate. */
+static void quantize_group_ends(const double* xg, int n, int bits, double lo, double hi,
+                                uint8_t* codes, double* s16, double* z16, double* u) {
+  const double levels = (double)((1 << bits) - 1);
+  double s = (hi - lo) / levels;   /* spacing of 2^b levels over [lo, hi] */
+  double z = lo;                   /* zero point = lower clip end */
+  double sr = wko_fp16(s), zr = wko_fp16(z);
+  *s16 = sr;
+  *z16 = zr;
+  for (int i = 0; i < n; ++i) {
+    double ui = 0.0, c = 0.0;
+    if (sr != 0.0) {
+      ui = (xg[i] - zr) / sr;
+      c = rint(ui);                /* round half to even */
+      if (c < 0.0) c = 0.0;
+      if (c > levels) c = levels;
+    }
+    codes[i] = (uint8_t)c;
+    if (u) u[i] = ui;
+  }
+}
+
+/* Quantize n_groups groups of n values each (groups contiguous), clip ends
+ * at the p_lo and p_hi percentiles of the group (asymmetric, adaptive zero
+ * point).  Outputs per group: s16, z16 (the stored binary16 scale and zero
+ * point), per element: code (0 .. 2^bits - 1) and u = (x - z16) / s16 (the
+ * unrounded code coordinate, 0 when s16 == 0; lets callers see rounding
+ * boundaries).  Returns 0, or -1 on bad arguments. */
 int wko_quantize(const double* x, int64_t n_groups, int n, int bits,
                  double p_lo, double p_hi, uint8_t* codes, double* s16,
                  double* z16, double* u) {
   if (n < 1 || bits < 1 || bits > 8 || !(p_lo <= p_hi)) return -1;
   double* scratch = (double*)malloc(sizeof(double) * (size_t)n);
   if (!scratch) return -1;
-  const double levels = (double)((1 << bits) - 1);
   for (int64_t g = 0; g < n_groups; ++g) {
     const double* xg = x + g * n;
     double lo = wko_percentile(xg, n, p_lo, scratch);
     double hi = wko_percentile(xg, n, p_hi, scratch);
-    double s = (hi - lo) / levels;   /* spacing of 2^b levels over [lo, hi] */
-    double z = lo;                   /* adaptive zero point = lower clip end */
-    double sr = wko_fp16(s), zr = wko_fp16(z);
-    s16[g] = sr;
-    z16[g] = zr;
-    for (int i = 0; i < n; ++i) {
-      double ui = 0.0, c = 0.0;
-      if (sr != 0.0) {
-        ui = (xg[i] - zr) / sr;
-        c = rint(ui);                /* round half to even */
-        if (c < 0.0) c = 0.0;
-        if (c > levels) c = levels;
-      }
-      codes[g * n + i] = (uint8_t)c;
-      if (u) u[g * n + i] = ui;
-    }
+    quantize_group_ends(xg, n, bits, lo, hi, codes + g * n, s16 + g, z16 + g,
+                        u ? u + g * n : 0);
   }
   free(scratch);
+  return 0;
+}
+
+/* The QuEST-style symmetric quantizer [P3 B.3: 2^b equally spaced levels from
+ * -alpha to alpha on the RMS-normalized group]: clip ends -alpha * rms and
+ * +alpha * rms with rms = sqrt(sum_i x_i^2 / n), then the same binary16
+ * scale / zero and codes as above.  Returns 0, or -1 on bad arguments. */
+int wko_quantize_rms(const double* x, int64_t n_groups, int n, int bits, double alpha,
+                     uint8_t* codes, double* s16, double* z16, double* u) {
+  if (n < 1 || bits < 1 || bits > 8 || !(alpha >= 0.0)) return -1;
+  for (int64_t g = 0; g < n_groups; ++g) {
+    const double* xg = x + g * n;
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) ss += xg[i] * xg[i];
+    const double rms = sqrt(ss / (double)n);
+    quantize_group_ends(xg, n, bits, -alpha * rms, alpha * rms, codes + g * n, s16 + g,
+                        z16 + g, u ? u + g * n : 0);
+  }
   return 0;
 }
 

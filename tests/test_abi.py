@@ -177,3 +177,21 @@ def test_reset_and_status_strings():
     for s in range(6):
         assert wk.wushkv_status_str(s)
     assert wk.wushkv_status_str(99) == "unknown status"
+
+
+def test_gaussian_alpha_matches_oracle():
+    """The library's own endpoint computation agrees with the oracle's
+    (independent implementations of the same minimization)."""
+    import oracle
+    for bits in (2, 3, 4):
+        a = wk.wushkv_gaussian_alpha(bits)
+        assert abs(a - oracle.quest_alpha(bits)) <= 1e-6 * a
+    assert wk.wushkv_gaussian_alpha(0) == 0.0 and wk.wushkv_gaussian_alpha(9) == 0.0
+
+
+def test_codec_config_check():
+    assert wk.wushkv_config_check(_cfg(codec=wk.WUSHKV_CODEC_RMS)) == wk.WUSHKV_OK
+    assert wk.wushkv_config_check(_cfg(codec=wk.WUSHKV_CODEC_RMS, clip_alpha=2.0)) == wk.WUSHKV_OK
+    assert wk.wushkv_config_check(_cfg(codec=2)) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_config_check(_cfg(clip_alpha=-1.0)) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_config_check(_cfg(clip_alpha=float("nan"))) == wk.WUSHKV_EINVAL

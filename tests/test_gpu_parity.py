@@ -36,13 +36,20 @@ def _gpu():
 
 
 def _cache(w: synth.Workload, *, bits=None, S=None, R=None, F=None, max_batch=None, ctx_cap=None,
-           p_lo=None, p_hi=None, n_layers=None):
+           p_lo=None, p_hi=None, n_layers=None, rms_alpha=None):
+    codec = {} if rms_alpha is None else dict(codec=1, clip_alpha=rms_alpha)
     return DeviceCache(n_layers=n_layers or 1, n_q_heads=w.n_q, n_kv_heads=w.n_kv,
                        bits=bits or w.bits[0], sink=w.sink if S is None else S,
                        recent=w.recent if R is None else R, flush=F or w.flush,
                        p_lo=p_lo or w.p_lo, p_hi=p_hi or w.p_hi,
                        max_batch=max_batch or w.batch, ctx_cap=ctx_cap or max(w.lengths()),
-                       io_dtype=w.torch_io, device="cuda")
+                       io_dtype=w.torch_io, device="cuda", **codec)
+
+
+def _alpha_of(dc):
+    """The oracle's argument for the cache's codec: None (percentile clip) or
+    the RMS codec's endpoint."""
+    return dc.cfg.clip_alpha if dc.cfg.codec == 1 else None
 
 
 def _inputs(w, layer, seq, L):
@@ -73,7 +80,8 @@ def _oracle_units(w, ks, vs, T, dc):
         for h in range(w.n_kv):
             units[(si, h)] = oracle.cache_unit(
                 k[:, h].double().numpy(), v[:, h].double().numpy(), T[h].astype(np.float64),
-                S=c.sink, R=c.recent, F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi)
+                S=c.sink, R=c.recent, F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi,
+                alpha=_alpha_of(dc))
     return units
 
 
@@ -90,10 +98,10 @@ def _check_state(dc, w, ks, vs, T):
 
 
 def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None, lengths=None,
-             check_attn=True):
+             check_attn=True, rms_alpha=None):
     lengths = lengths or w.lengths()
     dc = _cache(w, bits=bits, S=S, R=R, F=F, p_lo=p_lo, p_hi=p_hi, max_batch=len(lengths),
-                ctx_cap=max(lengths))
+                ctx_cap=max(lengths), rms_alpha=rms_alpha)
     T, Tq = synth.transforms(w, 0)
     ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
     slots = list(range(len(lengths)))
@@ -272,7 +280,8 @@ def test_decode_twice_bitwise_deterministic():
 
 # ------------------------------------------------------------------ decode step
 
-def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_every=1):
+def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_every=1,
+               rms_alpha=None):
     """Prefill L0s[i] positions per sequence with wushkv_append, then n_steps
     fused decode steps.  Each step's output is checked against the oracle's
     attention over the state before the flush (section 4.4: the new entry
@@ -280,7 +289,8 @@ def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_ever
     at length L + 1 with recent + 1 -- and the final cache against the oracle
     cache at its length."""
     lengths = [L0 + n_steps for L0 in L0s]
-    dc = _cache(w, bits=bits, S=S, R=R, F=F, max_batch=len(lengths), ctx_cap=max(lengths))
+    dc = _cache(w, bits=bits, S=S, R=R, F=F, max_batch=len(lengths), ctx_cap=max(lengths),
+                rms_alpha=rms_alpha)
     c = dc.cfg
     T, Tq = synth.transforms(w, 0)
     ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
@@ -304,7 +314,8 @@ def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_ever
             units = {h: oracle.cache_unit(ks[si][:Lq, h].double().numpy(),
                                           vs[si][:Lq, h].double().numpy(),
                                           T[h].astype(np.float64), S=c.sink, R=c.recent + 1,
-                                          F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi)
+                                          F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi,
+                                          alpha=_alpha_of(dc))
                      for h in range(w.n_kv)}
             check_attention(out[si], reference_attention(w, T, q[si], units))
     torch.cuda.synchronize()
@@ -363,3 +374,26 @@ def test_decode_step_same_cache_as_append():
             assert np.array_equal(a[key][4:sq], b[key][4:sq]), key
         for key in ("kwin", "vwin"):
             assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
+
+
+# ------------------------------------------------------------------ RMS codec
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_rms_codec_fp32_path(bits):
+    """The RMS (QuEST-style) codec through the rank-sort kernel (fp32 inputs):
+    prefill, token appends, decode; endpoint = the Gaussian-optimal alpha."""
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [700, 1, 1, 300, 22], bits=bits, rms_alpha=oracle.quest_alpha(bits))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_rms_codec_prefill_kernel(bits):
+    """bf16 inputs: the matrix-core prefill kernel with RMS clip ends, then
+    token appends through the one-position path (both sum squares in the same
+    order)."""
+    w = _bf16_workload(2600, bits=bits)
+    _run_e2e(w, [2000, 1, 1, 598], bits=bits, rms_alpha=oracle.quest_alpha(bits))
+
+
+def test_rms_codec_decode_step():
+    _run_steps(synth.WORKLOADS[0], [500], 12, rms_alpha=1.9)

@@ -365,3 +365,68 @@ def test_cache_unit_nothing_quantized_equals_sdpa_on_bf16():
     got = oracle.attention(qc, K[None], V[None])
     ref = _sdpa(qc, K[None], V[None])
     assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+# ------------------------------------------------------------ RMS (QuEST-style) codec
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("alpha", [0.7, 1.5, 2.5])
+def test_gaussian_grid_mse_matches_numeric_integration(bits, alpha):
+    """Closed-form E[(z - Q_alpha(z))^2] against direct quadrature of the
+    integrand over each decision interval (appendix B.3's grid of 2^b levels
+    from -alpha to alpha)."""
+    from scipy import integrate
+    from scipy.stats import norm
+    n = 1 << bits
+    levels = np.linspace(-alpha, alpha, n)
+    edges = np.concatenate([[-np.inf], (levels[:-1] + levels[1:]) / 2, [np.inf]])
+    total = 0.0
+    for k, y in enumerate(levels):
+        val, _ = integrate.quad(lambda z: (z - y) ** 2 * norm.pdf(z), edges[k], edges[k + 1],
+                                epsabs=1e-14, epsrel=1e-13, limit=200)
+        total += val
+    assert abs(oracle.gaussian_grid_mse(alpha, bits) - total) <= 1e-10
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_gaussian_alpha_optimal_and_monte_carlo(bits):
+    a = oracle.quest_alpha(bits)
+    f = oracle.gaussian_grid_mse(a, bits)
+    for d in (1e-3, -1e-3, 1e-2, -1e-2):
+        assert oracle.gaussian_grid_mse(a + d, bits) > f
+    # the error of that grid on Gaussian samples
+    z = np.random.default_rng(7 + bits).standard_normal(1_000_000)
+    n = 1 << bits
+    delta = 2 * a / (n - 1)
+    c = np.clip(np.rint((z + a) / delta), 0, n - 1)
+    mse = np.mean((z - (-a + delta * c)) ** 2)
+    assert abs(mse - f) <= 0.01 * f
+    # more levels, wider optimal endpoint and smaller error
+    if bits > 2:
+        assert a > oracle.quest_alpha(bits - 1)
+        assert f < oracle.gaussian_grid_mse(oracle.quest_alpha(bits - 1), bits - 1)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize_rms_brute_force(bits):
+    """Clip ends -alpha rms, +alpha rms; binary16 scale and zero; each code is
+    the nearest level z16 + c s16 (ties to the even level), by exhaustive
+    search over the levels."""
+    rng = np.random.default_rng(40 + bits)
+    x = rng.standard_normal((64, 128)) * rng.lognormal(0, 1, (1, 128))
+    x = oracle.bf16(x)
+    alpha = 1.7
+    r = oracle.quantize_rms(x, bits, alpha)
+    n = 1 << bits
+    for g in range(x.shape[0]):
+        rms = np.sqrt(np.sum(x[g] ** 2) / 128)
+        lo, hi = -alpha * rms, alpha * rms
+        s16 = oracle.fp16((hi - lo) / (n - 1))
+        z16 = oracle.fp16(lo)
+        assert r["s16"][g] == s16 and r["z16"][g] == z16
+        levels = z16 + s16 * np.arange(n)
+        for i in range(128):
+            d = np.abs(x[g, i] - levels)
+            best = np.flatnonzero(d == d.min())
+            want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            assert r["codes"][g, i] == want
