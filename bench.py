@@ -113,6 +113,60 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, workload, path, commands, algo
     return "\n".join(lines) + "\n"
 
 
+def filter_counters(src, dst):
+    """Keep the rows of this library's kernels from a rocprofv3 counter CSV."""
+    import csv
+    with open(src) as f, open(dst, "w", newline="") as g:
+        r = csv.DictReader(f)
+        w = csv.DictWriter(g, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for row in r:
+            if "wkv::" in row["Kernel_Name"]:
+                w.writerow({k: row[k] for k in w.fieldnames})
+
+
+def summarize_counters(csvs, kernel, commands, duration_us=None):
+    """Medians over the dispatches of `kernel` of the SQ counters in the given
+    (filtered) counter CSVs, with the ratios used in the design notes."""
+    import collections
+    import csv
+    import statistics
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                per[(path, r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+    vals = collections.defaultdict(list)
+    for d in per.values():
+        for c, v in d.items():
+            vals[c].append(v)
+    m = {c: statistics.median(v) for c, v in vals.items()}
+    lines = [f"# SQ counters of {kernel}: median per dispatch over {len(per)} dispatches",
+             "# commands (run from /tmp with TMPDIR=/tmp; R = repository root):"]
+    lines += [f"#   {c}" for c in commands]
+    lines += [f"{c}: {v:.0f}" for c, v in sorted(m.items())]
+    if "SQ_WAVE_CYCLES" in m and m["SQ_WAVE_CYCLES"] > 0:
+        wc = m["SQ_WAVE_CYCLES"]
+        for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY",
+                  "SQ_WAIT_INST_ANY"):
+            if c in m:
+                lines.append(f"{c}_per_wave_cycle: {m[c] / wc:.3f}")
+    if "SQ_WAVES" in m and m["SQ_WAVES"] > 0:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                  "SQ_LDS_BANK_CONFLICT"):
+            if c in m:
+                lines.append(f"{c}_per_wave: {m[c] / m['SQ_WAVES']:.0f}")
+    if duration_us and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        # matrix-unit busy cycles summed over SIMDs against the kernel's
+        # duration (kernel trace) x 2.4 GHz x 1024 SIMDs (4 per CU, 256 CUs)
+        lines.append(f"kernel_avg_duration_us: {duration_us}")
+        lines.append("mfma_busy_fraction: "
+                     f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (duration_us * 1e-6 * 2.4e9 * 1024):.4f}")
+    lines.append(f"kernel_source_sha256_16: {kernel_source_hash()}")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_trace(stats_csv, commands, top=8):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -336,7 +390,27 @@ def main():
     ap.add_argument("--summarize-trace", metavar="STATS_CSV",
                     help="write the kernel-trace summary from rocprofv3 --stats output and exit")
     ap.add_argument("--commands", nargs="*", default=[], help="profiling commands to record")
+    ap.add_argument("--filter-counters", nargs=2, metavar=("SRC", "DST"),
+                    help="keep this library's kernels from a rocprofv3 counter CSV and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="write the SQ-counter summary of --kernel from filtered CSVs and exit")
+    ap.add_argument("--kernel", default="split_kernel")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--duration-us", type=float, default=None,
+                    help="average kernel duration (kernel trace) for the MFMA busy fraction")
     args = ap.parse_args()
+    if args.filter_counters:
+        filter_counters(*args.filter_counters)
+        return
+    if args.summarize_counters:
+        text = summarize_counters(args.summarize_counters, args.kernel, args.commands,
+                                  args.duration_us)
+        out = args.out or os.path.join(PROFILES, f"{args.kernel.split('<')[0]}_counters.txt")
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(out, "w") as fh:
+            fh.write(text)
+        print(out)
+        return
     if args.summarize_pmc or args.summarize_trace:
         from decode_attention_wushkv_amd import synth
         w = synth.WORKLOADS[args.workload]
