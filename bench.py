@@ -367,6 +367,151 @@ def prefill_rate(wid, bits, dev, reps=3):
                     "(selection and quantization), not HBM or MFMA"}
 
 
+def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
+    """Build the workload's cache through the library (prefill appends, layer
+    by layer), then time K decode steps (pass A, no instrumentation) and K more
+    with HIP events around every split launch (pass B).  page_size > 0 builds a
+    paged cache whose pool holds exactly the pages the sequences need, handed
+    out in a seeded shuffled order."""
+    import numpy as np
+    import torch
+
+    import decode_attention_wushkv_amd as wk
+    from decode_attention_wushkv_amd import synth
+    from decode_attention_wushkv_amd.device_cache import DeviceCache
+
+    targets = w.lengths()
+    B = len(targets)
+    L0 = [t - (W + 2 * K) for t in targets]
+    S, R, F = w.sink, w.recent, w.flush
+    slots = list(range(B))
+    paging = {}
+    if page_size:
+        # pages holding quantized positions at the final lengths
+        n_pages = sum((squant(t, S, R, F) - 1) // page_size + 1 - S // page_size for t in targets)
+        paging = dict(page_size=page_size, n_pages=n_pages,
+                      page_seed=page_seed if page_seed is not None else 7 + page_size)
+    dc = DeviceCache(n_layers=w.n_layers, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits, sink=S,
+                     recent=R, flush=F, p_lo=w.p_lo, p_hi=w.p_hi, max_batch=B,
+                     ctx_cap=max(targets), io_dtype=w.torch_io, device=dev, **paging)
+
+    # ---- build the cache through the library (prefill appends), layer by layer
+    t_build = time.perf_counter()
+    tks, tqs = [], []
+    for layer in range(w.n_layers):
+        T, Tq = synth.transforms(w, layer)
+        tks.append(torch.from_numpy(T).to(dev))
+        tqs.append(torch.from_numpy(Tq).to(dev))
+        scales = synth.channel_scales(w, layer)
+        parts_k, parts_v = [], []
+        for s in range(B):
+            k, v = synth.keys_values(w, layer, s, 0, L0[s], device=dev, scales=scales)
+            parts_k.append(k)
+            parts_v.append(v)
+        kk = torch.cat(parts_k) if B > 1 else parts_k[0]
+        vv = torch.cat(parts_v) if B > 1 else parts_v[0]
+        del parts_k, parts_v
+        dc.append(layer, slots, L0, kk, vv, tks[layer])
+        del kk, vv
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t_build
+    print(f"[bench] cache built: {w.name}, {bits}-bit, {dc.layout.total_bytes / 2**30:.2f} GiB arena"
+          f"{f', pages of {page_size}' if page_size else ''}, {build_s:.1f} s",
+          file=sys.stderr, flush=True)
+
+    # ---- per-step inputs, resident before timing
+    layer_scales = [synth.channel_scales(w, layer) for layer in range(w.n_layers)]
+    steps_in = []
+    for st in range(W + 2 * K):
+        per_layer = []
+        for layer in range(w.n_layers):
+            scales = layer_scales[layer]
+            ks, vs = [], []
+            for s in range(B):
+                k, v = synth.keys_values(w, layer, s, L0[s] + st, 1, device=dev, scales=scales)
+                ks.append(k)
+                vs.append(v)
+            q = synth.queries(w, layer, st, B, device=dev)
+            per_layer.append((torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), q))
+        steps_in.append(per_layer)
+    out = torch.empty((B, w.n_q, 128), dtype=torch.float32, device=dev)
+    dc.workspace(B)
+    stream = torch.cuda.current_stream(dev)
+
+    def layer_call(st, layer):
+        k1, v1, q = steps_in[st][layer]
+        if fused:
+            dc.decode_step(layer, slots, k1, v1, tks[layer], q, tqs[layer], out)
+        else:
+            dc.append(layer, slots, [1] * B, k1, v1, tks[layer])
+            dc.decode_attn(layer, slots, q, tqs[layer], out)
+
+    # HIP events bracketing every split launch of pass B, created and recorded
+    # once beforehand so that the timed loop only records them
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(K * w.n_layers)]
+    for e0, e1 in ev_pairs:
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+
+    for st in range(W):
+        for layer in range(w.n_layers):
+            layer_call(st, layer)
+
+    def timed_pass(first, instrument):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        i = 0
+        for st in range(first, first + K):
+            for layer in range(w.n_layers):
+                if instrument:
+                    e0, e1 = ev_pairs[i]
+                    i += 1
+                    wk.wushkv_set_split_events(dc.handle, e0.cuda_event, e1.cuda_event)
+                layer_call(st, layer)
+                if instrument:
+                    wk.wushkv_set_split_events(dc.handle, None, None)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    # pass A: the step metric, no instrumentation in the stream
+    total_ms = timed_pass(W, False)
+    ms_per_step = total_ms / K
+    # pass B: the same steps continued, split kernel bracketed by HIP events
+    total_b_ms = timed_pass(W + K, True)
+    split_ms = [a.elapsed_time(b) for a, b in ev_pairs]
+
+    # algorithmic bytes of the attention reads over the timed steps of pass A
+    bytes_total = 0
+    for st in range(W, W + K):
+        for s in range(B):
+            Lnow = L0[s] + st + 1
+            bytes_total += w.n_layers * w.n_kv * unit_bytes(Lnow, S, R, F, bits, fused)
+    bytes_per_step = bytes_total / K
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    # per split launch of pass B (the same sequences, K positions longer)
+    bytes_b = 0
+    for st in range(W + K, W + 2 * K):
+        for s in range(B):
+            bytes_b += w.n_layers * w.n_kv * unit_bytes(L0[s] + st + 1, S, R, F, bits, fused)
+    bytes_per_launch = bytes_b / (K * w.n_layers)
+    split_avg_ms = float(np.mean(split_ms))
+    achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
+    append_tok_s = B * w.n_layers * K / (total_ms * 1e-3)
+
+    n_launches = len(split_ms)
+    del dc, steps_in, out
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms_per_step, value=value, achieved=achieved, split_avg_ms=split_avg_ms,
+                bytes_per_launch=bytes_per_launch, total_b_ms=total_b_ms,
+                append_tok_s=append_tok_s, build_s=build_s, launches=n_launches,
+                n_pages=paging.get("n_pages"))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -377,6 +522,10 @@ def main():
     ap.add_argument("--path", choices=("step", "append+attn"), default="step",
                     help="fused wushkv_decode_step, or wushkv_append then wushkv_decode_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="time a paged cache with pages of this many positions (0: contiguous)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the secondary measurement of the same steps on a paged cache")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-append measurement")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the streaming-read ceiling and the bf16-cache comparison")
@@ -455,10 +604,7 @@ def main():
     S, R, F = w.sink, w.recent, w.flush
     slots = list(range(B))
 
-    dc = DeviceCache(n_layers=w.n_layers, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits, sink=S,
-                     recent=R, flush=F, p_lo=w.p_lo, p_hi=w.p_hi, max_batch=B,
-                     ctx_cap=max(targets), io_dtype=w.torch_io, device=dev)
-
+    fused = args.path == "step"
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -468,114 +614,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- build the cache through the library (prefill appends), layer by layer
-    t_build = time.perf_counter()
-    tks, tqs = [], []
-    for layer in range(w.n_layers):
-        T, Tq = synth.transforms(w, layer)
-        tks.append(torch.from_numpy(T).to(dev))
-        tqs.append(torch.from_numpy(Tq).to(dev))
-        scales = synth.channel_scales(w, layer)
-        parts_k, parts_v = [], []
-        for s in range(B):
-            k, v = synth.keys_values(w, layer, s, 0, L0[s], device=dev, scales=scales)
-            parts_k.append(k)
-            parts_v.append(v)
-        kk = torch.cat(parts_k) if B > 1 else parts_k[0]
-        vv = torch.cat(parts_v) if B > 1 else parts_v[0]
-        del parts_k, parts_v
-        dc.append(layer, slots, L0, kk, vv, tks[layer])
-        del kk, vv
-    torch.cuda.synchronize()
-    build_s = time.perf_counter() - t_build
-    print(f"[bench] cache built: {w.name}, {bits}-bit, {dc.layout.total_bytes / 2**30:.2f} GiB arena, "
-          f"{build_s:.1f} s", file=sys.stderr, flush=True)
-
-    # ---- per-step inputs, resident before timing
-    layer_scales = [synth.channel_scales(w, layer) for layer in range(w.n_layers)]
-    steps_in = []
-    for st in range(W + 2 * K):
-        per_layer = []
-        for layer in range(w.n_layers):
-            scales = layer_scales[layer]
-            ks, vs = [], []
-            for s in range(B):
-                k, v = synth.keys_values(w, layer, s, L0[s] + st, 1, device=dev, scales=scales)
-                ks.append(k)
-                vs.append(v)
-            q = synth.queries(w, layer, st, B, device=dev)
-            per_layer.append((torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), q))
-        steps_in.append(per_layer)
-    out = torch.empty((B, w.n_q, 128), dtype=torch.float32, device=dev)
-    dc.workspace(B)
-    stream = torch.cuda.current_stream(dev)
-
-    fused = args.path == "step"
-
-    def layer_call(st, layer):
-        k1, v1, q = steps_in[st][layer]
-        if fused:
-            dc.decode_step(layer, slots, k1, v1, tks[layer], q, tqs[layer], out)
-        else:
-            dc.append(layer, slots, [1] * B, k1, v1, tks[layer])
-            dc.decode_attn(layer, slots, q, tqs[layer], out)
-
-    # HIP events bracketing every split launch of pass B, created and recorded
-    # once beforehand so that the timed loop only records them
-    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(K * w.n_layers)]
-    for e0, e1 in ev_pairs:
-        e0.record(stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-
-    for st in range(W):
-        for layer in range(w.n_layers):
-            layer_call(st, layer)
-
-    def timed_pass(first, instrument):
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        i = 0
-        for st in range(first, first + K):
-            for layer in range(w.n_layers):
-                if instrument:
-                    e0, e1 = ev_pairs[i]
-                    i += 1
-                    wk.wushkv_set_split_events(dc.handle, e0.cuda_event, e1.cuda_event)
-                layer_call(st, layer)
-                if instrument:
-                    wk.wushkv_set_split_events(dc.handle, None, None)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
-
-    # pass A: the step metric, no instrumentation in the stream
-    total_ms = timed_pass(W, False)
-    ms_per_step = total_ms / K
-    # pass B: the same steps continued, split kernel bracketed by HIP events
-    total_b_ms = timed_pass(W + K, True)
-    split_ms = [a.elapsed_time(b) for a, b in ev_pairs]
-
-    # algorithmic bytes of the attention reads over the timed steps of pass A
-    bytes_total = 0
-    for st in range(W, W + K):
-        for s in range(B):
-            Lnow = L0[s] + st + 1
-            bytes_total += w.n_layers * w.n_kv * unit_bytes(Lnow, S, R, F, bits, fused)
-    bytes_per_step = bytes_total / K
-    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    # per split launch of pass B (the same sequences, K positions longer)
-    bytes_b = 0
-    for st in range(W + K, W + 2 * K):
-        for s in range(B):
-            bytes_b += w.n_layers * w.n_kv * unit_bytes(L0[s] + st + 1, S, R, F, bits, fused)
-    bytes_per_launch = bytes_b / (K * w.n_layers)
-    split_avg_ms = float(np.mean(split_ms))
-    achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
-    append_tok_s = B * w.n_layers * K / (total_ms * 1e-3)
+    m = measure_decode(w, bits, K, W, dev, fused, page_size=args.page_size)
+    ms_per_step, value, achieved = m["ms_per_step"], m["value"], m["achieved"]
+    split_avg_ms, bytes_per_launch = m["split_avg_ms"], m["bytes_per_launch"]
+    total_b_ms, append_tok_s, build_s = m["total_b_ms"], m["append_tok_s"], m["build_s"]
+    n_launches = m["launches"]
 
     traffic = stored_traffic(w.name, args.path)
     if traffic is not None:
@@ -607,14 +650,22 @@ def main():
                      "kernel": "split_kernel (split-K scan over codes + windows"
                                + (", fused one-token append)" if fused else ")"),
                      "bytes_per_launch": int(bytes_per_launch),
-                     "avg_launch_ms": round(split_avg_ms, 5), "launches": len(split_ms),
+                     "avg_launch_ms": round(split_avg_ms, 5), "launches": n_launches,
                      "timing": "HIP events around every split launch of a second timed pass of "
                                f"{K} steps ({round(total_b_ms / K, 4)} ms/step with the events)"},
         "cache_build_s": round(build_s, 2),
     }
-    if not args.no_prefill or not args.no_reference:
-        del dc, steps_in, out
-        torch.cuda.empty_cache()
+    if not args.no_paged and args.page_size == 0:
+        pg = measure_decode(w, bits, K, W, dev, fused, page_size=128)
+        res["paged"] = {
+            "page_size": 128, "n_pages": pg["n_pages"],
+            "note": "the same steps on a paged cache: quantized planes in 128-position pages "
+                    "handed out in shuffled order, block table read by the kernels",
+            "ms_per_step": round(pg["ms_per_step"], 4), "value": round(pg["value"], 2),
+            "split_achieved": round(pg["achieved"], 2),
+            "split_frac": round(pg["achieved"] / HBM_PEAK_GBS, 4),
+            "avg_launch_ms": round(pg["split_avg_ms"], 5),
+            "step_time_vs_contiguous": round(pg["ms_per_step"] / ms_per_step, 4)}
     if not args.no_reference:
         ceil = read_ceiling(bytes_per_launch, dev)
         res["roofline"]["read_ceiling_gbs"] = ceil

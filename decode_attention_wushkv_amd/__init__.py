@@ -26,7 +26,8 @@ EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_append", "wushkv_decode_workspace_bytes",
     "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events",
-    "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_status_str",
+    "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_set_block_table",
+    "wushkv_status_str",
 )
 
 
@@ -38,6 +39,7 @@ class wushkv_config(ctypes.Structure):
         ("flush", ctypes.c_int32), ("p_lo", ctypes.c_double), ("p_hi", ctypes.c_double),
         ("max_batch", ctypes.c_int32), ("ctx_cap", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
         ("codec", ctypes.c_int32), ("clip_alpha", ctypes.c_double),
+        ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
     ]
 
 
@@ -49,7 +51,8 @@ class wushkv_layout_t(ctypes.Structure):
         (f"off_{n}", _U64) for n in ("kcode", "vcode", "ksz", "vsz", "ksink", "vsink", "kring", "vring")
     ] + [
         (f"bytes_{n}", _U64) for n in ("kcode", "vcode", "ksz", "vsz", "ksink", "vsink", "kring", "vring")
-    ] + [(n, ctypes.c_int32) for n in ("code_bytes", "vblock", "ctx_blocks", "cpos", "ring_slots", "units")]
+    ] + [(n, ctypes.c_int32) for n in ("code_bytes", "vblock", "ctx_blocks", "cpos", "ring_slots", "units",
+                                       "page_size", "n_pages", "pages_per_seq")]
 
 
 class WushkvError(RuntimeError):
@@ -93,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_decode_attn.argtypes = [P, i32, i32, i32p, P, P, P, P, _U64, P]
     L.wushkv_decode_step.restype = ctypes.c_int
     L.wushkv_decode_step.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P, _U64, P]
+    L.wushkv_set_block_table.restype = ctypes.c_int
+    L.wushkv_set_block_table.argtypes = [P, P]
     L.wushkv_set_split_events.restype = ctypes.c_int
     L.wushkv_set_split_events.argtypes = [P, P, P]
     L.wushkv_gaussian_alpha.restype = ctypes.c_double
@@ -117,9 +122,10 @@ def _i32_array(xs):
 
 def make_config(*, n_layers, n_q_heads, n_kv_heads, bits, sink, recent, flush=1, p_lo=0.01,
                 p_hi=0.99, max_batch, ctx_cap, io_dtype, head_dim=128, codec=WUSHKV_CODEC_PERCENTILE,
-                clip_alpha=0.0) -> wushkv_config:
+                clip_alpha=0.0, page_size=0, n_pages=0) -> wushkv_config:
     return wushkv_config(n_layers, n_q_heads, n_kv_heads, head_dim, bits, sink, recent, flush,
-                         p_lo, p_hi, max_batch, ctx_cap, io_dtype, codec, clip_alpha)
+                         p_lo, p_hi, max_batch, ctx_cap, io_dtype, codec, clip_alpha, page_size,
+                         n_pages)
 
 
 # ------------------------------------------------------------- C-ABI mirrors
@@ -211,6 +217,11 @@ def wushkv_stream_read_probe(buf_ptr: int, nbytes: int, blocks: int, out_ptr: in
     _check(lib().wushkv_stream_read_probe(ctypes.c_void_p(buf_ptr), int(nbytes), int(blocks),
                                           ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)),
            "wushkv_stream_read_probe")
+
+
+def wushkv_set_block_table(cache: int, table_ptr: int) -> None:
+    _check(lib().wushkv_set_block_table(ctypes.c_void_p(cache), ctypes.c_void_p(table_ptr)),
+           "wushkv_set_block_table")
 
 
 def wushkv_set_split_events(cache: int, ev_start: int | None, ev_stop: int | None) -> None:

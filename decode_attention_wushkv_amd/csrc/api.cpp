@@ -15,6 +15,7 @@ struct wushkv_cache {
   wushkv_config cfg;
   wushkv_layout_t lay;
   uint8_t* arena;
+  const int32_t* table = nullptr;  // paged caches: device block table [max_batch][pages_per_seq]
   std::vector<int32_t> len;  // [n_layers][max_batch]
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
 };
@@ -88,6 +89,14 @@ extern "C" wushkv_status wushkv_config_check(const wushkv_config* c) {
   }
   // The window split scores all sink + ring entries in one workgroup.
   if ((int64_t)c->sink + c->recent + c->flush - 1 > WINDOW_MAX) return WUSHKV_EUNSUPPORTED;
+  // Paged quantized planes: pages of a power-of-two number of positions, at
+  // least one decode sub-chunk (128) and at most 2^20.
+  if (c->page_size == 0) {
+    if (c->n_pages != 0) return WUSHKV_EINVAL;
+  } else {
+    const int P = c->page_size;
+    if (P < 128 || P > (1 << 20) || (P & (P - 1)) != 0 || c->n_pages < 1) return WUSHKV_EINVAL;
+  }
   return WUSHKV_OK;
 }
 
@@ -105,9 +114,18 @@ extern "C" wushkv_status wushkv_layout(const wushkv_config* c, wushkv_layout_t* 
   L.ring_slots = c->recent + c->flush - 1;
   L.units = c->n_layers * c->max_batch * c->n_kv_heads;
   const uint64_t u = (uint64_t)L.units;
-  L.bytes_kcode = u * (uint64_t)L.cpos * L.code_bytes;
-  L.bytes_vcode = u * (uint64_t)L.ctx_blocks * D * 16;
-  L.bytes_ksz = u * (uint64_t)L.cpos * 4;
+  // rows of the quantized planes (one per position and KV head)
+  uint64_t rows = u * (uint64_t)L.cpos;
+  if (c->page_size > 0) {
+    L.page_size = c->page_size;
+    L.n_pages = c->n_pages;
+    L.pages_per_seq = (c->ctx_cap + c->page_size - 1) / c->page_size;
+    rows = (uint64_t)c->n_layers * (uint64_t)c->n_pages * (uint64_t)c->n_kv_heads *
+           (uint64_t)c->page_size;
+  }
+  L.bytes_kcode = rows * L.code_bytes;
+  L.bytes_vcode = rows / L.vblock * D * 16;
+  L.bytes_ksz = rows * 4;
   L.bytes_vsz = L.bytes_ksz;
   L.bytes_ksink = u * (uint64_t)c->sink * D * 2;
   L.bytes_vsink = L.bytes_ksink;
@@ -200,6 +218,17 @@ static Geometry geometry_of(const wushkv_cache* c) {
   g.p_hi = c->cfg.p_hi;
   g.codec = c->cfg.codec;
   g.alpha = c->cfg.clip_alpha > 0.0 ? c->cfg.clip_alpha : wushkv_gaussian_alpha(c->cfg.bits);
+  if (c->cfg.page_size > 0) {
+    g.table = c->table;
+    g.pps = c->lay.pages_per_seq;
+    g.page_shift = __builtin_ctz((unsigned)c->cfg.page_size);
+    g.n_pages = c->cfg.n_pages;
+  } else {
+    g.table = nullptr;
+    g.pps = 0;
+    g.page_shift = 0;
+    g.n_pages = c->cfg.max_batch;
+  }
   return g;
 }
 
@@ -222,6 +251,7 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
   if (n_seq > MAXSEQ) return WUSHKV_EUNSUPPORTED;
   if (n_seq == 0) return WUSHKV_OK;
   if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
+  if (c->cfg.page_size > 0 && !c->table) return WUSHKV_EINVAL;
   int64_t total = 0;
   int max_new = 0;
   for (int i = 0; i < n_seq; ++i) {
@@ -319,6 +349,7 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   if (step && (((uintptr_t)k % esz) || ((uintptr_t)v % esz) || ((uintptr_t)tk % 16)))
     return WUSHKV_EINVAL;
   if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
+  if (c->cfg.page_size > 0 && !c->table) return WUSHKV_EINVAL;
   if (ws_bytes < wushkv_decode_workspace_bytes(c, n_seq)) return WUSHKV_EWORKSPACE;
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
@@ -381,6 +412,12 @@ extern "C" wushkv_status wushkv_decode_step(wushkv_cache* c, int32_t layer, int3
                                             float* out, void* ws, uint64_t ws_bytes,
                                             void* stream) {
   return decode_common(c, layer, n_seq, slots, k, v, tk, q, tq, out, ws, ws_bytes, stream, true);
+}
+
+extern "C" wushkv_status wushkv_set_block_table(wushkv_cache* c, const int32_t* table) {
+  if (!c || c->cfg.page_size == 0 || !table || ((uintptr_t)table % 4)) return WUSHKV_EINVAL;
+  c->table = table;
+  return WUSHKV_OK;
 }
 
 extern "C" wushkv_status wushkv_set_split_events(wushkv_cache* c, void* ev_start, void* ev_stop) {

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   const int n = a.s.n_new[si];
   const int L1 = L0 + n;
   const int64_t unit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
+  const QMap qm = qmap_of(g, a.layer, slot, h);
   const int sq0 = squant_of(L0, g.S, g.R, g.F);
   const int sq1 = squant_of(L1, g.S, g.R, g.F);
 
@@ -51,10 +52,10 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       const int64_t row = (unit * g.W + (p - g.S) % g.W) * D + i;
       float kx = bf16_bits_to_f32(a.pl.kring[row]);
       float vx = bf16_bits_to_f32(a.pl.vring[row]);
-      store_quantized(p, kx, vx, L, vr, a.pl, unit, g);
+      store_quantized(p, kx, vx, L, vr, a.pl, qm, g);
     }
     if (a.mode == APPEND_EVICT) {
-      vrow_flush(vr, a.pl, unit, g);
+      vrow_flush(vr, a.pl, qm, g);
       return;
     }
   }
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
     if (c1 > L1) c1 = L1;
   }
   if (c0 >= c1) {
-    vrow_flush(vr, a.pl, unit, g);
+    vrow_flush(vr, a.pl, qm, g);
     return;
   }
 
@@ -103,11 +104,11 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       a.pl.kring[o] = kb;
       a.pl.vring[o] = vb;
     } else {
-      store_quantized(p, bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), L, vr, a.pl, unit, g);
+      store_quantized(p, bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), L, vr, a.pl, qm, g);
     }
     __syncthreads();  // kvec reuse
   }
-  vrow_flush(vr, a.pl, unit, g);
+  vrow_flush(vr, a.pl, qm, g);
 }
 
 }  // namespace

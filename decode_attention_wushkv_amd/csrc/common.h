@@ -53,7 +53,56 @@ struct Geometry {
   double p_lo, p_hi;
   int codec;     // WUSHKV_CODEC_PERCENTILE or WUSHKV_CODEC_RMS
   double alpha;  // RMS codec endpoint (resolved)
+  // Quantized planes.  Contiguous: a unit's positions are rows unit * cpos +
+  // p.  Paged: rows ((layer * n_pages + page) * n_kv + head) << page_shift +
+  // (p & (page - 1)) with page = table[slot * pps + (p >> page_shift)].
+  const int32_t* table;  // block table [max_batch][pps] (device); null when contiguous
+  int pps, page_shift, n_pages;
 };
+
+// Where the quantized planes keep one (layer, sequence, KV head): position p
+// is row r of kcode (bytes r * code_bytes), ksz and vsz, and its value codes
+// lie in block r / vblock of vcode.  A page (at least 128 positions, a power
+// of two) holds whole decode sub-chunks and value-code blocks.
+struct QMap {
+  const int32_t* pages;  // the sequence's block-table row; null when contiguous
+  int64_t base;          // row of position 0 (contiguous) or of physical page 0 (paged)
+  int64_t stride;        // rows from one physical page to the next (paged)
+  int shift, n_pages;
+};
+
+__host__ __device__ inline QMap qmap_of(const Geometry& g, int layer, int slot, int head) {
+  QMap m;
+  m.shift = g.page_shift;
+  m.n_pages = g.n_pages;
+  if (g.table) {
+    m.pages = g.table + (int64_t)slot * g.pps;
+    m.stride = (int64_t)g.n_kv << g.page_shift;
+    m.base = ((int64_t)layer * g.n_pages * g.n_kv + head) << g.page_shift;
+  } else {
+    m.pages = nullptr;
+    m.stride = 0;
+    m.base = (((int64_t)layer * g.max_batch + slot) * g.n_kv + head) * g.cpos;
+  }
+  return m;
+}
+
+// Row of position p; -1 when the block table maps no page of the pool there
+// (writers then skip the position).
+__device__ __forceinline__ int64_t qrow(const QMap& m, int p) {
+  if (!m.pages) return m.base + p;
+  const int pg = m.pages[p >> m.shift];
+  if ((unsigned)pg >= (unsigned)m.n_pages) return -1;
+  return m.base + pg * m.stride + (p & ((1 << m.shift) - 1));
+}
+
+// Row of position p for reads: an unmapped page reads the pool's first page
+// (results for that sequence are then unspecified, but no access leaves the
+// arena).
+__device__ __forceinline__ int64_t qrow_read(const QMap& m, int p) {
+  const int64_t r = qrow(m, p);
+  return r >= 0 ? r : (int64_t)(p & ((1 << m.shift) - 1));
+}
 
 // squant(L): end of the quantized region [S, squant) at length L (section 4.4).
 __host__ __device__ inline int squant_of(int L, int S, int R, int F) {

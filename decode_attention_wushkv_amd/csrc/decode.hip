@@ -289,8 +289,9 @@ __device__ void compensate_query(const DecodeArgs& a, int h, int si, uint32_t* s
 
 // Registers holding one sub-chunk's codes: key codes (lane pair per
 // position), scale/zero words, value rows of dimensions lane and lane + 64.
-// Loads are unconditional: a sub-chunk never leaves its unit (cpos is a
-// multiple of 128); positions outside [lo, hi) are masked arithmetically.
+// Loads are unconditional: a sub-chunk never leaves its unit (cpos and the
+// page size are multiples of 128); positions outside [lo, hi) are masked
+// arithmetically.
 template <int BITS, int G>
 struct SubBuf {
   using C = SplitCfg<BITS, G>;
@@ -300,14 +301,14 @@ struct SubBuf {
 };
 
 template <int BITS, int G>
-__device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a, int64_t unit,
+__device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a, const QMap& qm,
                                          int pbase) {
   using C = SplitCfg<BITS, G>;
-  const Geometry& g = a.g;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
-  const uint8_t* kb = a.pl.kcode + (unit * g.cpos + pbase + tq) * C::CB + half * (C::CB / 2);
-  const uint32_t* kz = a.pl.ksz + unit * g.cpos + pbase + tq;
-  const uint32_t* vz = a.pl.vsz + unit * g.cpos + pbase + tq;
+  const int64_t row = qrow_read(qm, pbase);
+  const uint8_t* kb = a.pl.kcode + (row + tq) * C::CB + half * (C::CB / 2);
+  const uint32_t* kz = a.pl.ksz + row + tq;
+  const uint32_t* vz = a.pl.vsz + row + tq;
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
 #pragma unroll
@@ -315,7 +316,7 @@ __device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a
     b.ksz[r] = kz[32 * r];
     b.vsz[r] = vz[32 * r];
   }
-  const uint8_t* vb = a.pl.vcode + ((unit * g.ctx_blocks + pbase / C::VB) * D + lane) * 16;
+  const uint8_t* vb = a.pl.vcode + ((row / C::VB) * D + lane) * 16;
 #pragma unroll
   for (int k = 0; k < C::NBW; ++k) {
     b.vc[k][0] = *(const uint4*)(vb + (int64_t)k * D * 16);
@@ -508,7 +509,7 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
 // of codes in flight; leaves the partial (o[D], m, l) of head gg at
 // out + gg * hstride.  A already holds sub-chunk c0.
 template <int BITS, int G>
-__device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride, int c_end, int lo,
+__device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stride, int c_end, int lo,
                            int hi, const float* qsc, const uint32_t* qdw, uint32_t* wsm, float* out,
                            int64_t hstride, SubBuf<BITS, G>& A) {
   using C = SplitCfg<BITS, G>;
@@ -538,12 +539,12 @@ __device__ void quant_wave(const DecodeArgs& a, int64_t unit, int c0, int stride
   int c = c0;  // A holds sub-chunk c0 (loaded by the caller) when c0 < c_end
   while (c < c_end) {
     int cn = c + stride;
-    if (cn < c_end) load_sub<BITS, G>(B, a, unit, cn * C::TW);
+    if (cn < c_end) load_sub<BITS, G>(B, a, qm, cn * C::TW);
     process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
     if (c >= c_end) break;
     cn = c + stride;
-    if (cn < c_end) load_sub<BITS, G>(A, a, unit, cn * C::TW);
+    if (cn < c_end) load_sub<BITS, G>(A, a, qm, cn * C::TW);
     process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
   }
@@ -599,7 +600,8 @@ __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
 // for it, as codes.  Threads 0..127 handle key dimensions, 128..255 value
 // dimensions.
 template <int BITS, int G>
-__device__ void step_append(const DecodeArgs& a, int64_t unit, int Lq, int sq, uint32_t* sm) {
+__device__ void step_append(const DecodeArgs& a, int64_t unit, const QMap& qm, int Lq, int sq,
+                            uint32_t* sm) {
   using C = SplitCfg<BITS, G>;
   const Geometry& g = a.g;
   const int tid = threadIdx.x, i = tid & (D - 1);
@@ -616,7 +618,7 @@ __device__ void step_append(const DecodeArgs& a, int64_t unit, int Lq, int sq, u
   for (int p = sq; p < e1; ++p) {
     const int64_t row = (unit * g.W + (p - g.S) % g.W) * D + i;
     const float x = bf16_bits_to_f32(is_v ? a.pl.vring[row] : a.pl.kring[row]);
-    store_quantized(p, x, x, ql, vr, a.pl, unit, g);
+    store_quantized(p, x, x, ql, vr, a.pl, qm, g);
   }
   __syncthreads();  // ring reads above complete before the ring write below
   const uint16_t nb = is_v ? vnew[i] : knew[i];
@@ -628,9 +630,9 @@ __device__ void step_append(const DecodeArgs& a, int64_t unit, int Lq, int sq, u
     (is_v ? a.pl.vring : a.pl.kring)[o] = nb;
   } else {
     const float x = bf16_bits_to_f32(nb);
-    store_quantized(L0, x, x, ql, vr, a.pl, unit, g);
+    store_quantized(L0, x, x, ql, vr, a.pl, qm, g);
   }
-  vrow_flush(vr, a.pl, unit, g);
+  vrow_flush(vr, a.pl, qm, g);
 }
 
 // ---------------------------------------------------------------- window
@@ -824,6 +826,7 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
   const int h = u % g.n_kv, si = u / g.n_kv;
   const int slot = a.s.slot[si], Lq = a.s.len[si], sq = a.s.squant[si];
   const int64_t unit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
+  const QMap qm = qmap_of(g, a.layer, slot, h);
   const int qbase = si * g.n_q + h * G;
 
   // the quantized region [S, sq) in sub-chunks of TW positions, spread over
@@ -868,10 +871,10 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
         cstride = a.n_splits;
       }
       SubBuf<BITS, C::GW> A;
-      if (c0 < cend) load_sub<BITS, C::GW>(A, a, unit, c0 * C::TW);
+      if (c0 < cend) load_sub<BITS, C::GW>(A, a, qm, c0 * C::TW);
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       float* dst = a.wsp + ((int64_t)(qbase + w * C::GW) * nsp + j) * PS;
-      quant_wave<BITS, C::GW>(a, unit, c0, cstride, cend, lo, hi,
+      quant_wave<BITS, C::GW>(a, qm, c0, cstride, cend, lo, hi,
                               (const float*)(sm + C::O_QSC) + w * C::GW * 4,
                               sm + C::O_QD + w * C::GW * 16 * DIGP, sm + C::O_UNION + w * C::WAVE,
                               dst, (int64_t)nsp * PS, A);
@@ -890,11 +893,11 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
       }
       // first sub-chunk's codes in flight while the query is compensated
       SubBuf<BITS, G> A;
-      if (c0 < cend) load_sub<BITS, G>(A, a, unit, c0 * C::TW);
+      if (c0 < cend) load_sub<BITS, G>(A, a, qm, c0 * C::TW);
       compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
       uint32_t* wbase = sm + C::O_UNION;
       float* part = (float*)(wbase + 4 * C::WAVE);  // [4 waves][G][D + 2]
-      quant_wave<BITS, G>(a, unit, c0, cstride, cend, lo, hi, (const float*)(sm + C::O_QSC),
+      quant_wave<BITS, G>(a, qm, c0, cstride, cend, lo, hi, (const float*)(sm + C::O_QSC),
                           sm + C::O_QD, wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A);
       __syncthreads();
       // merge the four wave partials (a wave without sub-chunks has l = 0)
@@ -933,7 +936,7 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
       }
     }
   }
-  if (a.k_new && j == a.n_splits) step_append<BITS, G>(a, unit, Lq, sq, sm);
+  if (a.k_new && j == a.n_splits) step_append<BITS, G>(a, unit, qm, Lq, sq, sm);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the

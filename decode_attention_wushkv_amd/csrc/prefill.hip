@@ -111,6 +111,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
   const int c1 = min(L1, base + ((int)blockIdx.x + 1) * PCH);
   if (c0 >= c1) return;
   const int64_t unit = ((int64_t)a.layer * g.max_batch + a.s.slot[si]) * g.n_kv + h;
+  const QMap qm = qmap_of(g, a.layer, a.s.slot[si], h);
   const int sq1 = squant_of(L1, g.S, g.R, g.F);
   const int qlo = max(L0, g.S), qhi = min(L1, sq1);  // new positions that are quantized
   constexpr int LEV = (1 << BITS) - 1;
@@ -171,6 +172,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
   load_tile(p0);
 
   for (; p0 < c1; p0 += PT) {
+    // quantized-plane row of the tile's first position (a tile never crosses
+    // a page); -1 when its page is unmapped, and then no code is stored
+    const int64_t trow = p0 + PT > qlo && p0 < qhi ? qrow(qm, p0) : -1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = tid + 256 * u;
@@ -368,14 +372,14 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
           }
         }
       }
-      if (quant) {
+      if (quant && trow >= 0) {
         if (!isv) {
-          uint4* kd = (uint4*)(a.pl.kcode + (unit * g.cpos + p) * (16 * BITS) + hh * 8 * BITS);
+          uint4* kd = (uint4*)(a.pl.kcode + (trow + t) * (16 * BITS) + hh * 8 * BITS);
 #pragma unroll
           for (int q = 0; q < BITS / 2; ++q)
             kd[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
         }
-        if (hh == 0) (isv ? a.pl.vsz : a.pl.ksz)[unit * g.cpos + p] = (uint32_t)s16 | ((uint32_t)z16 << 16);
+        if (hh == 0) (isv ? a.pl.vsz : a.pl.ksz)[trow + t] = (uint32_t)s16 | ((uint32_t)z16 << 16);
       }
     }
     __syncthreads();
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
         const int blk = x / D, dim = x % D;
         const int b0 = p0 + blk * VB;
         const int lo = max(b0, max(c0, qlo)), hi = min(b0 + VB, min(c1, qhi));
-        if (lo >= hi) continue;
+        if (lo >= hi || trow < 0) continue;
         uint32_t m[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
           m[q] = h2 <= l2 ? 0u : ((h2 - l2 >= 32 ? 0xFFFFFFFFu : ((1u << (h2 - l2)) - 1u)) << l2);
         }
         const uint32_t* src = &L.vrow[(blk * D + dim) * 4];
-        uint4* dst = (uint4*)(a.pl.vcode + ((unit * g.ctx_blocks + b0 / VB) * D + dim) * 16);
+        uint4* dst = (uint4*)(a.pl.vcode + ((trow / VB + blk) * D + dim) * 16);
         uint4 row = make_uint4(src[0], src[1], src[2], src[3]);
         if ((m[0] & m[1] & m[2] & m[3]) != 0xFFFFFFFFu) {
           const uint4 old = *dst;

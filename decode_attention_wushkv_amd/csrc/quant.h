@@ -224,9 +224,15 @@ struct VRow {
   uint32_t m0, m1, m2, m3;  // which bits are set
 };
 
-__device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl, int64_t unit, const Geometry& g) {
+__device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl, const QMap& qm, const Geometry& g) {
   if (r.blk < 0) return;
-  uint4* p = (uint4*)(pl.vcode + ((unit * g.ctx_blocks + r.blk) * D + (threadIdx.x & (D - 1))) * 16);
+  const int64_t row = qrow(qm, r.blk * g.vblock);
+  if (row < 0) {  // unmapped page: nothing is written
+    r.blk = -1;
+    return;
+  }
+  const int64_t vblk = row >> (g.bits == 2 ? 6 : 5);  // row / vblock
+  uint4* p = (uint4*)(pl.vcode + (vblk * D + (threadIdx.x & (D - 1))) * 16);
   uint4 old = *p;
   old.x = (old.x & ~r.m0) | r.b0;
   old.y = (old.y & ~r.m1) | r.b1;
@@ -236,11 +242,11 @@ __device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl, int64_t un
   r.blk = -1;
 }
 
-__device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes& pl, int64_t unit,
+__device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes& pl, const QMap& qm,
                                          const Geometry& g) {
   const int blk = p / g.vblock;
   if (blk != r.blk) {
-    vrow_flush(r, pl, unit, g);
+    vrow_flush(r, pl, qm, g);
     r.blk = blk;
     r.b0 = r.b1 = r.b2 = r.b3 = r.m0 = r.m1 = r.m2 = r.m3 = 0u;
   }
@@ -264,7 +270,7 @@ __device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes&
 // threads 0..127 hold the key entry (kx), threads 128..255 the value entry
 // (vx) and both groups run at once.
 __device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, const Planes& pl,
-                                int64_t unit, const Geometry& g) {
+                                const QMap& qm, const Geometry& g) {
   const int i = threadIdx.x & (D - 1);
   const bool two = blockDim.x == 2 * D;
   const bool is_v = two && threadIdx.x >= D;
@@ -282,15 +288,16 @@ __device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds&
   if (!is_v) L.codes[0][i] = kc;
   __syncthreads();
   const int words = g.code_bytes / 4;  // 8 (2-bit) or 16 (4-bit)
-  if (threadIdx.x < words) {
+  const int64_t row = qrow(qm, p);     // -1: unmapped page, nothing is stored
+  if (threadIdx.x < words && row >= 0) {
     const int per = 32 / g.bits;
     uint32_t w = 0;
     for (int e = 0; e < per; ++e) w |= (uint32_t)L.codes[0][threadIdx.x * per + e] << (e * g.bits);
-    ((uint32_t*)(pl.kcode + (unit * g.cpos + p) * g.code_bytes))[threadIdx.x] = w;
+    ((uint32_t*)(pl.kcode + row * g.code_bytes))[threadIdx.x] = w;
   }
-  if (threadIdx.x == 0) pl.ksz[unit * g.cpos + p] = ksz;
-  if (threadIdx.x == (two ? D : 0)) pl.vsz[unit * g.cpos + p] = vsz;
-  if (!two || is_v) vrow_add(vr, p, vc, pl, unit, g);
+  if (threadIdx.x == 0 && row >= 0) pl.ksz[row] = ksz;
+  if (threadIdx.x == (two ? D : 0) && row >= 0) pl.vsz[row] = vsz;
+  if (!two || is_v) vrow_add(vr, p, vc, pl, qm, g);
   __syncthreads();  // codes[] reuse
 }
 

@@ -1,19 +1,28 @@
 """PyTorch plumbing around the C ABI: allocate the cache arena, the decode
 workspace and the output on a HIP device and pass raw addresses and the
-current stream to libwushkv.  No arithmetic of the method happens here."""
+current stream to libwushkv.  For paged caches it also keeps the block table
+(a host-side free list of physical pages, mirrored to the device table the
+kernels read).  No arithmetic of the method happens here."""
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import (WUSHKV_IO_BF16, WUSHKV_IO_FP32, make_config, wushkv_append, wushkv_cache_create,
                wushkv_cache_destroy, wushkv_decode_attn, wushkv_decode_step,
-               wushkv_decode_workspace_bytes, wushkv_get_len, wushkv_layout, wushkv_reset_seq)
+               wushkv_decode_workspace_bytes, wushkv_get_len, wushkv_layout, wushkv_reset_seq,
+               wushkv_set_block_table)
 
 
 class DeviceCache:
+    """page_size > 0 makes the quantized planes paged: a pool of n_pages pages
+    per layer, handed out from a free list in the order given by page_seed (a
+    seeded shuffle; None keeps ascending order) as sequences grow."""
+
     def __init__(self, *, n_layers, n_q_heads, n_kv_heads, bits, sink, recent, flush=1,
                  p_lo=0.01, p_hi=0.99, max_batch, ctx_cap, io_dtype: torch.dtype,
-                 device="cuda", codec=0, clip_alpha=0.0):
+                 device="cuda", codec=0, clip_alpha=0.0, page_size=0, n_pages=0,
+                 page_seed=None):
         io = WUSHKV_IO_BF16 if io_dtype == torch.bfloat16 else WUSHKV_IO_FP32
         if io_dtype not in (torch.bfloat16, torch.float32):
             raise ValueError("io dtype must be bfloat16 or float32")
@@ -21,7 +30,7 @@ class DeviceCache:
         self.cfg = make_config(n_layers=n_layers, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                                bits=bits, sink=sink, recent=recent, flush=flush, p_lo=p_lo,
                                p_hi=p_hi, max_batch=max_batch, ctx_cap=ctx_cap, io_dtype=io, codec=codec,
-                               clip_alpha=clip_alpha)
+                               clip_alpha=clip_alpha, page_size=page_size, n_pages=n_pages)
         self.layout = wushkv_layout(self.cfg)
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:
@@ -30,6 +39,43 @@ class DeviceCache:
         self.arena = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=self.device)
         self.handle = wushkv_cache_create(self.cfg, self.arena.data_ptr(), self.layout.total_bytes)
         self._ws = None
+        self.table = None
+        if page_size:
+            pps = self.layout.pages_per_seq
+            self.table_host = np.full((max_batch, pps), -1, dtype=np.int32)
+            self.table = torch.full((max_batch, pps), -1, dtype=torch.int32, device=self.device)
+            order = np.arange(n_pages, dtype=np.int64)
+            if page_seed is not None:
+                order = np.random.default_rng(page_seed).permutation(n_pages)
+            self._free = [int(x) for x in order[::-1]]   # pop() takes the front of `order`
+            self._mapped = [0] * max_batch                 # logical pages [0, n) examined per slot
+            wushkv_set_block_table(self.handle, self.table.data_ptr())
+
+    def squant(self, L: int) -> int:
+        c = self.cfg
+        return c.sink + c.flush * (max(0, L - c.recent - c.sink) // c.flush)
+
+    def reserve(self, slot: int, length: int):
+        """Map every page that holds a quantized position of slot at `length`
+        (positions [sink, squant(length))); no-op for contiguous caches."""
+        if self.table is None:
+            return
+        sq, P = self.squant(length), self.layout.page_size
+        need = (sq - 1) // P + 1 if sq > self.cfg.sink else 0
+        if need <= self._mapped[slot]:
+            return
+        row = self.table_host[slot]
+        for i in range(max(self._mapped[slot], self.cfg.sink // P), need):
+            if row[i] < 0:
+                if not self._free:
+                    raise RuntimeError("page pool exhausted")
+                row[i] = self._free.pop()
+        self._mapped[slot] = need
+        # stream-ordered: the kernels enqueued after this copy see the new entries
+        self.table[slot].copy_(torch.from_numpy(row.copy()))
+
+    def pages_in_use(self) -> int:
+        return 0 if self.table is None else int((self.table_host >= 0).sum())
 
     def close(self):
         if self.handle:
@@ -51,7 +97,14 @@ class DeviceCache:
         return self.arena[off:off + n]
 
     def reset_seq(self, slot: int):
+        """Forget slot; a paged cache returns its pages to the free list."""
         wushkv_reset_seq(self.handle, slot)
+        if self.table is not None:
+            row = self.table_host[slot]
+            self._free.extend(int(x) for x in row[row >= 0][::-1])
+            row[:] = -1
+            self._mapped[slot] = 0
+            self.table[slot].copy_(torch.from_numpy(row.copy()))
 
     def get_len(self, layer: int, slot: int):
         return wushkv_get_len(self.handle, layer, slot)
@@ -60,6 +113,9 @@ class DeviceCache:
         for t in (k, v):
             assert t.dtype == self.io_dtype and t.is_contiguous() and t.device == self.device
         assert tk.dtype == torch.float32 and tk.is_contiguous() and tk.device == self.device
+        if self.table is not None:
+            for s, n in zip(slots, n_new):
+                self.reserve(s, self.get_len(layer, s)[0] + n)
         wushkv_append(self.handle, layer, slots, n_new, k.data_ptr(), v.data_ptr(), tk.data_ptr(),
                       self._stream())
 
@@ -95,6 +151,9 @@ class DeviceCache:
             out = torch.empty((n_seq, self.cfg.n_q_heads, 128), dtype=torch.float32,
                               device=self.device)
         ws = self.workspace(n_seq)
+        if self.table is not None:
+            for s in slots:
+                self.reserve(s, self.get_len(layer, s)[0] + 1)
         wushkv_decode_step(self.handle, layer, slots, k.data_ptr(), v.data_ptr(), tk.data_ptr(),
                            q.data_ptr(), tq.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
                            self._stream())

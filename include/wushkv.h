@@ -84,6 +84,10 @@ typedef struct {
   int32_t io_dtype;     /* WUSHKV_IO_FP32 or WUSHKV_IO_BF16 for k, v, q inputs   */
   int32_t codec;        /* WUSHKV_CODEC_PERCENTILE (0) or WUSHKV_CODEC_RMS       */
   double clip_alpha;    /* RMS codec endpoint; 0 = wushkv_gaussian_alpha(bits)   */
+  int32_t page_size;    /* 0: contiguous quantized planes per slot; else paged:  */
+                        /* positions per page, a power of two in [128, 2^20]    */
+  int32_t n_pages;      /* paged: physical pages per layer in the pool (>= 1);  */
+                        /* contiguous: must be 0                                */
 } wushkv_config;
 
 /*
@@ -105,6 +109,20 @@ typedef struct {
  *   kring,vring bfloat16 [unit][ring_slots][d]     recent window; position p
  *                 (p >= sink) lives in slot (p - sink) % ring_slots.
  *
+ * Paged caches (page_size P > 0) keep the quantized planes (kcode, vcode,
+ * ksz, vsz) in a pool of n_pages physical pages per layer, each holding P
+ * positions of every KV head, the form of the paged KV caches of the serving
+ * system the paper integrates the method into (paper page, section 2 on
+ * SGLang's paged caches; section 5.3 for the integration):
+ *
+ *   kcode  uint8  [layer][page][head][P][code_bytes]
+ *   vcode  uint8  [layer][page][head][P/vblock][d][16]
+ *   ksz,vsz uint16[layer][page][head][P][2]
+ *
+ * Position p of slot s lives at offset p % P of physical page
+ * table[s][p / P] of the block table bound with wushkv_set_block_table (the
+ * same page in every layer).  Windows (sink, ring) stay per slot as above.
+ *
  * Keys in the cache are in the transformed basis (T_K k, rounded to bfloat16
  * before quantization); values are as given (rounded to bfloat16).  After a
  * sequence reaches length L, positions [sink, squant(L)) are quantized and
@@ -124,6 +142,9 @@ typedef struct {
   int32_t cpos;         /* positions per unit: ctx_cap rounded up to 128 */
   int32_t ring_slots;   /* recent + flush - 1                        */
   int32_t units;        /* n_layers * max_batch * n_kv_heads         */
+  int32_t page_size;    /* paged: P; contiguous: 0                   */
+  int32_t n_pages;      /* paged: physical pages per layer; else 0   */
+  int32_t pages_per_seq; /* paged: block-table row length ceil(ctx_cap / P); else 0 */
 } wushkv_layout_t;
 
 typedef struct wushkv_cache wushkv_cache;
@@ -147,6 +168,24 @@ wushkv_status wushkv_layout(const wushkv_config* cfg, wushkv_layout_t* out);
 wushkv_status wushkv_cache_create(const wushkv_config* cfg, void* arena, uint64_t arena_bytes,
                                   wushkv_cache** out);
 void wushkv_cache_destroy(wushkv_cache* cache);
+
+/*
+ * Paged caches only (EINVAL otherwise, or for a null or unaligned table):
+ * bind the block table, device int32 [max_batch][pages_per_seq].  Entry
+ * [s][i] names the physical page (0 <= id < n_pages) that holds positions
+ * [i P, (i + 1) P) of slot s in every layer.  Kernels read the table when
+ * they run, in stream order, so the caller may change entries between calls
+ * with stream-ordered copies; the table must stay allocated while calls that
+ * use it are in flight.  Before a call, every page holding a position that
+ * the call quantizes (positions of [sink, squant(L')) it writes) or that
+ * attention reads (positions of [sink, squant(L))) must be mapped, and two
+ * slots must not map the same page.  Entries of pages without such positions
+ * are not read.  An out-of-range entry makes the library skip the writes to
+ * that page and read the pool's first page instead: the results for that
+ * sequence are then unspecified, but no access leaves the arena.  Host only;
+ * append and decode calls on a paged cache with no table return EINVAL.
+ */
+wushkv_status wushkv_set_block_table(wushkv_cache* cache, const int32_t* table);
 
 /* Forget slot's contents in every layer (length 0; S_quant back to sink). */
 wushkv_status wushkv_reset_seq(wushkv_cache* cache, int32_t slot);

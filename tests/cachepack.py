@@ -47,6 +47,37 @@ def bf16_to_f64(u16: np.ndarray) -> np.ndarray:
     return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def row_runs(dc, layer: int, slot: int, head: int, n: int):
+    """Runs (first position, first row or None when unmapped, positions) of the
+    quantized-plane rows holding positions [0, n) of one unit, per the
+    documented contiguous or paged layout (the block table read back from the
+    device)."""
+    c, lay = dc.cfg, dc.layout
+    if lay.page_size == 0:
+        return [(0, _unit(dc, layer, slot, head) * lay.cpos, lay.cpos)]
+    P = lay.page_size
+    table = dc.table[slot].cpu().numpy()
+    runs = []
+    for i in range((max(n, 1) + P - 1) // P):
+        pg = int(table[i])
+        row0 = ((layer * lay.n_pages + pg) * c.n_kv_heads + head) * P if 0 <= pg < lay.n_pages else None
+        runs.append((i * P, row0, P))
+    return runs
+
+
+def _read_rows(dc, runs, name, row_bytes, rows_per_unit=1):
+    """Concatenate plane bytes of the runs ([positions, row_bytes]; zeros for
+    unmapped runs); rows_per_unit > 1 reads whole value-code blocks."""
+    parts = []
+    for _, row0, cnt in runs:
+        nb = cnt // rows_per_unit * row_bytes
+        if row0 is None:
+            parts.append(np.zeros(nb, dtype=np.uint8))
+        else:
+            parts.append(_slice(dc, name, row0 // rows_per_unit * row_bytes, nb).cpu().numpy())
+    return np.concatenate(parts)
+
+
 def read_unit(dc, layer: int, slot: int, head: int, L: int) -> dict:
     """Canonical contents of one unit at length L: codes [L, 128] (uint8; rows
     outside the quantized region are garbage), s/z [L], window values [L, 128]
@@ -54,16 +85,16 @@ def read_unit(dc, layer: int, slot: int, head: int, L: int) -> dict:
     c, lay = dc.cfg, dc.layout
     u = _unit(dc, layer, slot, head)
     bits, S, W = c.bits, c.sink, lay.ring_slots
-    cb, cpos, VB = lay.code_bytes, lay.cpos, lay.vblock
+    cb, VB = lay.code_bytes, lay.vblock
     n = max(L, 1)
-    kraw = _slice(dc, "kcode", u * cpos * cb, cpos * cb).cpu().numpy().reshape(cpos, cb)[:n]
+    runs = row_runs(dc, layer, slot, head, n)
+    kraw = _read_rows(dc, runs, "kcode", cb).reshape(-1, cb)[:n]
     kcodes = unpack_bits(kraw, bits, 128).astype(np.uint8)
-    vraw = _slice(dc, "vcode", u * lay.ctx_blocks * 128 * 16, lay.ctx_blocks * 128 * 16)
-    vraw = vraw.cpu().numpy().reshape(lay.ctx_blocks, 128, 16)
+    vraw = _read_rows(dc, runs, "vcode", 128 * 16, VB).reshape(-1, 128, 16)
     vc = unpack_bits(vraw, bits, VB)                     # [blocks, 128 dims, VB]
     vcodes = vc.transpose(0, 2, 1).reshape(-1, 128)[:n].astype(np.uint8)
-    ksz = _slice(dc, "ksz", u * cpos * 4, cpos * 4).cpu().numpy().view(np.uint32)[:n]
-    vsz = _slice(dc, "vsz", u * cpos * 4, cpos * 4).cpu().numpy().view(np.uint32)[:n]
+    ksz = _read_rows(dc, runs, "ksz", 4).view(np.uint32)[:n]
+    vsz = _read_rows(dc, runs, "vsz", 4).view(np.uint32)[:n]
     ks, kz = f16_pair(ksz)
     vs, vz = f16_pair(vsz)
     sq = S + c.flush * (max(0, L - c.recent - S) // c.flush)
@@ -91,28 +122,37 @@ def write_unit(dc, layer: int, slot: int, head: int, L: int, contents: dict) -> 
     c, lay = dc.cfg, dc.layout
     u = _unit(dc, layer, slot, head)
     bits, S, W = c.bits, c.sink, lay.ring_slots
-    cb, cpos, VB = lay.code_bytes, lay.cpos, lay.vblock
+    cb, VB = lay.code_bytes, lay.vblock
     dev = dc.device
-    kc = np.zeros((cpos, 128), dtype=np.uint8)
-    vcd = np.zeros((cpos, 128), dtype=np.uint8)
+    runs = row_runs(dc, layer, slot, head, L)
+    npos = sum(cnt for _, _, cnt in runs)
+    kc = np.zeros((npos, 128), dtype=np.uint8)
+    vcd = np.zeros((npos, 128), dtype=np.uint8)
     kc[:L] = contents["kcodes"][:L]
     vcd[:L] = contents["vcodes"][:L]
-    kraw = pack_bits(kc, bits)
-    vblk = vcd.reshape(lay.ctx_blocks, VB, 128).transpose(0, 2, 1)    # [blocks, dims, VB]
+    kraw = pack_bits(kc, bits)                                          # [positions, cb]
+    vblk = vcd.reshape(npos // VB, VB, 128).transpose(0, 2, 1)          # [blocks, dims, VB]
     vraw = pack_bits(np.ascontiguousarray(vblk), bits)                  # [blocks, dims, 16]
-    _slice(dc, "kcode", u * cpos * cb, cpos * cb).copy_(torch.from_numpy(kraw.reshape(-1)).to(dev))
-    _slice(dc, "vcode", u * lay.ctx_blocks * 2048, lay.ctx_blocks * 2048).copy_(
-        torch.from_numpy(vraw.reshape(-1)).to(dev))
 
     def sz(s, z):
-        out = np.zeros(cpos, dtype=np.uint32)
+        out = np.zeros(npos, dtype=np.uint32)
         su = np.asarray(s[:L], dtype=np.float16).view(np.uint16).astype(np.uint32)
         zu = np.asarray(z[:L], dtype=np.float16).view(np.uint16).astype(np.uint32)
         out[:L] = su | (zu << 16)
-        return torch.from_numpy(out.view(np.uint8)).to(dev)
+        return out
 
-    _slice(dc, "ksz", u * cpos * 4, cpos * 4).copy_(sz(contents["ks16"], contents["kz16"]))
-    _slice(dc, "vsz", u * cpos * 4, cpos * 4).copy_(sz(contents["vs16"], contents["vz16"]))
+    ksz = sz(contents["ks16"], contents["kz16"])
+    vsz = sz(contents["vs16"], contents["vz16"])
+    for p0, row0, cnt in runs:
+        if row0 is None:
+            continue
+        planes = (("kcode", kraw[p0:p0 + cnt], row0 * cb),
+                  ("vcode", vraw[p0 // VB:(p0 + cnt) // VB], row0 // VB * 2048),
+                  ("ksz", ksz[p0:p0 + cnt].view(np.uint8), row0 * 4),
+                  ("vsz", vsz[p0:p0 + cnt].view(np.uint8), row0 * 4))
+        for name, arr, off in planes:
+            arr = np.ascontiguousarray(arr).reshape(-1)
+            _slice(dc, name, off, arr.size).copy_(torch.from_numpy(arr).to(dev))
 
     def bf(x):
         return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.uint8)

@@ -195,3 +195,55 @@ def test_codec_config_check():
     assert wk.wushkv_config_check(_cfg(codec=2)) == wk.WUSHKV_EINVAL
     assert wk.wushkv_config_check(_cfg(clip_alpha=-1.0)) == wk.WUSHKV_EINVAL
     assert wk.wushkv_config_check(_cfg(clip_alpha=float("nan"))) == wk.WUSHKV_EINVAL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=128, n_pages=10), wk.WUSHKV_OK),
+    (dict(page_size=4096, n_pages=1), wk.WUSHKV_OK),
+    (dict(page_size=64, n_pages=10), wk.WUSHKV_EINVAL),     # below one decode sub-chunk
+    (dict(page_size=384, n_pages=10), wk.WUSHKV_EINVAL),    # not a power of two
+    (dict(page_size=128, n_pages=0), wk.WUSHKV_EINVAL),     # empty pool
+    (dict(page_size=0, n_pages=3), wk.WUSHKV_EINVAL),       # pool size without paging
+    (dict(page_size=1 << 21, n_pages=1), wk.WUSHKV_EINVAL),
+])
+def test_paged_config_check(kw, status):
+    assert wk.wushkv_config_check(_cfg(**kw)) == status
+
+
+def test_paged_layout():
+    """Paged planes hold n_pages pages of page_size positions per (layer, KV
+    head); windows stay per slot; the block-table row covers ctx_cap."""
+    cfg = _cfg(n_layers=3, n_kv_heads=8, n_q_heads=32, max_batch=5, ctx_cap=1000,
+               page_size=256, n_pages=7)
+    lay = wk.wushkv_layout(cfg)
+    rows = 3 * 7 * 8 * 256
+    assert (lay.page_size, lay.n_pages, lay.pages_per_seq) == (256, 7, 4)
+    assert lay.bytes_kcode == rows * 32 and lay.bytes_vcode == rows * 32
+    assert lay.bytes_ksz == rows * 4 and lay.bytes_vsz == rows * 4
+    assert lay.bytes_ksink == 3 * 5 * 8 * 4 * 256
+    assert lay.bytes_kring == 3 * 5 * 8 * 128 * 256
+    flat = wk.wushkv_layout(_cfg(n_layers=3, n_kv_heads=8, n_q_heads=32, max_batch=5, ctx_cap=1000))
+    assert (flat.page_size, flat.n_pages, flat.pages_per_seq) == (0, 0, 0)
+    assert flat.bytes_ksink == lay.bytes_ksink
+
+
+def test_block_table_binding():
+    P = 1 << 41
+    h, _ = _fake_cache()
+    with pytest.raises(wk.WushkvError):      # contiguous cache
+        wk.wushkv_set_block_table(h, P)
+    wk.wushkv_cache_destroy(h)
+    h, _ = _fake_cache(page_size=128, n_pages=4)
+    need = wk.wushkv_decode_workspace_bytes(h, 1)
+    # no table bound yet: appends and decodes are refused before any launch
+    assert wk.wushkv_append(h, 0, [0], [1], P, P, P, check=False) == wk.WUSHKV_EINVAL
+    assert wk.wushkv_decode_step(h, 0, [0], P, P, P, P, P, P, P, need, check=False) == \
+        wk.WUSHKV_EINVAL
+    with pytest.raises(wk.WushkvError):
+        wk.wushkv_set_block_table(h, 0)
+    with pytest.raises(wk.WushkvError):
+        wk.wushkv_set_block_table(h, P + 2)
+    wk.wushkv_set_block_table(h, P)
+    assert wk.wushkv_append(h, 0, [0], [0], P, P, P, check=False) == wk.WUSHKV_OK
+    assert wk.wushkv_get_len(h, 0, 0) == (0, 4)
+    wk.wushkv_cache_destroy(h)

@@ -36,8 +36,15 @@ def _gpu():
 
 
 def _cache(w: synth.Workload, *, bits=None, S=None, R=None, F=None, max_batch=None, ctx_cap=None,
-           p_lo=None, p_hi=None, n_layers=None, rms_alpha=None):
+           p_lo=None, p_hi=None, n_layers=None, rms_alpha=None, page=0):
+    """page > 0: a paged cache with pages of that many positions, a pool of
+    every slot's worth plus three, handed out in a seeded shuffled order (so
+    consecutive pages of a sequence are scattered through the pool)."""
     codec = {} if rms_alpha is None else dict(codec=1, clip_alpha=rms_alpha)
+    if page:
+        nb, cap = max_batch or w.batch, ctx_cap or max(w.lengths())
+        codec.update(page_size=page, n_pages=nb * ((cap + page - 1) // page) + 3,
+                     page_seed=1234 + page)
     return DeviceCache(n_layers=n_layers or 1, n_q_heads=w.n_q, n_kv_heads=w.n_kv,
                        bits=bits or w.bits[0], sink=w.sink if S is None else S,
                        recent=w.recent if R is None else R, flush=F or w.flush,
@@ -98,10 +105,10 @@ def _check_state(dc, w, ks, vs, T):
 
 
 def _run_e2e(w, plan, *, bits=None, S=None, R=None, F=None, p_lo=None, p_hi=None, lengths=None,
-             check_attn=True, rms_alpha=None):
+             check_attn=True, rms_alpha=None, page=0):
     lengths = lengths or w.lengths()
     dc = _cache(w, bits=bits, S=S, R=R, F=F, p_lo=p_lo, p_hi=p_hi, max_batch=len(lengths),
-                ctx_cap=max(lengths), rms_alpha=rms_alpha)
+                ctx_cap=max(lengths), rms_alpha=rms_alpha, page=page)
     T, Tq = synth.transforms(w, 0)
     ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
     slots = list(range(len(lengths)))
@@ -281,7 +288,7 @@ def test_decode_twice_bitwise_deterministic():
 # ------------------------------------------------------------------ decode step
 
 def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_every=1,
-               rms_alpha=None):
+               rms_alpha=None, page=0):
     """Prefill L0s[i] positions per sequence with wushkv_append, then n_steps
     fused decode steps.  Each step's output is checked against the oracle's
     attention over the state before the flush (section 4.4: the new entry
@@ -290,7 +297,7 @@ def _run_steps(w, L0s, n_steps, *, bits=None, S=None, R=None, F=None, check_ever
     cache at its length."""
     lengths = [L0 + n_steps for L0 in L0s]
     dc = _cache(w, bits=bits, S=S, R=R, F=F, max_batch=len(lengths), ctx_cap=max(lengths),
-                rms_alpha=rms_alpha)
+                rms_alpha=rms_alpha, page=page)
     c = dc.cfg
     T, Tq = synth.transforms(w, 0)
     ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
@@ -397,3 +404,97 @@ def test_rms_codec_prefill_kernel(bits):
 
 def test_rms_codec_decode_step():
     _run_steps(synth.WORKLOADS[0], [500], 12, rms_alpha=1.9)
+
+
+# ------------------------------------------------------------------ paged cache
+
+def test_paged_fp32_path():
+    """Paged quantized planes (128-position pages, shuffled pool) through the
+    rank-sort append kernel: prefill, token appends, decode attention."""
+    _run_e2e(synth.WORKLOADS[0], [700, 1, 1, 300, 22], page=128)
+
+
+@pytest.mark.parametrize("page,bits", [(128, 2), (256, 4), (1024, 2)])
+def test_paged_prefill_kernel(page, bits):
+    """The matrix-core prefill kernel writing paged planes: tiles that start
+    mid-page, pages shared out across a ragged GQA batch."""
+    w = synth.WORKLOADS[1]
+    _run_e2e(w, [700, 3, 1, 1, 600, 5], bits=bits, lengths=[1310, 2, 907], page=page)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_paged_decode_steps_batched_flush(bits):
+    """Fused decode steps on a paged cache with the paper's evaluation windows
+    (sink 16, recent 128, flush 16): pages mapped as the quantized region
+    grows, 16 ring entries quantized every 16th step."""
+    _run_steps(synth.WORKLOADS[1], [1500, 0, 777], 40, bits=bits, S=16, R=128, F=16,
+               check_every=8, page=128)
+
+
+def test_paged_equals_contiguous():
+    """A paged cache and a contiguous one fed the same inputs store the same
+    codes, scale/zero and windows and produce bit-identical attention."""
+    w = synth.WORKLOADS[1]
+    lengths = [1310, 2, 907]
+    slots = list(range(3))
+    T, Tq = synth.transforms(w, 0)
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    ks, vs = zip(*[_inputs(w, 0, si, L + 20) for si, L in enumerate(lengths)])
+    outs = []
+    caches = []
+    for page in (0, 128):
+        dc = _cache(w, max_batch=3, ctx_cap=max(lengths) + 20, page=page)
+        kk = torch.cat([ks[i][:lengths[i]] for i in slots]).cuda().contiguous()
+        vv = torch.cat([vs[i][:lengths[i]] for i in slots]).cuda().contiguous()
+        dc.append(0, slots, lengths, kk, vv, tk)
+        o = []
+        for st in range(20):
+            k1 = torch.stack([ks[i][lengths[i] + st] for i in slots]).cuda().contiguous()
+            v1 = torch.stack([vs[i][lengths[i] + st] for i in slots]).cuda().contiguous()
+            q = synth.queries(w, 0, st, 3).cuda()
+            o.append(dc.decode_step(0, slots, k1, v1, tk, q, tq).cpu())
+        outs.append(torch.stack(o))
+        caches.append(dc)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    for si, L in enumerate(lengths):
+        for h in range(w.n_kv):
+            a = read_unit(caches[0], 0, si, h, L + 20)
+            b = read_unit(caches[1], 0, si, h, L + 20)
+            sq = a["squant"]
+            for key in ("kcodes", "vcodes", "ks16", "kz16", "vs16", "vz16"):
+                assert np.array_equal(a[key][4:sq], b[key][4:sq]), key
+            for key in ("kwin", "vwin"):
+                assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
+
+
+def test_paged_pages_reused_after_reset():
+    """Pages returned by a finished sequence are handed to a new one: its
+    results depend only on its own entries (stale codes in reused pages are
+    overwritten before they are read)."""
+    w = _bf16_workload(1800)
+    dc = _cache(w, max_batch=2, ctx_cap=1800, page=128)
+    T, Tq = synth.transforms(w, 0)
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    k, v = _inputs(w, 0, 0, 1800)
+    dc.append(0, [0], [1800], k.cuda(), v.cuda(), tk)
+    used = dc.pages_in_use()
+    dc.reset_seq(0)
+    assert dc.pages_in_use() == 0
+    k2, v2 = synth.keys_values(w, 0, 1, 0, 1500)
+    dc.append(0, [1], [1200], k2[:1200].contiguous().cuda(), v2[:1200].contiguous().cuda(), tk)
+    dc.append(0, [1], [300], k2[1200:].contiguous().cuda(), v2[1200:].contiguous().cuda(), tk)
+    assert 0 < dc.pages_in_use() <= used
+    q = synth.queries(w, 0, 0, 1)
+    out = dc.decode_attn(0, [1], q.cuda(), tq).cpu().numpy()
+    torch.cuda.synchronize()
+    units = {}
+    for h in range(w.n_kv):
+        orc = oracle.cache_unit(k2[:, h].double().numpy(), v2[:, h].double().numpy(),
+                                T[h].astype(np.float64), S=w.sink, R=w.recent, F=w.flush,
+                                bits=2, p_lo=w.p_lo, p_hi=w.p_hi)
+        gpu = read_unit(dc, 0, 1, h, 1500)
+        check_windows(gpu, orc)
+        check_codes(gpu, orc, 2)
+        units[h] = orc
+    check_attention(out[0], reference_attention(w, T, q[0], units))
