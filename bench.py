@@ -526,6 +526,8 @@ def main():
                     help="time a paged cache with pages of this many positions (0: contiguous)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the secondary measurement of the same steps on a paged cache")
+    ap.add_argument("--no-3bit", action="store_true",
+                    help="skip the secondary measurement of the same steps on a 3-bit cache")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-append measurement")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the streaming-read ceiling and the bf16-cache comparison")
@@ -655,17 +657,25 @@ def main():
                                f"{K} steps ({round(total_b_ms / K, 4)} ms/step with the events)"},
         "cache_build_s": round(build_s, 2),
     }
+    def variant(m, note, **extra):
+        return dict(extra, note=note, ms_per_step=round(m["ms_per_step"], 4),
+                    value=round(m["value"], 2), split_achieved=round(m["achieved"], 2),
+                    split_frac=round(m["achieved"] / HBM_PEAK_GBS, 4),
+                    avg_launch_ms=round(m["split_avg_ms"], 5),
+                    bytes_per_launch=int(m["bytes_per_launch"]),
+                    step_time_vs_headline=round(m["ms_per_step"] / ms_per_step, 4))
+
     if not args.no_paged and args.page_size == 0:
         pg = measure_decode(w, bits, K, W, dev, fused, page_size=128)
-        res["paged"] = {
-            "page_size": 128, "n_pages": pg["n_pages"],
-            "note": "the same steps on a paged cache: quantized planes in 128-position pages "
-                    "handed out in shuffled order, block table read by the kernels",
-            "ms_per_step": round(pg["ms_per_step"], 4), "value": round(pg["value"], 2),
-            "split_achieved": round(pg["achieved"], 2),
-            "split_frac": round(pg["achieved"] / HBM_PEAK_GBS, 4),
-            "avg_launch_ms": round(pg["split_avg_ms"], 5),
-            "step_time_vs_contiguous": round(pg["ms_per_step"] / ms_per_step, 4)}
+        res["paged"] = variant(
+            pg, "the same steps on a paged cache: quantized planes in 128-position pages "
+                "handed out in shuffled order, block table read by the kernels",
+            page_size=128, n_pages=pg["n_pages"])
+    if not args.no_3bit and bits == 2:
+        b3 = measure_decode(w, 3, K, W, dev, fused)
+        res["bits_3"] = variant(
+            b3, "the same steps on a 3-bit cache (low two bits and high bit in separate "
+                "planes, 104 B per quantized token-head)", bits=3)
     if not args.no_reference:
         ceil = read_ceiling(bytes_per_launch, dev)
         res["roofline"]["read_ceiling_gbs"] = ceil

@@ -82,7 +82,7 @@ extern "C" wushkv_status wushkv_config_check(const wushkv_config* c) {
   if (c->codec != WUSHKV_CODEC_PERCENTILE && c->codec != WUSHKV_CODEC_RMS) return WUSHKV_EINVAL;
   if (!(c->clip_alpha >= 0.0 && c->clip_alpha < 1e6)) return WUSHKV_EINVAL;
   if (c->head_dim != D) return WUSHKV_EUNSUPPORTED;
-  if (c->bits != 2 && c->bits != 4) return WUSHKV_EUNSUPPORTED;
+  if (c->bits < 2 || c->bits > 4) return WUSHKV_EUNSUPPORTED;
   {
     const int G = c->n_q_heads / c->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return WUSHKV_EUNSUPPORTED;
@@ -107,7 +107,9 @@ extern "C" wushkv_status wushkv_layout(const wushkv_config* c, wushkv_layout_t* 
   wushkv_layout_t L;
   memset(&L, 0, sizeof(L));
   L.code_bytes = D * c->bits / 8;
-  L.vblock = 128 / c->bits;
+  // value-code block: one 16-byte row per dimension (2, 4 bits) or two
+  // low-plane rows and one high-plane row (3 bits)
+  L.vblock = c->bits == 3 ? 128 : 128 / c->bits;
   // positions per unit: ctx_cap rounded up to 128 (whole decode sub-chunks)
   L.cpos = (c->ctx_cap + 127) / 128 * 128;
   L.ctx_blocks = L.cpos / L.vblock;
@@ -124,7 +126,7 @@ extern "C" wushkv_status wushkv_layout(const wushkv_config* c, wushkv_layout_t* 
            (uint64_t)c->page_size;
   }
   L.bytes_kcode = rows * L.code_bytes;
-  L.bytes_vcode = rows / L.vblock * D * 16;
+  L.bytes_vcode = rows * L.code_bytes;
   L.bytes_ksz = rows * 4;
   L.bytes_vsz = L.bytes_ksz;
   L.bytes_ksink = u * (uint64_t)c->sink * D * 2;

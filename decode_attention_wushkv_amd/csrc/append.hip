@@ -24,7 +24,7 @@ __device__ __forceinline__ uint16_t io_to_bf16(const void* base, int64_t idx) {
   return f32_to_bf16(((const float*)base)[idx]);
 }
 
-template <int IO_BF16>
+template <int IO_BF16, bool B3>
 __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   __shared__ QLds L;
   __shared__ float kvec[D];
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   const int sq0 = squant_of(L0, g.S, g.R, g.F);
   const int sq1 = squant_of(L1, g.S, g.R, g.F);
 
-  VRow vr;
-  vr.blk = -1;
+  VRows vr;
+  vrows_init(vr);
 
   // Entries already in the ring that leave the recent window.
   if (a.mode != APPEND_CHUNKED) {
@@ -52,10 +52,10 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       const int64_t row = (unit * g.W + (p - g.S) % g.W) * D + i;
       float kx = bf16_bits_to_f32(a.pl.kring[row]);
       float vx = bf16_bits_to_f32(a.pl.vring[row]);
-      store_quantized(p, kx, vx, L, vr, a.pl, qm, g);
+      store_quantized<B3>(p, kx, vx, L, vr, a.pl, qm, g);
     }
     if (a.mode == APPEND_EVICT) {
-      vrow_flush(vr, a.pl, qm, g);
+      vrows_flush<B3>(vr, a.pl);
       return;
     }
   }
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
     if (c1 > L1) c1 = L1;
   }
   if (c0 >= c1) {
-    vrow_flush(vr, a.pl, qm, g);
+    vrows_flush<B3>(vr, a.pl);
     return;
   }
 
@@ -104,21 +104,26 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       a.pl.kring[o] = kb;
       a.pl.vring[o] = vb;
     } else {
-      store_quantized(p, bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), L, vr, a.pl, qm, g);
+      store_quantized<B3>(p, bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), L, vr, a.pl, qm, g);
     }
     __syncthreads();  // kvec reuse
   }
-  vrow_flush(vr, a.pl, qm, g);
+  vrows_flush<B3>(vr, a.pl);
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, int io_bf16, int grid_x, int n_seq, hipStream_t st) {
   dim3 grid(grid_x, a.g.n_kv, n_seq);
-  if (io_bf16)
-    hipLaunchKernelGGL(append_kernel<1>, grid, dim3(128), 0, st, a);
+  const bool b3 = a.g.bits == 3;
+  if (io_bf16 && b3)
+    hipLaunchKernelGGL((append_kernel<1, true>), grid, dim3(128), 0, st, a);
+  else if (io_bf16)
+    hipLaunchKernelGGL((append_kernel<1, false>), grid, dim3(128), 0, st, a);
+  else if (b3)
+    hipLaunchKernelGGL((append_kernel<0, true>), grid, dim3(128), 0, st, a);
   else
-    hipLaunchKernelGGL(append_kernel<0>, grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((append_kernel<0, false>), grid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

@@ -14,9 +14,21 @@ constexpr int MAXSEQ = 128;     // sequences per call (kernel-argument tables)
 constexpr int WINDOW_MAX = 1024; // sink + ring entries scored by one workgroup
 constexpr int CHUNK = 256;       // prefill append: positions per workgroup (multiple of vblock)
 
-// Decode sub-chunk of one wave: 128 positions at 2 bits, 64 at 4 bits (equal
-// code bytes; a multiple of the value-code block).
-__host__ __device__ constexpr int sub_len(int bits) { return 256 / bits; }
+// Decode sub-chunk of one wave: 128 positions at 2 bits, 64 at 3 and 4 bits
+// (whole 16-byte value rows; at 3 bits half of a block's high-plane row).
+__host__ __device__ constexpr int sub_len(int bits) { return bits == 2 ? 128 : 64; }
+
+// 3-bit codes are stored as two bit planes: the low two bits of every code in
+// the 2-bit packing, and the high bit in a 1-bit plane where bit 4 n + k of
+// 32-bit word j holds element 32 j + 16 (k >> 1) + 2 n + (k & 1) (element =
+// dimension of a key row, position of a value row).  Then (word >> k) &
+// 0x11111111 lines up nibble for nibble with the even (k even) or odd (k odd)
+// elements of 2-bit word 2 j + (k >> 1), which the decode kernels unpack as
+// (w & 0x33333333) and ((w >> 2) & 0x33333333).  hi_bit(e) is the bit of
+// element e (0 <= e < 128) in its 128-bit high plane.
+__host__ __device__ constexpr int hi_bit(int e) {
+  return 32 * (e >> 5) + 4 * ((e & 15) >> 1) + ((((e & 31) >> 4) << 1) | (e & 1));
+}
 // Upper bound on workgroups per (sequence, KV head) in one decode call (the
 // host picks the actual count from the GPU's occupancy); sizes the workspace.
 __host__ __device__ inline int max_chunks(int n_seq, int n_kv) {
@@ -62,8 +74,10 @@ struct Geometry {
 
 // Where the quantized planes keep one (layer, sequence, KV head): position p
 // is row r of kcode (bytes r * code_bytes), ksz and vsz, and its value codes
-// lie in block r / vblock of vcode.  A page (at least 128 positions, a power
-// of two) holds whole decode sub-chunks and value-code blocks.
+// lie in block r / vblock of vcode (one 16-byte row per dimension at 2 and 4
+// bits; at 3 bits two low-plane rows and one high-plane row).  A page (at
+// least 128 positions, a power of two) holds whole decode sub-chunks and
+// value-code blocks.
 struct QMap {
   const int32_t* pages;  // the sequence's block-table row; null when contiguous
   int64_t base;          // row of position 0 (contiguous) or of physical page 0 (paged)

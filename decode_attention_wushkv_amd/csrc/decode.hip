@@ -149,14 +149,17 @@ __device__ __forceinline__ void wave_sync() {
 template <int BITS, int G>
 struct SplitCfg {
   static constexpr int TW = sub_len(BITS);     // positions per wave sub-chunk
-  static constexpr int VB = 128 / BITS;        // positions per value-code block
-  static constexpr int NBW = TW / VB;          // value blocks per sub-chunk (2)
+  // positions per 16-byte value row of a dimension (at 3 bits: per low-plane
+  // row; a sub-chunk reads half of its block's high-plane row)
+  static constexpr int VB = BITS == 3 ? 64 : 128 / BITS;
+  static constexpr int NBW = TW / VB;          // value rows per sub-chunk (2; 1 at 3 bits)
   static constexpr int CB = 16 * BITS;         // key-code bytes per position
   static constexpr int ROWS = TW / 32;         // positions per lane pair
-  static constexpr int KQ = CB / 32;           // uint4 per lane (half a position)
-  static constexpr int GS = BITS == 2 ? 16 : 8;  // positions per 32-bit value-row word
+  static constexpr int KQ = BITS == 4 ? 2 : 1; // uint4 per lane (half a position; low plane at 3 bits)
+  static constexpr bool SPLIT2 = BITS != 4;    // 2-bit nibble unpacking (low plane at 3 bits)
+  static constexpr int GS = SPLIT2 ? 16 : 8;   // positions per 32-bit value-row word
   static constexpr int NG = TW / GS;           // value-row words per sub-chunk (8)
-  static constexpr int WGW = BITS == 2 ? 2 * WDIG : WDIG;  // digit words per row word
+  static constexpr int WGW = SPLIT2 ? 2 * WDIG : WDIG;  // digit words per row word
   static constexpr int WGP = (WGW + 3) / 4 * 4;            // ... padded to 16 bytes
   static constexpr bool QREG = G <= 2;         // query digits held in registers
   // G >= 4: head split (the four waves of a quantized workgroup walk the same
@@ -263,13 +266,13 @@ __device__ void compensate_query(const DecodeArgs& a, int h, int si, uint32_t* s
   __syncthreads();
   // digit words: group x / DIGP of 8 dimensions, digit k = x % DIGP; nibble n
   // holds that digit of one dimension of the group.
-  //   2 bits: group = half * 8 + w * 2 + parity, dims 64 half + 16 w + 2 n + parity
-  //   4 bits: group = half * 8 + w,              dims 64 half + 8 w + n
+  //   2, 3 bits: group = half * 8 + w * 2 + parity, dims 64 half + 16 w + 2 n + parity
+  //   4 bits:    group = half * 8 + w,              dims 64 half + 8 w + n
   for (int x = tid; x < G * 16 * DIGP; x += 256) {
     const int gg = x / (16 * DIGP), rem = x % (16 * DIGP);
     const int grp16 = rem / DIGP, k = rem % DIGP, half = grp16 >> 3;
     int e0, step;
-    if (BITS == 2) {
+    if (BITS != 4) {
       e0 = 64 * half + 16 * ((grp16 >> 1) & 3) + (grp16 & 1);
       step = 2;
     } else {
@@ -298,6 +301,10 @@ struct SubBuf {
   uint4 kc[C::ROWS][C::KQ];
   uint32_t ksz[C::ROWS], vsz[C::ROWS];
   uint4 vc[C::NBW][2];
+  // 3 bits: high-plane bits of the keys (half a position) and of the value
+  // rows (the sub-chunk's 64 positions)
+  uint2 kh[BITS == 3 ? C::ROWS : 1];
+  uint2 vh[2];
 };
 
 template <int BITS, int G>
@@ -306,21 +313,34 @@ __device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
   const int64_t row = qrow_read(qm, pbase);
-  const uint8_t* kb = a.pl.kcode + (row + tq) * C::CB + half * (C::CB / 2);
+  // 3 bits: low plane in bytes [0, 32) of a position, high plane in [32, 48)
+  const uint8_t* kb = a.pl.kcode + (row + tq) * C::CB + half * (BITS == 3 ? 16 : C::CB / 2);
   const uint32_t* kz = a.pl.ksz + row + tq;
   const uint32_t* vz = a.pl.vsz + row + tq;
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
 #pragma unroll
     for (int q = 0; q < C::KQ; ++q) b.kc[r][q] = ((const uint4*)(kb + (int64_t)(32 * r) * C::CB))[q];
+    if constexpr (BITS == 3)
+      b.kh[r] = *(const uint2*)(a.pl.kcode + (row + tq + 32 * r) * C::CB + 32 + 8 * half);
     b.ksz[r] = kz[32 * r];
     b.vsz[r] = vz[32 * r];
   }
-  const uint8_t* vb = a.pl.vcode + ((row / C::VB) * D + lane) * 16;
+  // value rows of dimensions lane and lane + 64; at 3 bits the 128-position
+  // block holds two low-plane rows (the sub-chunk's is row sel) and the
+  // high-plane row (the sub-chunk's half at byte 8 sel)
+  const int sel = BITS == 3 ? (int)((row >> 6) & 1) : 0;
+  const uint8_t* vb = BITS == 3 ? a.pl.vcode + (((row >> 7) * 3 + sel) * D + lane) * 16
+                                : a.pl.vcode + ((row / C::VB) * D + lane) * 16;
 #pragma unroll
   for (int k = 0; k < C::NBW; ++k) {
     b.vc[k][0] = *(const uint4*)(vb + (int64_t)k * D * 16);
     b.vc[k][1] = *(const uint4*)(vb + (int64_t)k * D * 16 + 64 * 16);
+  }
+  if constexpr (BITS == 3) {
+    const uint8_t* hb = vb + (2 - sel) * D * 16 + 8 * sel;
+    b.vh[0] = *(const uint2*)hb;
+    b.vh[1] = *(const uint2*)(hb + 64 * 16);
   }
 }
 
@@ -371,6 +391,14 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
           // x = 2 w + parity: parity 0 takes the even dimensions of code word w
           const uint32_t dw = d[x >> 1];
           X = (int)((x & 1) ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u));
+        } else if constexpr (BITS == 3) {
+          // low two bits as at 2 bits, high bit from high-plane word w / 2 at
+          // shift k = 2 (w & 1) + parity (the plane's element order)
+          const uint32_t dw = d[x >> 1];
+          const uint32_t hw = (x >> 2) ? b.kh[r].y : b.kh[r].x;
+          const int k = (((x >> 1) & 1) << 1) | (x & 1);
+          const uint32_t lo2 = (x & 1) ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u);
+          X = (int)(lo2 | (((hw >> k) & 0x11111111u) << 2));
         } else {
           X = (int)(d[x] ^ 0x88888888u);  // code - 8 as a signed nibble
         }
@@ -413,7 +441,7 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
 #pragma unroll
     for (int r = 0; r < C::ROWS; ++r) {
       const int t = 32 * r + tq;
-      const int slot = BITS == 2 ? ((t & ~15) | ((t & 1) << 3) | ((t & 15) >> 1)) : t;
+      const int slot = C::SPLIT2 ? ((t & ~15) | ((t & 1) << 3) | ((t & 15) >> 1)) : t;
       lsum[gg] += pw[r][gg];
       zsum[gg] = fmaf(pw[r][gg], vz[r], zsum[gg]);
       if (!half) wq[gg * C::TW + slot] = (uint32_t)fminf(rintf(pw[r][gg] * vs[r] * wscale), (float)WMAX);
@@ -427,7 +455,7 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
   for (int x = lane; x < G * C::NG * C::WGW; x += 64) {
     const int gg = x / (C::NG * C::WGW), rem = x % (C::NG * C::WGW);
     const int gi = rem / C::WGW, r2 = rem % C::WGW;
-    const int par = BITS == 2 ? r2 / WDIG : 0, k = r2 % WDIG;
+    const int par = C::SPLIT2 ? r2 / WDIG : 0, k = r2 % WDIG;
     const uint4* src = (const uint4*)(wq + gg * C::TW + gi * C::GS + par * 8);
     const uint4 s0 = src[0], s1 = src[1];
     const uint32_t wv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -468,8 +496,16 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          if constexpr (BITS == 2) {
-            const uint32_t E = rw[e][w] & 0x33333333u, Od = (rw[e][w] >> 2) & 0x33333333u;
+          if constexpr (C::SPLIT2) {
+            uint32_t E = rw[e][w] & 0x33333333u, Od = (rw[e][w] >> 2) & 0x33333333u;
+            if constexpr (BITS == 3) {
+              // high bits of positions 16 w + 2 n (+ 1) of the sub-chunk:
+              // word w / 2 of its half row, shifts 2 (w & 1) and 2 (w & 1) + 1
+              const uint32_t hw = (w >> 1) ? b.vh[e].y : b.vh[e].x;
+              const int k0 = (w & 1) << 1;
+              E |= ((hw >> k0) & 0x11111111u) << 2;
+              Od |= ((hw >> (k0 + 1)) & 0x11111111u) << 2;
+            }
 #pragma unroll
             for (int k = 0; k < WDIG; ++k) {
               pa[gg][e][k] = __builtin_amdgcn_udot8(E, W[k], pa[gg][e][k], false);
@@ -611,14 +647,14 @@ __device__ void step_append(const DecodeArgs& a, int64_t unit, const QMap& qm, i
   QLds& ql = *(QLds*)(sm + C::O_UNION);
   const uint16_t* knew = (const uint16_t*)(sm + C::O_UNION + C::O_NEW);
   const uint16_t* vnew = knew + D;
-  VRow vr;
-  vr.blk = -1;
+  VRows vr;
+  vrows_init(vr);
   __syncthreads();  // window scores in the union are dead
   const int e1 = sq1 < L0 ? sq1 : L0;
   for (int p = sq; p < e1; ++p) {
     const int64_t row = (unit * g.W + (p - g.S) % g.W) * D + i;
     const float x = bf16_bits_to_f32(is_v ? a.pl.vring[row] : a.pl.kring[row]);
-    store_quantized(p, x, x, ql, vr, a.pl, qm, g);
+    store_quantized<BITS == 3>(p, x, x, ql, vr, a.pl, qm, g);
   }
   __syncthreads();  // ring reads above complete before the ring write below
   const uint16_t nb = is_v ? vnew[i] : knew[i];
@@ -630,9 +666,9 @@ __device__ void step_append(const DecodeArgs& a, int64_t unit, const QMap& qm, i
     (is_v ? a.pl.vring : a.pl.kring)[o] = nb;
   } else {
     const float x = bf16_bits_to_f32(nb);
-    store_quantized(L0, x, x, ql, vr, a.pl, qm, g);
+    store_quantized<BITS == 3>(L0, x, x, ql, vr, a.pl, qm, g);
   }
-  vrow_flush(vr, a.pl, qm, g);
+  vrows_flush<BITS == 3>(vr, a.pl);
 }
 
 // ---------------------------------------------------------------- window
@@ -1034,9 +1070,11 @@ hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t 
   hipError_t e;
   if (ev_start && (e = hipEventRecord(ev_start, st)) != hipSuccess) return e;
   if (io_bf16)
-    e = a.g.bits == 2 ? launch_split_g<1, 2>(a, st) : launch_split_g<1, 4>(a, st);
+    e = a.g.bits == 2 ? launch_split_g<1, 2>(a, st)
+      : a.g.bits == 3 ? launch_split_g<1, 3>(a, st) : launch_split_g<1, 4>(a, st);
   else
-    e = a.g.bits == 2 ? launch_split_g<0, 2>(a, st) : launch_split_g<0, 4>(a, st);
+    e = a.g.bits == 2 ? launch_split_g<0, 2>(a, st)
+      : a.g.bits == 3 ? launch_split_g<0, 3>(a, st) : launch_split_g<0, 4>(a, st);
   if (e != hipSuccess) return e;
   if (ev_stop && (e = hipEventRecord(ev_stop, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.g.n_q, a.n_seq), dim3(256), 0, st, a);

@@ -54,7 +54,9 @@ struct __align__(16) PLds {
   uint16_t v[PT * RS];    // values (bf16)
   uint16_t kq[PT * RS];   // transformed keys (bf16)
   uint16_t fix[FIXMAX];   // entries to recompute: row << 7 | dimension
-  uint32_t vrow[2 * D * 4];  // value-code rows of the tile (two blocks at 4 bits)
+  uint32_t vrow[2 * D * 4];  // value-code rows of the tile: two blocks at 4 bits; at 3 bits
+                             // the low-plane row and (words 0..1) the tile's half of the
+                             // high-plane row
   int nfix;
 };
 
@@ -115,7 +117,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
   const int sq1 = squant_of(L1, g.S, g.R, g.F);
   const int qlo = max(L0, g.S), qhi = min(L1, sq1);  // new positions that are quantized
   constexpr int LEV = (1 << BITS) - 1;
-  constexpr int VB = 128 / BITS;                     // positions per value-code block
+  // positions per value-code row of 16 bytes per dimension (the low plane's
+  // at 3 bits)
+  constexpr int VB = BITS == 3 ? 64 : 128 / BITS;
 
   // percentile interpolation points (fp64 exactly as in quant.h)
   const double hlo = g.p_lo * (double)(D - 1), hhi = g.p_hi * (double)(D - 1);
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
       // rounded down, non-strict (odd c) against it rounded up
       float bnd[LEV];
       float inv = 0.f, zf = (float)zd;
-      if (BITS == 2) {
+      if (BITS <= 3) {
 #pragma unroll
         for (int c = 0; c < LEV; ++c) {
           const double tb = zd + ((double)c + 0.5) * sd;
@@ -336,7 +340,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
       } else {
         inv = sd == 0.0 ? 0.f : (float)(1.0 / sd);
       }
-      uint32_t packed[BITS * 2];  // codes of this lane's 64 dimensions
+      // codes of this lane's 64 dimensions; at 3 bits words 0..3 hold the low
+      // plane and words 4..5 the high plane
+      uint32_t packed[BITS * 2];
 #pragma unroll
       for (int q = 0; q < BITS * 2; ++q) packed[q] = 0u;
 #pragma unroll
@@ -348,8 +354,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
           const int d = 8 * c + e;  // dimension 64 hh + d
           const float x = __uint_as_float((e & 1) ? (uw[e >> 1] & 0xFFFF0000u) : (uw[e >> 1] << 16));
           int code;
-          if (BITS == 2) {
-            code = (x > bnd[0] ? 1 : 0) + (x >= bnd[1] ? 1 : 0) + (x > bnd[2] ? 1 : 0);
+          if (BITS <= 3) {
+            code = 0;
+#pragma unroll
+            for (int c2 = 0; c2 < LEV; ++c2) code += (c2 & 1) ? (x >= bnd[c2] ? 1 : 0) : (x > bnd[c2] ? 1 : 0);
           } else if (sd == 0.0) {
             code = 0;
           } else {
@@ -363,21 +371,49 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
               cc += 1;
             code = cc;
           }
-          packed[(d * BITS) >> 5] |= (uint32_t)code << ((d * BITS) & 31);
+          if (BITS == 3) {
+            // selects rather than indexing keep the words in registers
+            const uint32_t lv = ((uint32_t)code & 3u) << (2 * (d & 15));
+            const int hb = hi_bit(d);
+            const uint32_t hv = ((uint32_t)code >> 2) << (hb & 31);
+            const int lw = d >> 4;
+            packed[0] |= lw == 0 ? lv : 0u;
+            packed[1] |= lw == 1 ? lv : 0u;
+            packed[2] |= lw == 2 ? lv : 0u;
+            packed[3] |= lw == 3 ? lv : 0u;
+            packed[4] |= hb < 32 ? hv : 0u;
+            packed[5] |= hb < 32 ? 0u : hv;
+          } else {
+            packed[(d * BITS) >> 5] |= (uint32_t)code << ((d * BITS) & 31);
+          }
           if (isv && quant) {
             // value row of dimension 64 hh + d, position t of the tile
             const int dim = 64 * hh + d;
-            const int blk = t / VB, pos = t % VB;
-            atomicOr(&L.vrow[(blk * D + dim) * 4 + (pos * BITS >> 5)], (uint32_t)code << ((pos * BITS) & 31));
+            if (BITS == 3) {
+              atomicOr(&L.vrow[dim * 4 + (t >> 4)], ((uint32_t)code & 3u) << (2 * (t & 15)));
+              // the tile is one half of its 128-position block: high-plane words
+              // 2 (p0 / 64 % 2) and + 1, kept in words 0..1 of the second row
+              const int hb = hi_bit(t);  // < 64: the half's bits are those of t
+              atomicOr(&L.vrow[(D + dim) * 4 + (hb >> 5)], ((uint32_t)code >> 2) << (hb & 31));
+            } else {
+              const int blk = t / VB, pos = t % VB;
+              atomicOr(&L.vrow[(blk * D + dim) * 4 + (pos * BITS >> 5)], (uint32_t)code << ((pos * BITS) & 31));
+            }
           }
         }
       }
       if (quant && trow >= 0) {
         if (!isv) {
-          uint4* kd = (uint4*)(a.pl.kcode + (trow + t) * (16 * BITS) + hh * 8 * BITS);
+          if (BITS == 3) {
+            uint8_t* kr = a.pl.kcode + (trow + t) * 48;
+            *(uint4*)(kr + 16 * hh) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+            *(uint2*)(kr + 32 + 8 * hh) = make_uint2(packed[4], packed[5]);
+          } else {
+            uint4* kd = (uint4*)(a.pl.kcode + (trow + t) * (16 * BITS) + hh * 8 * BITS);
 #pragma unroll
-          for (int q = 0; q < BITS / 2; ++q)
-            kd[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
+            for (int q = 0; q < BITS / 2; ++q)
+              kd[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
+          }
         }
         if (hh == 0) (isv ? a.pl.vsz : a.pl.ksz)[trow + t] = (uint32_t)s16 | ((uint32_t)z16 << 16);
       }
@@ -386,7 +422,55 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AppendArgs a) {
 
     // ---- value-code rows: one 16-byte row per (block, dimension); rows
     // partly outside the quantized positions of the tile keep their other bits
-    {
+    if constexpr (BITS == 3) {
+      // the tile's low-plane row (16 bytes per dimension) and its half of the
+      // block's high-plane row (8 bytes: no other tile writes them)
+      const int lo = max(p0, max(c0, qlo)), hi = min(p0 + PT, min(c1, qhi));
+      const int64_t vb = 3 * (trow >> 7);
+      const int sel = (int)((trow & 127) >> 6);
+      for (int x = tid; x < 2 * D; x += 256) {
+        const int which = x / D, dim = x % D;
+        if (lo >= hi || trow < 0) continue;
+        const uint32_t* src = &L.vrow[(which * D + dim) * 4];
+        if (which == 0) {
+          uint32_t m[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int bl = (lo - p0) * 2 - 32 * q, bh = (hi - p0) * 2 - 32 * q;
+            const int l2 = bl < 0 ? 0 : (bl > 32 ? 32 : bl), h2 = bh < 0 ? 0 : (bh > 32 ? 32 : bh);
+            m[q] = h2 <= l2 ? 0u : ((h2 - l2 >= 32 ? 0xFFFFFFFFu : ((1u << (h2 - l2)) - 1u)) << l2);
+          }
+          uint4* dst = (uint4*)(a.pl.vcode + ((vb + sel) * D + dim) * 16);
+          uint4 row = make_uint4(src[0], src[1], src[2], src[3]);
+          if ((m[0] & m[1] & m[2] & m[3]) != 0xFFFFFFFFu) {
+            const uint4 old = *dst;
+            row.x = (old.x & ~m[0]) | (row.x & m[0]);
+            row.y = (old.y & ~m[1]) | (row.y & m[1]);
+            row.z = (old.z & ~m[2]) | (row.z & m[2]);
+            row.w = (old.w & ~m[3]) | (row.w & m[3]);
+          }
+          *dst = row;
+        } else {
+          uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
+          if (lo > p0 || hi < p0 + PT) {
+            m0 = m1 = 0u;
+            for (int t = lo - p0; t < hi - p0; ++t) {
+              const int hb = hi_bit(t);
+              if (hb < 32) m0 |= 1u << hb;
+              else m1 |= 1u << (hb - 32);
+            }
+          }
+          uint2* dst = (uint2*)(a.pl.vcode + ((vb + 2) * D + dim) * 16 + 8 * sel);
+          uint2 row = make_uint2(src[0], src[1]);
+          if ((m0 & m1) != 0xFFFFFFFFu) {
+            const uint2 old = *dst;
+            row.x = (old.x & ~m0) | (row.x & m0);
+            row.y = (old.y & ~m1) | (row.y & m1);
+          }
+          *dst = row;
+        }
+      }
+    } else {
       const int nblk = PT / VB;  // 1 (2 bits) or 2 (4 bits)
       for (int x = tid; x < nblk * D; x += 256) {
         const int blk = x / D, dim = x % D;
@@ -423,6 +507,8 @@ hipError_t launch_prefill(const AppendArgs& a, int grid_x, int n_seq, hipStream_
   dim3 grid(grid_x, a.g.n_kv, n_seq);
   if (a.g.bits == 2)
     hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(256), 0, st, a);
+  else if (a.g.bits == 3)
+    hipLaunchKernelGGL(prefill_kernel<3>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(256), 0, st, a);
   return hipGetLastError();

@@ -215,45 +215,52 @@ __device__ __forceinline__ int quantize_group(float x, QLds& L, const Geometry& 
   return c;
 }
 
-// Accumulates value-code bits of one dimension row for consecutive positions
-// and writes each 16-byte row once (read-modify-write keeps other positions).
-// Named fields rather than arrays keep the row in registers.
+// Accumulates value-code bits of one 16-byte row of one dimension (row index
+// in units of D x 16 bytes of vcode) for consecutive positions and writes the
+// row once (read-modify-write keeps other positions' bits).  Named fields
+// rather than arrays keep the row in registers.
 struct VRow {
-  int blk;
+  int64_t row;              // -1: empty
   uint32_t b0, b1, b2, b3;  // code bits
   uint32_t m0, m1, m2, m3;  // which bits are set
 };
+// Rows a value code goes to: lo (2- and 4-bit codes, the low plane of 3-bit
+// codes) and hi (the high plane of 3-bit codes).
+struct VRows {
+  VRow lo, hi;
+};
 
-__device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl, const QMap& qm, const Geometry& g) {
-  if (r.blk < 0) return;
-  const int64_t row = qrow(qm, r.blk * g.vblock);
-  if (row < 0) {  // unmapped page: nothing is written
-    r.blk = -1;
-    return;
-  }
-  const int64_t vblk = row >> (g.bits == 2 ? 6 : 5);  // row / vblock
-  uint4* p = (uint4*)(pl.vcode + (vblk * D + (threadIdx.x & (D - 1))) * 16);
+__device__ __forceinline__ void vrows_init(VRows& v) { v.lo.row = v.hi.row = -1; }
+
+__device__ __forceinline__ void vrow_flush(VRow& r, const Planes& pl) {
+  if (r.row < 0) return;
+  uint4* p = (uint4*)(pl.vcode + (r.row * D + (threadIdx.x & (D - 1))) * 16);
   uint4 old = *p;
   old.x = (old.x & ~r.m0) | r.b0;
   old.y = (old.y & ~r.m1) | r.b1;
   old.z = (old.z & ~r.m2) | r.b2;
   old.w = (old.w & ~r.m3) | r.b3;
   *p = old;
-  r.blk = -1;
+  r.row = -1;
 }
 
-__device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes& pl, const QMap& qm,
-                                         const Geometry& g) {
-  const int blk = p / g.vblock;
-  if (blk != r.blk) {
-    vrow_flush(r, pl, qm, g);
-    r.blk = blk;
+template <bool B3>
+__device__ __forceinline__ void vrows_flush(VRows& v, const Planes& pl) {
+  vrow_flush(v.lo, pl);
+  if constexpr (B3) vrow_flush(v.hi, pl);
+}
+
+// Put the nb-bit field code at bit `bit` (0..127) of row `row`.
+__device__ __forceinline__ void vrow_put(VRow& r, int64_t row, int bit, uint32_t code, int nb,
+                                         const Planes& pl) {
+  if (row != r.row) {
+    vrow_flush(r, pl);
+    r.row = row;
     r.b0 = r.b1 = r.b2 = r.b3 = r.m0 = r.m1 = r.m2 = r.m3 = 0u;
   }
-  const int bit = (p % g.vblock) * g.bits;
   const int w = bit >> 5;
-  const uint32_t cv = (uint32_t)code << (bit & 31);
-  const uint32_t mv = ((1u << g.bits) - 1u) << (bit & 31);
+  const uint32_t cv = code << (bit & 31);
+  const uint32_t mv = ((1u << nb) - 1u) << (bit & 31);
   r.b0 |= w == 0 ? cv : 0u;
   r.b1 |= w == 1 ? cv : 0u;
   r.b2 |= w == 2 ? cv : 0u;
@@ -264,12 +271,30 @@ __device__ __forceinline__ void vrow_add(VRow& r, int p, int code, const Planes&
   r.m3 |= w == 3 ? mv : 0u;
 }
 
+// The value code of the position at row prow of the per-position planes.
+// B3: the cache holds 3-bit codes (a compile-time choice, so that the 2- and
+// 4-bit kernels carry no high-plane accumulator).
+template <bool B3>
+__device__ __forceinline__ void vrows_add(VRows& v, int64_t prow, int code, const Planes& pl,
+                                          const Geometry& g) {
+  if constexpr (B3) {
+    const int64_t blk = prow >> 7;
+    const int t = (int)(prow & 127);
+    vrow_put(v.lo, 3 * blk + (t >> 6), (t & 63) * 2, (uint32_t)code & 3u, 2, pl);
+    vrow_put(v.hi, 3 * blk + 2, hi_bit(t), (uint32_t)code >> 2, 1, pl);
+  } else {
+    const int sh = g.bits == 2 ? 6 : 5;  // log2(vblock)
+    vrow_put(v.lo, prow >> sh, (int)(prow & ((1 << sh) - 1)) * g.bits, (uint32_t)code, g.bits, pl);
+  }
+}
+
 // Quantize key and value entries of position p and store codes and
 // scale/zero.  128-thread workgroups: thread i holds dimension i of both (kx,
 // vx) and the two groups run one after the other.  256-thread workgroups:
 // threads 0..127 hold the key entry (kx), threads 128..255 the value entry
 // (vx) and both groups run at once.
-__device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds& L, VRow& vr, const Planes& pl,
+template <bool B3>
+__device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds& L, VRows& vr, const Planes& pl,
                                 const QMap& qm, const Geometry& g) {
   const int i = threadIdx.x & (D - 1);
   const bool two = blockDim.x == 2 * D;
@@ -287,17 +312,26 @@ __device__ __forceinline__ void store_quantized(int p, float kx, float vx, QLds&
   }
   if (!is_v) L.codes[0][i] = kc;
   __syncthreads();
-  const int words = g.code_bytes / 4;  // 8 (2-bit) or 16 (4-bit)
+  const int words = g.code_bytes / 4;  // 8 (2-bit), 12 (3-bit) or 16 (4-bit)
   const int64_t row = qrow(qm, p);     // -1: unmapped page, nothing is stored
   if (threadIdx.x < words && row >= 0) {
-    const int per = 32 / g.bits;
+    const int t = threadIdx.x;
     uint32_t w = 0;
-    for (int e = 0; e < per; ++e) w |= (uint32_t)L.codes[0][threadIdx.x * per + e] << (e * g.bits);
-    ((uint32_t*)(pl.kcode + row * g.code_bytes))[threadIdx.x] = w;
+    if (B3) {
+      if (t < 8)  // low plane: elements 16 t + e at bits 2 e
+        for (int e = 0; e < 16; ++e) w |= ((uint32_t)L.codes[0][16 * t + e] & 3u) << (2 * e);
+      else        // high plane word t - 8
+        for (int e = 32 * (t - 8); e < 32 * (t - 7); ++e)
+          w |= ((uint32_t)L.codes[0][e] >> 2) << (hi_bit(e) & 31);
+    } else {
+      const int per = 32 / g.bits;
+      for (int e = 0; e < per; ++e) w |= (uint32_t)L.codes[0][t * per + e] << (e * g.bits);
+    }
+    ((uint32_t*)(pl.kcode + row * g.code_bytes))[t] = w;
   }
   if (threadIdx.x == 0 && row >= 0) pl.ksz[row] = ksz;
   if (threadIdx.x == (two ? D : 0) && row >= 0) pl.vsz[row] = vsz;
-  if (!two || is_v) vrow_add(vr, p, vc, pl, qm, g);
+  if ((!two || is_v) && row >= 0) vrows_add<B3>(vr, row, vc, pl, g);
   __syncthreads();  // codes[] reuse
 }
 

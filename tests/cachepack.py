@@ -37,6 +37,36 @@ def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
     return out
 
 
+def hi_bit(e):
+    """Bit of element e (0..127) in the 128-bit high plane of 3-bit codes
+    (include/wushkv.h): bit 4 n + k of word j holds element
+    32 j + 16 (k >> 1) + 2 n + (k & 1)."""
+    e = np.asarray(e)
+    return 32 * (e >> 5) + 4 * ((e & 15) >> 1) + ((((e & 31) >> 4) << 1) | (e & 1))
+
+
+HI = hi_bit(np.arange(128))
+
+
+def unpack3(lo_raw: np.ndarray, hi_raw: np.ndarray) -> np.ndarray:
+    """3-bit codes of 128 elements from their low plane ([..., 32] bytes, 2-bit
+    packing) and high plane ([..., 16] bytes)."""
+    lo = unpack_bits(lo_raw, 2, 128)
+    hb = hi_raw[..., HI >> 3] >> (HI & 7) & 1
+    return lo | (hb << 2)
+
+
+def pack3(codes: np.ndarray):
+    """Inverse of unpack3: (low plane [..., 32], high plane [..., 16]) bytes."""
+    lo = pack_bits(codes & 3, 2)
+    hb = (codes >> 2) & 1
+    hi = np.zeros(codes.shape[:-1] + (16,), dtype=np.uint8)
+    for e in range(128):
+        b = int(HI[e])
+        hi[..., b >> 3] |= (hb[..., e] << (b & 7)).astype(np.uint8)
+    return lo, hi
+
+
 def f16_pair(u32: np.ndarray):
     s = (u32 & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
     z = (u32 >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
@@ -89,10 +119,19 @@ def read_unit(dc, layer: int, slot: int, head: int, L: int) -> dict:
     n = max(L, 1)
     runs = row_runs(dc, layer, slot, head, n)
     kraw = _read_rows(dc, runs, "kcode", cb).reshape(-1, cb)[:n]
-    kcodes = unpack_bits(kraw, bits, 128).astype(np.uint8)
-    vraw = _read_rows(dc, runs, "vcode", 128 * 16, VB).reshape(-1, 128, 16)
-    vc = unpack_bits(vraw, bits, VB)                     # [blocks, 128 dims, VB]
-    vcodes = vc.transpose(0, 2, 1).reshape(-1, 128)[:n].astype(np.uint8)
+    if bits == 3:
+        kcodes = unpack3(kraw[:, :32], kraw[:, 32:]).astype(np.uint8)
+        # block of 128 positions: low-plane rows for positions [0, 64) and
+        # [64, 128), then the high-plane row, each [128 dims][16 B]
+        vraw = _read_rows(dc, runs, "vcode", 3 * 128 * 16, 128).reshape(-1, 3, 128, 16)
+        lo = np.concatenate([vraw[:, 0], vraw[:, 1]], axis=-1)      # [blocks, dims, 32]
+        vc = unpack3(lo, vraw[:, 2])                                 # [blocks, dims, 128]
+        vcodes = vc.transpose(0, 2, 1).reshape(-1, 128)[:n].astype(np.uint8)
+    else:
+        kcodes = unpack_bits(kraw, bits, 128).astype(np.uint8)
+        vraw = _read_rows(dc, runs, "vcode", 128 * 16, VB).reshape(-1, 128, 16)
+        vc = unpack_bits(vraw, bits, VB)                     # [blocks, 128 dims, VB]
+        vcodes = vc.transpose(0, 2, 1).reshape(-1, 128)[:n].astype(np.uint8)
     ksz = _read_rows(dc, runs, "ksz", 4).view(np.uint32)[:n]
     vsz = _read_rows(dc, runs, "vsz", 4).view(np.uint32)[:n]
     ks, kz = f16_pair(ksz)
@@ -130,9 +169,17 @@ def write_unit(dc, layer: int, slot: int, head: int, L: int, contents: dict) -> 
     vcd = np.zeros((npos, 128), dtype=np.uint8)
     kc[:L] = contents["kcodes"][:L]
     vcd[:L] = contents["vcodes"][:L]
-    kraw = pack_bits(kc, bits)                                          # [positions, cb]
-    vblk = vcd.reshape(npos // VB, VB, 128).transpose(0, 2, 1)          # [blocks, dims, VB]
-    vraw = pack_bits(np.ascontiguousarray(vblk), bits)                  # [blocks, dims, 16]
+    vblk = np.ascontiguousarray(vcd.reshape(npos // VB, VB, 128).transpose(0, 2, 1))  # [blocks, dims, VB]
+    if bits == 3:
+        klo, khi = pack3(kc)
+        kraw = np.concatenate([klo, khi], axis=-1)                      # [positions, 48]
+        vlo, vhi = pack3(vblk)                                          # [blocks, dims, 32 / 16]
+        vraw = np.stack([vlo[..., :16], vlo[..., 16:], vhi], axis=1)    # [blocks, 3, dims, 16]
+        vrow_bytes = 3 * 2048
+    else:
+        kraw = pack_bits(kc, bits)                                      # [positions, cb]
+        vraw = pack_bits(vblk, bits)                                    # [blocks, dims, 16]
+        vrow_bytes = 2048
 
     def sz(s, z):
         out = np.zeros(npos, dtype=np.uint32)
@@ -147,7 +194,7 @@ def write_unit(dc, layer: int, slot: int, head: int, L: int, contents: dict) -> 
         if row0 is None:
             continue
         planes = (("kcode", kraw[p0:p0 + cnt], row0 * cb),
-                  ("vcode", vraw[p0 // VB:(p0 + cnt) // VB], row0 // VB * 2048),
+                  ("vcode", vraw[p0 // VB:(p0 + cnt) // VB], row0 // VB * vrow_bytes),
                   ("ksz", ksz[p0:p0 + cnt].view(np.uint8), row0 * 4),
                   ("vsz", vsz[p0:p0 + cnt].view(np.uint8), row0 * 4))
         for name, arr, off in planes:

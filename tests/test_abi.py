@@ -75,7 +75,9 @@ def test_footprint_4bit():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), wk.WUSHKV_EUNSUPPORTED),
-    (dict(bits=3), wk.WUSHKV_EUNSUPPORTED),
+    (dict(bits=5), wk.WUSHKV_EUNSUPPORTED),
+    (dict(bits=1), wk.WUSHKV_EUNSUPPORTED),
+    (dict(bits=3), wk.WUSHKV_OK),
     (dict(n_q_heads=30, n_kv_heads=8), wk.WUSHKV_EINVAL),
     (dict(n_q_heads=24, n_kv_heads=8), wk.WUSHKV_EUNSUPPORTED),
     (dict(p_lo=0.5, p_hi=0.5), wk.WUSHKV_EINVAL),
@@ -247,3 +249,33 @@ def test_block_table_binding():
     assert wk.wushkv_append(h, 0, [0], [0], P, P, P, check=False) == wk.WUSHKV_OK
     assert wk.wushkv_get_len(h, 0, 0) == (0, 4)
     wk.wushkv_cache_destroy(h)
+
+
+def test_layout_3bit():
+    """3-bit planes: 48 bytes per position and head for K and for V (the
+    scope's non-power-of-two packing), value blocks of 128 positions."""
+    lay = wk.wushkv_layout(_cfg(bits=3))
+    assert lay.code_bytes == 48 and lay.vblock == 128
+    assert lay.bytes_kcode == lay.bytes_vcode == 32 * 32 * 131072 * 48
+    assert lay.bytes_ksz == 32 * 32 * 131072 * 4
+
+
+def test_3bit_high_plane_order():
+    """The documented high-plane order: a bijection on the 128 elements, and
+    (word >> k) & 0x11111111 yields, nibble for nibble, the elements whose low
+    bits the 2-bit unpacking (w & 0x33333333, (w >> 2) & 0x33333333) of word
+    2 j + (k >> 1) yields."""
+    import numpy as np
+    from cachepack import HI, pack3, unpack3
+    assert sorted(HI.tolist()) == list(range(128))
+    for j in range(4):
+        for k in range(4):
+            w = 2 * j + (k >> 1)
+            for n in range(8):
+                lo_elem = 16 * w + 2 * n + (k & 1)     # nibble n of the 2-bit unpacking
+                assert HI[lo_elem] == 32 * j + 4 * n + k
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 8, size=(37, 128), dtype=np.uint8)
+    lo, hi = pack3(codes)
+    assert lo.shape == (37, 32) and hi.shape == (37, 16)
+    assert np.array_equal(unpack3(lo, hi), codes)

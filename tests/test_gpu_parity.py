@@ -139,7 +139,7 @@ def test_cfg0_token_by_token_small():
     _run_e2e(w, [1] * 300, lengths=[300])
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_cfg0_bits(bits):
     w = synth.WORKLOADS[0]
     _run_e2e(w, [700, 5, 300, 19], bits=bits)
@@ -214,7 +214,7 @@ def test_prefill_bf16_window_variants(S, R, F):
     _run_e2e(w, [37, 2000, 1, 700, 150, 1, 11])
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_prefill_bf16_bits(bits):
     w = _bf16_workload(3000, bits=bits)
     _run_e2e(w, [1100, 1900])
@@ -240,7 +240,8 @@ def test_other_percentiles():
 
 
 @pytest.mark.parametrize("bits,G,L", [(2, 1, 3001), (2, 4, 2048), (4, 8, 1500), (4, 2, 5),
-                                      (2, 8, 1027)])
+                                      (2, 8, 1027), (3, 1, 2111), (3, 2, 700), (3, 4, 1500),
+                                      (3, 8, 333)])
 def test_decode_on_identical_contents(bits, G, L):
     """Decode attention alone: arbitrary stored contents written into the arena
     (codes, binary16 scale/zero, bfloat16 windows) are read identically by the
@@ -344,7 +345,7 @@ def test_decode_step_from_empty(S, R, F):
     _run_steps(synth.WORKLOADS[0], [0], 60, S=S, R=R, F=F)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_step_gqa_ragged(bits):
     """bf16 io, 32 query / 8 KV heads, three sequences of different lengths
     (one starting empty) in each call."""
@@ -393,7 +394,7 @@ def test_rms_codec_fp32_path(bits):
     _run_e2e(w, [700, 1, 1, 300, 22], bits=bits, rms_alpha=oracle.quest_alpha(bits))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_rms_codec_prefill_kernel(bits):
     """bf16 inputs: the matrix-core prefill kernel with RMS clip ends, then
     token appends through the one-position path (both sum squares in the same
@@ -414,7 +415,7 @@ def test_paged_fp32_path():
     _run_e2e(synth.WORKLOADS[0], [700, 1, 1, 300, 22], page=128)
 
 
-@pytest.mark.parametrize("page,bits", [(128, 2), (256, 4), (1024, 2)])
+@pytest.mark.parametrize("page,bits", [(128, 2), (256, 4), (1024, 2), (128, 3)])
 def test_paged_prefill_kernel(page, bits):
     """The matrix-core prefill kernel writing paged planes: tiles that start
     mid-page, pages shared out across a ragged GQA batch."""
@@ -422,7 +423,7 @@ def test_paged_prefill_kernel(page, bits):
     _run_e2e(w, [700, 3, 1, 1, 600, 5], bits=bits, lengths=[1310, 2, 907], page=page)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_paged_decode_steps_batched_flush(bits):
     """Fused decode steps on a paged cache with the paper's evaluation windows
     (sink 16, recent 128, flush 16): pages mapped as the quantized region
@@ -498,3 +499,20 @@ def test_paged_pages_reused_after_reset():
         check_codes(gpu, orc, 2)
         units[h] = orc
     check_attention(out[0], reference_attention(w, T, q[0], units))
+
+
+# ------------------------------------------------------------------ 3-bit cache
+
+def test_3bit_window_variants_fp32_path():
+    """3-bit codes (two bit planes) through the rank-sort kernel with flush
+    batches: prefill, one-token appends, decode attention."""
+    w = synth.WORKLOADS[0]
+    _run_e2e(w, [513, 1, 1, 70, 1, 414], bits=3, S=16, R=128, F=16, lengths=[1000])
+
+
+def test_3bit_prefill_tiles_mid_block():
+    """bf16 prefill at 3 bits: appends that start and end inside 128-position
+    blocks, so tiles write one half of a block's high-plane row each, across
+    separate calls and workgroups."""
+    w = _bf16_workload(3100, bits=3)
+    _run_e2e(w, [37, 1050, 1, 64, 1000, 3, 945], bits=3)
