@@ -27,8 +27,9 @@ EXPORTS = (
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_append", "wushkv_decode_workspace_bytes",
     "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events",
     "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_set_block_table",
-    "wushkv_status_str",
+    "wushkv_chunk_workspace_bytes", "wushkv_chunk_step", "wushkv_status_str",
 )
+WUSHKV_MAX_CHUNK = 16
 
 
 class wushkv_config(ctypes.Structure):
@@ -96,6 +97,10 @@ def lib() -> ctypes.CDLL:
     L.wushkv_decode_attn.argtypes = [P, i32, i32, i32p, P, P, P, P, _U64, P]
     L.wushkv_decode_step.restype = ctypes.c_int
     L.wushkv_decode_step.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P, _U64, P]
+    L.wushkv_chunk_workspace_bytes.restype = _U64
+    L.wushkv_chunk_workspace_bytes.argtypes = [P, i32, i32]
+    L.wushkv_chunk_step.restype = ctypes.c_int
+    L.wushkv_chunk_step.argtypes = [P, i32, i32, i32p, i32p, P, P, P, P, P, P, P, _U64, P]
     L.wushkv_set_block_table.restype = ctypes.c_int
     L.wushkv_set_block_table.argtypes = [P, P]
     L.wushkv_set_split_events.restype = ctypes.c_int
@@ -204,6 +209,25 @@ def wushkv_decode_step(cache: int, layer: int, slots, k_ptr: int, v_ptr: int, tk
                                   vp(stream))
     if check:
         _check(st, "wushkv_decode_step")
+    return st
+
+
+def wushkv_chunk_workspace_bytes(cache: int, n_seq: int, max_new: int) -> int:
+    return int(lib().wushkv_chunk_workspace_bytes(ctypes.c_void_p(cache), int(n_seq), int(max_new)))
+
+
+def wushkv_chunk_step(cache: int, layer: int, slots, n_new, k_ptr: int, v_ptr: int, tk_ptr: int,
+                      q_ptr: int, tq_ptr: int, out_ptr: int, ws_ptr: int, ws_bytes: int,
+                      stream: int = 0, *, check: bool = True) -> int:
+    s, n = _i32_array(slots)
+    nn, n2 = _i32_array(n_new)
+    assert n == n2
+    vp = ctypes.c_void_p
+    st = lib().wushkv_chunk_step(vp(cache), int(layer), n, s, nn, vp(k_ptr), vp(v_ptr), vp(tk_ptr),
+                                 vp(q_ptr), vp(tq_ptr), vp(out_ptr), vp(ws_ptr), int(ws_bytes),
+                                 vp(stream))
+    if check:
+        _check(st, "wushkv_chunk_step")
     return st
 
 

@@ -7,8 +7,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libwushkv.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "append.hip", "decode.hip", "prefill.hip", "probe.hip")]
-HEADERS = [os.path.join(HERE, "csrc", h) for h in ("common.h", "quant.h")] + [
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "append.hip", "decode.hip", "prefill.hip", "chunk.hip", "probe.hip")]
+HEADERS = [os.path.join(HERE, "csrc", h) for h in ("common.h", "quant.h", "chunk.h")] + [
     os.path.join(ROOT, "include", "wushkv.h")]
 
 HIPCC_FLAGS = [

@@ -8,6 +8,7 @@
 
 #include "../../include/wushkv.h"
 #include "common.h"
+#include "chunk.h"
 
 using namespace wkv;
 
@@ -414,6 +415,86 @@ extern "C" wushkv_status wushkv_decode_step(wushkv_cache* c, int32_t layer, int3
                                             float* out, void* ws, uint64_t ws_bytes,
                                             void* stream) {
   return decode_common(c, layer, n_seq, slots, k, v, tk, q, tq, out, ws, ws_bytes, stream, true);
+}
+
+extern "C" uint64_t wushkv_chunk_workspace_bytes(const wushkv_cache* c, int32_t n_seq,
+                                                  int32_t max_new) {
+  if (!c || n_seq < 0 || max_new < 1 || max_new > CHUNK_MAX) return 0;
+  return chunk_ws_layout(n_seq, c->cfg.n_kv_heads, c->cfg.n_q_heads / c->cfg.n_kv_heads, max_new)
+      .total;
+}
+
+extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                           const int32_t* slots, const int32_t* n_new,
+                                           const void* k, const void* v, const float* tk,
+                                           const void* q, const float* tq, float* out, void* ws,
+                                           uint64_t ws_bytes, void* stream) {
+  if (!c || !slots || !n_new || layer < 0 || layer >= c->cfg.n_layers || n_seq < 0)
+    return WUSHKV_EINVAL;
+  if (n_seq > MAXSEQ || c->cfg.bits != 2) return WUSHKV_EUNSUPPORTED;
+  if (n_seq == 0) return WUSHKV_OK;
+  if (!k || !v || !tk || !q || !tq || !out || !ws) return WUSHKV_EINVAL;
+  const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;
+  if (((uintptr_t)k % esz) || ((uintptr_t)v % esz) || ((uintptr_t)q % esz) ||
+      ((uintptr_t)tk % 16) || ((uintptr_t)tq % 16) || ((uintptr_t)out % 16) || ((uintptr_t)ws % 256))
+    return WUSHKV_EINVAL;
+  if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
+  if (c->cfg.page_size > 0 && !c->table) return WUSHKV_EINVAL;
+  int C = 0, T = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    if (n_new[i] < 1 || n_new[i] > CHUNK_MAX) return WUSHKV_EINVAL;
+    const int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
+    if ((int64_t)L + n_new[i] > c->cfg.ctx_cap) return WUSHKV_ECAPACITY;
+    if (n_new[i] > C) C = n_new[i];
+    T += n_new[i];
+  }
+  const int G = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  const ChunkWs wl = chunk_ws_layout(n_seq, c->cfg.n_kv_heads, G, C);
+  if (ws_bytes < wl.total) return WUSHKV_EWORKSPACE;
+  ChunkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pl = planes_of(c);
+  a.g = geometry_of(c);
+  a.layer = layer;
+  a.n_seq = n_seq;
+  a.C = C;
+  a.RT = (C * G + CROWS - 1) / CROWS;
+  a.n_tok = T;
+  a.k = k;
+  a.v = v;
+  a.q = q;
+  a.tk = tk;
+  a.tq = tq;
+  a.out = out;
+  uint8_t* w = (uint8_t*)ws;
+  a.qf = (float*)(w + wl.qf);
+  a.qa = (uint4*)(w + wl.qa);
+  a.knew = (uint16_t*)(w + wl.knew);
+  a.part = (float*)(w + wl.part);
+  const int S = c->cfg.sink;
+  int max_sub = 0, win = 1, tok = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
+    const int sq = squant_of(L, S, c->cfg.recent, c->cfg.flush);
+    a.s.slot[i] = slots[i];
+    a.s.len[i] = L;
+    a.s.squant[i] = sq;
+    a.s.n_new[i] = n_new[i];
+    a.s.tok0[i] = tok;
+    tok += n_new[i];
+    const int nsub = sq > S ? (sq + CSUB - 1) / CSUB - S / CSUB : 0;
+    if (nsub > max_sub) max_sub = nsub;
+    const int e = (L < S ? L : S) + (L > sq ? L - sq : 0) + n_new[i];
+    if (e > win) win = e;
+  }
+  a.win_max = win;
+  const int cap = chunk_split_cap(n_seq * c->cfg.n_kv_heads * a.RT);
+  const int need = (max_sub + 3) / 4;
+  a.n_splits = need < cap ? need : cap;
+  hipError_t e = launch_chunk(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return WUSHKV_EDEVICE;
+  for (int i = 0; i < n_seq; ++i) c->len[(size_t)layer * c->cfg.max_batch + slots[i]] += n_new[i];
+  return WUSHKV_OK;
 }
 
 extern "C" wushkv_status wushkv_set_block_table(wushkv_cache* c, const int32_t* table) {

@@ -1,0 +1,648 @@
+// wushkv_chunk_step kernels: a chunk of up to 16 new positions per sequence
+// is appended in full precision, each new position's queries attend to the
+// cache up to and including that position, and the window is flushed
+// afterwards (WUSH-KV paper page, section 4.4 for the order; section 5.2 for
+// evaluation in 16-token chunks; section 4.1 for GQA head sharing; appendix
+// D.1 for the 1/sqrt(d) scale).
+//
+// Three launches per call:
+//   prep     one workgroup per (chunk position, KV head, sequence): the G
+//            compensated queries q' = T_K^{-T} q (prescaled by log2(e)/sqrt(d),
+//            with sigma = sum_i q'_i) as floats and as 24-bit fixed point in
+//            three balanced base-256 int8 digits laid out as MFMA operands; the
+//            new key transformed with the fp64 arithmetic of every append
+//            path and rounded to bfloat16, the new value rounded to bfloat16.
+//   attend   per (sequence, KV head, tile of 16 query rows): workgroups over
+//            the quantized region [sink, squant(L)) -- every chunk position
+//            sees all of it -- and one window workgroup over the sink, the
+//            ring and the chunk's own entries (causal inside the chunk).
+//            The quantized scan is a dense (16 rows) x (64 positions) x (128
+//            dims) contraction per sub-chunk on the int8 matrix cores
+//            (v_mfma_i32_16x16x64_i8): scores from the query digits and the
+//            2-bit codes unpacked to bytes, then o += w c from 15-bit
+//            fixed-point softmax weights (two int8 digits) and the value codes;
+//            the zero point factors out of both sums (q'.(z + s c) = z sigma +
+//            s q'.c).  The window workgroup works in fp32 on bfloat16 rows.
+//            Every wave writes its own partial (o, m, l) per row.
+//   merge    one workgroup per (chunk position, query head): log-sum-exp
+//            merge into the fp32 output; one more per (sequence, KV head)
+//            quantizes the entries leaving the recent window and stores the
+//            chunk's entries (after every read of the ring has finished).
+#include "chunk.h"
+#include "quant.h"
+
+namespace wkv {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr float kL2eSqrtD = 1.4426950408889634f / 11.313708498984761f;
+// Largest |q| (three balanced base-256 digits, each in [-128, 127]) and
+// largest softmax-weight code (two such digits).  16-bit queries left score
+// errors near 1e-3 relative on keys with large scales; 24 bits remove them.
+constexpr int Q8MAX = 8355711;
+constexpr int W8MAX = 32639;
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float h2f(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+template <int IO_BF16>
+__device__ __forceinline__ float ld_io(const void* p, int64_t i) {
+  if (IO_BF16) return bf2f(((const uint16_t*)p)[i]);
+  return ((const float*)p)[i];
+}
+
+template <int IO_BF16>
+__device__ __forceinline__ uint16_t io_bf16_bits(const void* p, int64_t i) {
+  if (IO_BF16) return ((const uint16_t*)p)[i];
+  return f32_to_bf16(((const float*)p)[i]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dppf<0xB1>(x));
+  x = fmaxf(x, dppf<0x4E>(x));
+  x = fmaxf(x, dppf<0x124>(x));
+  x = fmaxf(x, dppf<0x128>(x));
+  return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dppf<0xB1>(x);
+  x += dppf<0x4E>(x);
+  x += dppf<0x124>(x);
+  x += dppf<0x128>(x);
+  return x;
+}
+
+__device__ __forceinline__ void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16 two-bit codes (a 32-bit word) as 16 int8 MFMA operand bytes: byte e
+// holds element 4 (e % 4) + e / 4.
+__device__ __forceinline__ v4i unpack2(uint32_t d) {
+  v4i r;
+  r[0] = (int)(d & 0x03030303u);
+  r[1] = (int)((d >> 2) & 0x03030303u);
+  r[2] = (int)((d >> 4) & 0x03030303u);
+  r[3] = (int)((d >> 6) & 0x03030303u);
+  return r;
+}
+
+// Operand byte of element m (0 <= m < 16) in the order of unpack2.
+__device__ __forceinline__ int opnd_byte(int m) { return 4 * (m & 3) + (m >> 2); }
+
+// Two balanced base-256 digits of |x| <= 32639: x = 256 hi + lo.
+__device__ __forceinline__ void digits8(int x, int& lo, int& hi) {
+  lo = ((x + 128) & 255) - 128;
+  hi = (x - lo) >> 8;
+}
+
+// Three balanced base-256 digits of |x| <= 8355711: x = 65536 d2 + 256 d1 + d0.
+__device__ __forceinline__ void digits8x3(int x, int& d0, int& d1, int& d2) {
+  d0 = ((x + 128) & 255) - 128;
+  x = (x - d0) >> 8;
+  d1 = ((x + 128) & 255) - 128;
+  d2 = (x - d1) >> 8;
+}
+
+__device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- prep
+
+template <int IO_BF16>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
+  __shared__ float qv[8][D];
+  __shared__ float hs[2][8][D];
+  __shared__ float qs[8][D];
+  __shared__ float stat[8][2];
+  __shared__ float kin[D];
+  const int c = blockIdx.x, h = blockIdx.y, si = blockIdx.z, tid = threadIdx.x;
+  const Geometry& g = a.g;
+  const int G = g.G, M = a.C * G, i = tid & (D - 1), hf = tid >> 7;
+  const bool valid = c < a.s.n_new[si];
+  const int64_t tok = (int64_t)a.s.tok0[si] + c;  // row in k, v, q, out
+  const int64_t unit = (int64_t)si * g.n_kv + h;  // (sequence, KV head) of this call
+  for (int x = tid; x < G * D; x += 256)
+    qv[x / D][x % D] = valid ? ld_io<IO_BF16>(a.q, (tok * g.n_q + h * G) * D + x) : 0.f;
+  float t[64];
+  const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D + 64 * hf);
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const float4 t4 = tp[x];
+    t[4 * x] = t4.x;
+    t[4 * x + 1] = t4.y;
+    t[4 * x + 2] = t4.z;
+    t[4 * x + 3] = t4.w;
+  }
+  if (tid < D) kin[tid] = valid ? ld_io<IO_BF16>(a.k, (tok * g.n_kv + h) * D + tid) : 0.f;
+  __syncthreads();
+  for (int gg = 0; gg < G; ++gg) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) acc = fmaf(t[j], qv[gg][64 * hf + j], acc);
+    hs[hf][gg][i] = acc;
+  }
+  __syncthreads();
+  if (tid < D)
+    for (int gg = 0; gg < G; ++gg) qs[gg][i] = (hs[0][gg][i] + hs[1][gg][i]) * kL2eSqrtD;
+  __syncthreads();
+  // sigma and max |q'| per head: 32 lanes per head, four dimensions each
+  {
+    const int gg = tid >> 5, part = tid & 31;
+    float s = 0.f, mx = 0.f;
+    if (gg < G)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = qs[gg][4 * part + e];
+        s += x;
+        mx = fmaxf(mx, fabsf(x));
+      }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      s += __shfl_xor(s, o);
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (gg < G && part == 0) {
+      stat[gg][0] = s;
+      stat[gg][1] = mx;
+    }
+  }
+  __syncthreads();
+  // float rows, sigma and 1/S_q; int8 operand digits (zero for positions
+  // past the sequence's chunk and for the padding rows of the last tile)
+  const int nrows = a.RT * CROWS;
+  for (int x = tid; x < G * D; x += 256) {
+    const int gg = x / D, d = x % D;
+    const int row = c * G + gg;
+    const float maxabs = stat[gg][1];
+    const float sq = maxabs > 0.f ? (float)Q8MAX / maxabs : 1.f;
+    int qi = 0;
+    if (valid) {
+      qi = (int)rintf(qs[gg][d] * sq);
+      qi = qi > Q8MAX ? Q8MAX : (qi < -Q8MAX ? -Q8MAX : qi);
+    }
+    float* qrow = a.qf + (unit * M + row) * (D + 4);
+    qrow[d] = valid ? qs[gg][d] : 0.f;
+    if (d == 0) {
+      qrow[D] = valid ? stat[gg][0] : 0.f;
+      qrow[D + 1] = valid ? 1.f / sq : 0.f;
+      qrow[D + 2] = 0.f;
+      qrow[D + 3] = 0.f;
+    }
+    int d0, d1, d2;
+    digits8x3(qi, d0, d1, d2);
+    const int rt = row >> 4, r16 = row & 15;
+    const int ks = d >> 6, grp = (d >> 4) & 3;
+    const int lane = r16 + 16 * grp, e = opnd_byte(d & 15);
+    int8_t* base = (int8_t*)(a.qa + ((unit * a.RT + rt) * 2 + ks) * 3 * 64);
+    base[(0 * 64 + lane) * 16 + e] = (int8_t)d0;
+    base[(1 * 64 + lane) * 16 + e] = (int8_t)d1;
+    base[(2 * 64 + lane) * 16 + e] = (int8_t)d2;
+  }
+  if (c == 0)  // padding rows [C G, RT 16) of the last tile: zero digits
+    for (int x = tid; x < (nrows - M) * D; x += 256) {
+      const int row = M + x / D, d = x % D;
+      const int rt = row >> 4, r16 = row & 15;
+      const int ks = d >> 6, grp = (d >> 4) & 3;
+      const int lane = r16 + 16 * grp, e = opnd_byte(d & 15);
+      int8_t* base = (int8_t*)(a.qa + ((unit * a.RT + rt) * 2 + ks) * 3 * 64);
+      base[(0 * 64 + lane) * 16 + e] = 0;
+      base[(1 * 64 + lane) * 16 + e] = 0;
+      base[(2 * 64 + lane) * 16 + e] = 0;
+    }
+  // the chunk position's new entry: k' = T_K k in fp64, one rounding; v
+  if (valid) {
+    uint16_t* dst = a.knew + (((int64_t)si * a.C + c) * g.n_kv + h) * 2 * D;
+    if (tid < D) {
+      const float* trow = a.tk + ((int64_t)h * D + tid) * D;
+      const double acc = transform_entry([&](int j) { return trow[j]; }, [&](int j) { return kin[j]; });
+      dst[tid] = f64_to_bf16(acc);
+    } else {
+      dst[D + i] = io_bf16_bits<IO_BF16>(a.v, (tok * g.n_kv + h) * D + i);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- attend
+
+// One sub-chunk of 64 positions for one wave: key-code words (position 16 cb
+// + lane % 16, dimensions 64 ks + 16 (lane / 16) ..), scale/zero words of
+// those positions, value-code words (dimension 16 db + lane % 16, positions
+// 16 (lane / 16) ..).
+struct CBuf {
+  uint32_t kc[4][2];
+  uint32_t ksz[4], vsz[4];
+  uint32_t vc[8];
+};
+
+__device__ __forceinline__ void cload(CBuf& b, const ChunkArgs& a, const QMap& qm, int pbase) {
+  const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
+  const int64_t row = qrow_read(qm, pbase);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int64_t r = row + 16 * cb + m16;
+    const uint32_t* kw = (const uint32_t*)(a.pl.kcode + r * 32) + grp;
+    b.kc[cb][0] = kw[0];
+    b.kc[cb][1] = kw[4];
+    b.ksz[cb] = a.pl.ksz[r];
+    b.vsz[cb] = a.pl.vsz[r];
+  }
+  const uint32_t* vw = (const uint32_t*)(a.pl.vcode + ((row >> 6) * D + m16) * 16) + grp;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) b.vc[db] = vw[db * 16 * 4];
+}
+
+__global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
+  extern __shared__ uint4 smem4[];
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m16 = lane & 15, grp = lane >> 4;
+  const int nsp = a.n_splits + 1, per = a.RT * nsp, NP = 4 * a.n_splits + 1;
+  int u, rem;
+  if (a.xcd_map) {
+    const int r = blockIdx.x >> 3;
+    u = (blockIdx.x & 7) + 8 * (r / per);
+    rem = r % per;
+  } else {
+    u = blockIdx.x / per;
+    rem = blockIdx.x % per;
+  }
+  const int rt = rem / nsp, j = rem % nsp;
+  const int h = u % g.n_kv, si = u / g.n_kv;
+  const int slot = a.s.slot[si], L = a.s.len[si], sq = a.s.squant[si], nn = a.s.n_new[si];
+  const int G = g.G, M = a.C * G;
+  float* part = a.part + ((int64_t)u * a.RT + rt) * NP * CROWS * PS;
+
+  if (j < a.n_splits) {
+    // ---------------- quantized region, one wave per run of sub-chunks
+    const QMap qm = qmap_of(g, a.layer, slot, h);
+    const int lo = g.S, hi = sq;
+    const int c_first = lo / CSUB;
+    const int c_end = hi > lo ? (hi + CSUB - 1) / CSUB : c_first;
+    const int nw = 4 * a.n_splits;
+    const int c0 = c_first + 4 * j + w;
+    const v4i* qa = (const v4i*)(a.qa + ((int64_t)u * a.RT + rt) * 6 * 64);
+    v4i A[2][3];  // [d half][digit]
+#pragma unroll
+    for (int x = 0; x < 6; ++x) A[x / 3][x % 3] = qa[x * 64 + lane];
+    float sig[4], inv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * rt + 4 * grp + r;
+      const float* qr = a.qf + ((int64_t)u * M + (row < M ? row : 0)) * (D + 4);
+      sig[r] = row < M ? qr[D] : 0.f;
+      inv[r] = row < M ? qr[D + 1] : 0.f;
+    }
+    uint16_t* wl = (uint16_t*)smem4 + w * 64 * 16;  // this wave's weight operands
+    float O[8][4], Mx[4], Lp[4], Zp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Mx[r] = -INFINITY;
+      Lp[r] = Zp[r] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) O[db][r] = 0.f;
+    }
+    CBuf B0, B1;
+    if (c0 < c_end) cload(B0, a, qm, c0 * CSUB);
+    for (int c = c0; c < c_end; c += nw) {
+      const int cn = c + nw;
+      if (cn < c_end) cload(B1, a, qm, cn * CSUB);
+      const int pbase = c * CSUB;
+      // ---- scores: D layout lane, r -> row 4 grp + r, position 16 cb + m16
+      float sc[4][4], vs[4], vz[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const v4i Bk = unpack2(B0.kc[cb][ks]);
+          a0 = mfma8(A[ks][0], Bk, a0);
+          a1 = mfma8(A[ks][1], Bk, a1);
+          a2 = mfma8(A[ks][2], Bk, a2);
+        }
+        const int p = pbase + 16 * cb + m16;
+        const bool ok = p >= lo && p < hi;
+        const float ksv = h2f(B0.ksz[cb] & 0xFFFFu), kzv = h2f(B0.ksz[cb] >> 16);
+        const uint32_t vw = ok ? B0.vsz[cb] : 0u;  // masked positions: scale and zero 0
+        vs[cb] = h2f(vw & 0xFFFFu);
+        vz[cb] = h2f(vw >> 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // 256 d2 + d1 sums stay below 2^24 (exact as floats); one rounding
+          const float dot = fmaf((float)(a2[r] * 256 + a1[r]), 256.f, (float)a0[r]);
+          sc[cb][r] = ok ? fmaf(ksv, dot * inv[r], kzv * sig[r]) : -INFINITY;
+        }
+      }
+      // ---- per row: sub-chunk max, weights p = exp2(s - m), w = p s_v
+      float m[4], wmax[4], lsum[4], zsum[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = fmaxf(fmaxf(sc[0][r], sc[1][r]), fmaxf(sc[2][r], sc[3][r]));
+        m[r] = row16_max(x);
+        float wm = 0.f;
+        lsum[r] = zsum[r] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const float p = __builtin_amdgcn_exp2f(sc[cb][r] - m[r]);
+          sc[cb][r] = p * vs[cb];
+          lsum[r] += p;
+          zsum[r] = fmaf(p, vz[cb], zsum[r]);
+          wm = fmaxf(wm, sc[cb][r]);
+        }
+        wmax[r] = row16_max(wm);
+      }
+      // ---- weight codes into this wave's A operand (row, position) layout:
+      // lane 4 grp + r + 16 cb, operand byte of m16; lo digit in the low byte
+      wave_fence();  // the previous sub-chunk's operand reads are done
+      const int eb = opnd_byte(m16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float wsc = wmax[r] > 0.f ? (float)W8MAX * __builtin_amdgcn_rcpf(wmax[r]) : 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          int wq = (int)rintf(sc[cb][r] * wsc);
+          wq = wq > W8MAX ? W8MAX : wq;
+          int dl, dh;
+          digits8(wq, dl, dh);
+          wl[((4 * grp + r) + 16 * cb) * 16 + eb] = (uint16_t)((dl & 255) | ((dh & 255) << 8));
+        }
+      }
+      wave_fence();
+      v4i Wl, Wh;
+      {
+        const uint4* src = (const uint4*)(wl + lane * 16);
+        const uint4 x0 = src[0], x1 = src[1];
+        const uint32_t dw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t d0 = dw[2 * q], d1 = dw[2 * q + 1];
+          Wl[q] = (int)((d0 & 0xFFu) | ((d0 >> 8) & 0xFF00u) | ((d1 & 0xFFu) << 16) | ((d1 << 8) & 0xFF000000u));
+          Wh[q] = (int)(((d0 >> 8) & 0xFFu) | ((d0 >> 16) & 0xFF00u) | ((d1 & 0xFF00u) << 8) | (d1 & 0xFF000000u));
+        }
+      }
+      // ---- online softmax fold and o += w c (lane, r -> row 4 grp + r, dim 16 db + m16)
+      float fo[4], fn[4], back[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float Mn = fmaxf(Mx[r], m[r]);
+        fo[r] = __builtin_amdgcn_exp2f(Mx[r] - Mn);
+        fn[r] = __builtin_amdgcn_exp2f(m[r] - Mn);
+        back[r] = wmax[r] * (1.f / (float)W8MAX) * fn[r];
+        Lp[r] = fmaf(Lp[r], fo[r], lsum[r] * fn[r]);
+        Zp[r] = fmaf(Zp[r], fo[r], zsum[r] * fn[r]);
+        Mx[r] = Mn;
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const v4i Bv = unpack2(B0.vc[db]);
+        const v4i pL = mfma8(Wl, Bv, v4i{0, 0, 0, 0});
+        const v4i pH = mfma8(Wh, Bv, v4i{0, 0, 0, 0});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[db][r] = fmaf(O[db][r], fo[r], (float)(pH[r] * 256 + pL[r]) * back[r]);
+      }
+      B0 = B1;
+    }
+    // ---- this wave's partial: o (unnormalized, zero-point term added), m, l
+    float* dst = part + (int64_t)(4 * j + w) * CROWS * PS;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float Lw = row16_sum(Lp[r]);
+      const float Zw = row16_sum(Zp[r]);
+      float* pr = dst + (4 * grp + r) * PS;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) pr[16 * db + m16] = O[db][r] + Zw;
+      if (m16 == 0) {
+        pr[D] = Mx[r];
+        pr[D + 1] = Lw;
+      }
+    }
+    return;
+  }
+
+  // ---------------- window: sink, ring and the chunk's own entries (fp32)
+  float* qs = (float*)smem4;            // [CROWS][D] q' rows of this tile
+  float* sc = qs + CROWS * D;           // [CROWS][win_max] scores, then weights
+  const int64_t wunit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
+  const int ns = L < g.S ? L : g.S;                 // sink entries already cached
+  const int nr = L > sq ? L - sq : 0;               // ring entries already cached
+  const int E = ns + nr + nn;
+  for (int x = tid; x < CROWS * D; x += 256) {
+    const int row = 16 * rt + x / D;
+    const bool rv = row < M && row / G < nn;
+    qs[x] = rv ? a.qf[((int64_t)u * M + row) * (D + 4) + x % D] : 0.f;
+  }
+  __syncthreads();
+  auto pos_of = [&](int e) { return e < ns ? e : (e < ns + nr ? sq + (e - ns) : L + (e - ns - nr)); };
+  auto row_ptr = [&](int e, int which) -> const uint16_t* {
+    if (e < ns) return (which ? a.pl.vsink : a.pl.ksink) + (wunit * g.S + e) * D;
+    if (e < ns + nr) {
+      const int p = sq + (e - ns);
+      return (which ? a.pl.vring : a.pl.kring) + (wunit * g.W + (p - g.S) % g.W) * D;
+    }
+    return a.knew + (((int64_t)si * a.C + (e - ns - nr)) * g.n_kv + h) * 2 * D + which * D;
+  };
+  for (int e = tid; e < E; e += 256) {
+    const uint4* kr = (const uint4*)row_ptr(e, 0);
+    float acc[CROWS];
+#pragma unroll
+    for (int r = 0; r < CROWS; ++r) acc[r] = 0.f;
+    for (int x = 0; x < 16; ++x) {
+      const uint4 k4 = kr[x];
+      const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const float kv = __uint_as_float((y & 1) ? (kw[y >> 1] & 0xFFFF0000u) : (kw[y >> 1] << 16));
+#pragma unroll
+        for (int r = 0; r < CROWS; ++r) acc[r] = fmaf(qs[r * D + 8 * x + y], kv, acc[r]);
+      }
+    }
+    const int p = pos_of(e);
+#pragma unroll
+    for (int r = 0; r < CROWS; ++r) {
+      const int row = 16 * rt + r;
+      const bool vis = row < M && row / G < nn && p <= L + row / G;
+      sc[r * a.win_max + e] = vis ? acc[r] : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // per row: max, weights, sum (16 threads per row)
+  float* rstat = sc + CROWS * a.win_max;  // [CROWS][2]: m, l
+  {
+    const int r = tid >> 4, part16 = tid & 15;
+    float mx = -INFINITY;
+    for (int e = part16; e < E; e += 16) mx = fmaxf(mx, sc[r * a.win_max + e]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float ls = 0.f;
+    for (int e = part16; e < E; e += 16) {
+      const float s = sc[r * a.win_max + e];
+      const float p = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mx);
+      sc[r * a.win_max + e] = p;
+      ls += p;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ls += __shfl_xor(ls, o);
+    if (part16 == 0) {
+      rstat[2 * r] = mx;
+      rstat[2 * r + 1] = ls;
+    }
+  }
+  __syncthreads();
+  // o[row][dim] = sum_e p v: thread = dimension, rows 8 hf .. 8 hf + 8
+  {
+    const int dim = tid & (D - 1), hf = tid >> 7;
+    float acc[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+    for (int e = 0; e < E; ++e) {
+      const float vv = bf2f(row_ptr(e, 1)[dim]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = fmaf(sc[(8 * hf + r) * a.win_max + e], vv, acc[r]);
+    }
+    float* dst = part + (int64_t)(NP - 1) * CROWS * PS;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float* pr = dst + (8 * hf + r) * PS;
+      pr[dim] = acc[r];
+      if (dim == 0) {
+        pr[D] = rstat[2 * (8 * hf + r)];
+        pr[D + 1] = rstat[2 * (8 * hf + r) + 1];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- merge, flush
+
+__global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
+  __shared__ float red[4][D];
+  __shared__ float mred[256];
+  __shared__ QLds ql;
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x;
+  const int nmerge = a.n_tok * g.n_q;
+  const int NP = 4 * a.n_splits + 1;
+  if ((int)blockIdx.x < nmerge) {
+    const int tr = blockIdx.x / g.n_q, jq = blockIdx.x % g.n_q;
+    int si = 0;
+    while (si + 1 < a.n_seq && a.s.tok0[si + 1] <= tr) ++si;
+    const int c = tr - a.s.tok0[si];
+    const int h = jq / g.G, gg = jq % g.G;
+    const int row = c * g.G + gg, rt = row >> 4, r16 = row & 15;
+    const float* src = a.part + (((int64_t)si * g.n_kv + h) * a.RT + rt) * NP * CROWS * PS + r16 * PS;
+    // maximum over the partials that hold weight
+    float mx = -INFINITY;
+    for (int x = tid; x < NP; x += 256) {
+      const float* px = src + (int64_t)x * CROWS * PS;
+      if (px[D + 1] > 0.f) mx = fmaxf(mx, px[D]);
+    }
+    mred[tid] = mx;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) mred[tid] = fmaxf(mred[tid], mred[tid + s]);
+      __syncthreads();
+    }
+    mx = mred[0];
+    __syncthreads();
+    // thread = (dimension, partial residue mod 2)
+    const int dim = tid & (D - 1), hf = tid >> 7;
+    float o = 0.f, l = 0.f;
+    for (int x = hf; x < NP; x += 2) {
+      const float* px = src + (int64_t)x * CROWS * PS;
+      const float lx = px[D + 1];
+      if (lx > 0.f) {
+        const float f = __builtin_amdgcn_exp2f(px[D] - mx);
+        o = fmaf(px[dim], f, o);
+        l = fmaf(lx, f, l);
+      }
+    }
+    red[hf][dim] = o;
+    red[2 + hf][dim] = l;
+    __syncthreads();
+    if (tid < D) a.out[((int64_t)tr * g.n_q + jq) * D + tid] = (red[0][tid] + red[1][tid]) / (red[2][tid] + red[3][tid]);
+    return;
+  }
+  // flush of one (sequence, KV head): entries leaving the recent window are
+  // quantized in position order (old ones from the ring, the chunk's from the
+  // workspace), then the chunk's entries that stay in bfloat16 are stored
+  const int fb = blockIdx.x - nmerge;
+  const int si = fb / g.n_kv, h = fb % g.n_kv;
+  const int slot = a.s.slot[si], L = a.s.len[si], nn = a.s.n_new[si];
+  const int sq0 = a.s.squant[si], sq1 = squant_of(L + nn, g.S, g.R, g.F);
+  const int i = tid & (D - 1);
+  const bool is_v = tid >= D;
+  const int64_t wunit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
+  const QMap qm = qmap_of(g, a.layer, slot, h);
+  const uint16_t* knew = a.knew + ((int64_t)si * a.C * g.n_kv + h) * 2 * D;  // + c n_kv 2 D
+  auto new_bits = [&](int c) { return knew[(int64_t)c * g.n_kv * 2 * D + (is_v ? D : 0) + i]; };
+  VRows vr;
+  vrows_init(vr);
+  for (int p = sq0; p < sq1; ++p) {
+    uint16_t b;
+    if (p < L) {
+      const int64_t o = (wunit * g.W + (p - g.S) % g.W) * D + i;
+      b = is_v ? a.pl.vring[o] : a.pl.kring[o];
+    } else {
+      b = new_bits(p - L);
+    }
+    const float x = bf2f(b);
+    store_quantized<false>(p, x, x, ql, vr, a.pl, qm, g);
+  }
+  vrows_flush<false>(vr, a.pl);
+  __syncthreads();  // ring reads above complete before the ring writes below
+  for (int p = L; p < L + nn; ++p) {
+    const uint16_t b = new_bits(p - L);
+    if (p < g.S) {
+      (is_v ? a.pl.vsink : a.pl.ksink)[(wunit * g.S + p) * D + i] = b;
+    } else if (p >= sq1) {
+      (is_v ? a.pl.vring : a.pl.kring)[(wunit * g.W + (p - g.S) % g.W) * D + i] = b;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
+  dim3 pgrid(a.C, a.g.n_kv, a.n_seq);
+  if (io_bf16)
+    hipLaunchKernelGGL(chunk_prep_kernel<1>, pgrid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(chunk_prep_kernel<0>, pgrid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds_q = 4 * 64 * 16 * 2;
+  const size_t lds_w = ((size_t)CROWS * D + (size_t)CROWS * a.win_max + 2 * CROWS) * 4;
+  const size_t lds = lds_q > lds_w ? lds_q : lds_w;
+  const int tiles = a.n_seq * a.g.n_kv * a.RT;
+  if (a.n_splits > 0) {
+    int dev = 0, cus = 0, per = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, chunk_kernel, 256, lds);
+    if (e != hipSuccess) return e;
+    int fill = (cus * (per > 0 ? per : 1) - tiles) / tiles;
+    if (fill < 1) fill = 1;
+    if (a.n_splits > fill) a.n_splits = fill;
+  }
+  a.xcd_map = (a.n_seq * a.g.n_kv) % 8 == 0;
+  hipLaunchKernelGGL(chunk_kernel, dim3(tiles * (a.n_splits + 1)), dim3(256), lds, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_merge_kernel, dim3(a.n_tok * a.g.n_q + a.n_seq * a.g.n_kv), dim3(256), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+}  // namespace wkv

@@ -9,7 +9,8 @@ import numpy as np
 import torch
 
 from . import (WUSHKV_IO_BF16, WUSHKV_IO_FP32, make_config, wushkv_append, wushkv_cache_create,
-               wushkv_cache_destroy, wushkv_decode_attn, wushkv_decode_step,
+               wushkv_cache_destroy, wushkv_chunk_step, wushkv_chunk_workspace_bytes,
+               wushkv_decode_attn, wushkv_decode_step,
                wushkv_decode_workspace_bytes, wushkv_get_len, wushkv_layout, wushkv_reset_seq,
                wushkv_set_block_table)
 
@@ -157,4 +158,29 @@ class DeviceCache:
         wushkv_decode_step(self.handle, layer, slots, k.data_ptr(), v.data_ptr(), tk.data_ptr(),
                            q.data_ptr(), tq.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
                            self._stream())
+        return out
+
+    def chunk_step(self, layer: int, slots, n_new, k: torch.Tensor, v: torch.Tensor,
+                   tk: torch.Tensor, q: torch.Tensor, tq: torch.Tensor,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+        """Append n_new[i] positions per sequence and attend each new position's
+        queries causally (chunk entries in full precision, flush after);
+        k, v are [sum(n_new)][n_kv][128], q is [sum(n_new)][n_q][128]."""
+        for t in (k, v, q):
+            assert t.dtype == self.io_dtype and t.is_contiguous() and t.device == self.device
+        for t in (tk, tq):
+            assert t.dtype == torch.float32 and t.is_contiguous() and t.device == self.device
+        n_tok = int(sum(n_new))
+        if out is None:
+            out = torch.empty((n_tok, self.cfg.n_q_heads, 128), dtype=torch.float32,
+                              device=self.device)
+        need = wushkv_chunk_workspace_bytes(self.handle, len(slots), max(n_new))
+        if getattr(self, "_cws", None) is None or self._cws.numel() < need:
+            self._cws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        if self.table is not None:
+            for s, n in zip(slots, n_new):
+                self.reserve(s, self.get_len(layer, s)[0] + n)
+        wushkv_chunk_step(self.handle, layer, slots, n_new, k.data_ptr(), v.data_ptr(),
+                          tk.data_ptr(), q.data_ptr(), tq.data_ptr(), out.data_ptr(),
+                          self._cws.data_ptr(), self._cws.numel(), self._stream())
         return out

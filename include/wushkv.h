@@ -259,6 +259,46 @@ wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_s
                                  const float* tk, const void* q, const float* tq, float* out,
                                  void* ws, uint64_t ws_bytes, void* stream);
 
+/* Largest number of new positions per sequence in one wushkv_chunk_step. */
+#define WUSHKV_MAX_CHUNK 16
+
+/* Bytes of device workspace wushkv_chunk_step needs for n_seq sequences whose
+ * largest chunk has max_new positions (0 if max_new is outside 1..16). */
+uint64_t wushkv_chunk_workspace_bytes(const wushkv_cache* cache, int32_t n_seq, int32_t max_new);
+
+/*
+ * One chunked step of one layer (paper page, section 4.4: each new chunk is
+ * first appended in full precision and used for its own attention output,
+ * then the entries that left the windows are quantized; section 5.2 evaluates
+ * in 16-token chunks).  For each of n_seq sequences (distinct slots, length
+ * L >= 0, L + n_new[i] <= ctx_cap), append n_new[i] (1..WUSHKV_MAX_CHUNK)
+ * positions and, for every new position L + c, attend its queries to the
+ * positions [0, L + c] of the cache (causal inside the chunk; quantized
+ * boundary squant(L), the chunk's own entries in bfloat16).  The cache left
+ * behind is the one wushkv_append of the same positions leaves.  Sequences
+ * of length L >= 1 with n_new = 1 give the result of wushkv_decode_step.
+ *
+ *   n_new   host int32 [n_seq].
+ *   k, v    device, io_dtype [sum(n_new)][n_kv_heads][d]: the sequences'
+ *           new positions concatenated in the order of slots[] (post-RoPE
+ *           keys; values in the value-transform basis).
+ *   tk, tq  device, float32 [n_kv_heads][d][d]: T_K and T_K^{-T}.
+ *   q       device, io_dtype [sum(n_new)][n_q_heads][d]: one query per new
+ *           position and query head (post-RoPE, uncompensated).
+ *   out     device, float32 [sum(n_new)][n_q_heads][d]: attention outputs in
+ *           the value-transform basis.
+ *   ws      device workspace of ws_bytes >= wushkv_chunk_workspace_bytes(
+ *           n_seq, max n_new), 256-byte aligned; contents on entry ignored.
+ * The quantized part runs on the int8 matrix cores: the compensated queries
+ * and the softmax weights in 24- and 15-bit fixed point against exact code
+ * products.  EUNSUPPORTED unless bits == 2.  Updates the host lengths on success; a failing call changes
+ * nothing.
+ */
+wushkv_status wushkv_chunk_step(wushkv_cache* cache, int32_t layer, int32_t n_seq,
+                                const int32_t* slots, const int32_t* n_new, const void* k,
+                                const void* v, const float* tk, const void* q, const float* tq,
+                                float* out, void* ws, uint64_t ws_bytes, void* stream);
+
 /* Instrumentation, not part of the method.  When ev_start and ev_stop are
  * hipEvent_t handles (created by the caller), every later wushkv_decode_attn
  * or wushkv_decode_step call on this cache records ev_start on its stream immediately before the

@@ -279,3 +279,28 @@ def test_3bit_high_plane_order():
     lo, hi = pack3(codes)
     assert lo.shape == (37, 32) and hi.shape == (37, 16)
     assert np.array_equal(unpack3(lo, hi), codes)
+
+
+def test_chunk_step_errors():
+    """Argument checks of wushkv_chunk_step fail before any launch and leave
+    the lengths unchanged."""
+    P = 1 << 41
+    h, _ = _fake_cache()
+    need = wk.wushkv_chunk_workspace_bytes(h, 2, 16)
+    assert need > 0 and wk.wushkv_chunk_workspace_bytes(h, 2, 17) == 0
+    assert wk.wushkv_chunk_workspace_bytes(h, 2, 0) == 0
+    step = lambda slots, nn, ws=need, q=P, k=P: wk.wushkv_chunk_step(
+        h, 0, slots, nn, k, P, P, q, P, P, P, ws, check=False)
+    assert step([0, 1], [16, 16], ws=need - 1) == wk.WUSHKV_EWORKSPACE
+    assert step([0, 1], [17, 1]) == wk.WUSHKV_EINVAL          # chunk too long
+    assert step([0, 1], [0, 1]) == wk.WUSHKV_EINVAL           # empty chunk
+    assert step([1, 1], [1, 1]) == wk.WUSHKV_EINVAL           # duplicate slot
+    assert step([0], [1], q=0) == wk.WUSHKV_EINVAL            # null query
+    assert step([0], [1], k=P + 1) == wk.WUSHKV_EINVAL        # misaligned key
+    for s in range(4):
+        assert wk.wushkv_get_len(h, 0, s) == (0, 4)
+    wk.wushkv_cache_destroy(h)
+    h, _ = _fake_cache(bits=4)
+    assert wk.wushkv_chunk_step(h, 0, [0], [1], P, P, P, P, P, P, P, need, check=False) == \
+        wk.WUSHKV_EUNSUPPORTED
+    wk.wushkv_cache_destroy(h)

@@ -516,3 +516,123 @@ def test_3bit_prefill_tiles_mid_block():
     separate calls and workgroups."""
     w = _bf16_workload(3100, bits=3)
     _run_e2e(w, [37, 1050, 1, 64, 1000, 3, 945], bits=3)
+
+
+# ------------------------------------------------------------------ chunked steps
+
+def _run_chunks(w, L0s, plan, *, bits=None, S=None, R=None, F=None, page=0, check_every=1):
+    """Prefill L0s[i] positions per sequence, then one wushkv_chunk_step per
+    entry of plan (a list of per-sequence chunk sizes).  Each new position's
+    output is checked against the oracle's causal attention over the cache of
+    section 4.4 at that moment: the quantized boundary of the length before
+    the chunk (the oracle cache with recent + chunk at the chunk's end), the
+    chunk's entries in bfloat16, positions up to the query's own.  The final
+    cache is checked against the oracle cache at its length."""
+    lengths = [L0 + sum(step[i] for step in plan) for i, L0 in enumerate(L0s)]
+    dc = _cache(w, bits=bits, S=S, R=R, F=F, max_batch=len(lengths), ctx_cap=max(lengths), page=page)
+    c = dc.cfg
+    T, Tq = synth.transforms(w, 0)
+    ks, vs = zip(*[_inputs(w, 0, si, L) for si, L in enumerate(lengths)])
+    slots = list(range(len(lengths)))
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    if any(L0s):
+        kk = torch.cat([ks[i][:L0s[i]] for i in slots]).cuda().contiguous()
+        vv = torch.cat([vs[i][:L0s[i]] for i in slots]).cuda().contiguous()
+        dc.append(0, slots, list(L0s), kk, vv, tk)
+    pos = list(L0s)
+    G = w.group
+    for st, nn in enumerate(plan):
+        kk = torch.cat([ks[i][pos[i]:pos[i] + nn[i]] for i in slots]).cuda().contiguous()
+        vv = torch.cat([vs[i][pos[i]:pos[i] + nn[i]] for i in slots]).cuda().contiguous()
+        q = synth.queries(w, 0, st, sum(nn))
+        out = dc.chunk_step(0, slots, nn, kk, vv, tk, q.cuda(), tq)
+        if st % check_every == 0 or st == len(plan) - 1:
+            out = out.cpu().numpy()
+            tok = 0
+            for si in slots:
+                L, n = pos[si], nn[si]
+                KV = []
+                for h in range(w.n_kv):
+                    unit = oracle.cache_unit(ks[si][:L + n, h].double().numpy(),
+                                             vs[si][:L + n, h].double().numpy(),
+                                             T[h].astype(np.float64), S=c.sink, R=c.recent + n,
+                                             F=c.flush, bits=c.bits, p_lo=c.p_lo, p_hi=c.p_hi)
+                    KV.append(oracle.readback(unit))
+                for cc in range(n):
+                    qc = np.concatenate([oracle.compensate(T[h].astype(np.float64),
+                                                           q[tok + cc, h * G:(h + 1) * G].double().numpy())
+                                         for h in range(w.n_kv)])
+                    K = np.stack([KV[h][0][:L + cc + 1] for h in range(w.n_kv)])
+                    V = np.stack([KV[h][1][:L + cc + 1] for h in range(w.n_kv)])
+                    check_attention(out[tok + cc], oracle.attention(qc, K, V))
+                tok += n
+        pos = [p + n for p, n in zip(pos, nn)]
+    torch.cuda.synchronize()
+    _check_state(dc, w, ks, vs, T)
+    return dc
+
+
+def _gqa_workload(L, *, G, n_kv=2, io="bf16"):
+    return synth.Workload(12, "chunk", 1, n_kv * G, n_kv, 1, L, (2,), 4, 128, 1, 0.01, 0.99, io)
+
+
+def test_chunk_step_fp32_inputs():
+    """fp32 inputs, 4 query heads on 1 KV head: prefill 700, then 16-position
+    chunks and a short one (every chunk crosses quantized flushes)."""
+    _run_chunks(synth.WORKLOADS[0], [700], [[16]] * 5 + [[7], [1], [16]])
+
+
+def test_chunk_step_gqa_ragged():
+    """32 query / 8 KV heads, three sequences (one starting empty) with ragged
+    chunk sizes in each call."""
+    _run_chunks(synth.WORKLOADS[1], [1500, 0, 777], [[16, 5, 16], [3, 16, 1], [16, 16, 16], [1, 2, 9]])
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_chunk_step_groups(G):
+    """Row tiles of 16 query rows: 16 positions x G heads (one tile at G = 1,
+    eight at G = 8)."""
+    _run_chunks(_gqa_workload(3000, G=G), [2100, 1333], [[16, 16], [16, 11], [4, 16]])
+
+
+def test_chunk_step_paper_windows_from_empty():
+    """The paper's evaluation windows (sink 16, recent 128, flush 16) from
+    empty sequences in 16-position chunks: the sink fills inside a chunk, the
+    ring fills, flushes of 16 follow."""
+    _run_chunks(synth.WORKLOADS[1], [0, 0], [[16, 16]] * 14 + [[5, 16]], S=16, R=128, F=16,
+                check_every=3)
+
+
+def test_chunk_step_paged():
+    _run_chunks(synth.WORKLOADS[1], [1100, 300], [[16, 16], [16, 3], [9, 16]], page=128)
+
+
+def test_chunk_step_same_cache_as_append():
+    """The cache a chunk step leaves equals the one wushkv_append of the same
+    positions leaves, bit for bit."""
+    w = synth.WORKLOADS[1]
+    L0, steps = 600, [16, 16, 7, 16, 1, 16]
+    n = sum(steps)
+    dc = _cache(w, S=4, R=32, F=4, max_batch=2, ctx_cap=L0 + n)
+    T, Tq = synth.transforms(w, 0)
+    k, v = _inputs(w, 0, 0, L0 + n)
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    dc.append(0, [0, 1], [L0, L0], torch.cat([k[:L0], k[:L0]]).cuda(), torch.cat([v[:L0], v[:L0]]).cuda(), tk)
+    p = L0
+    for st, m in enumerate(steps):
+        kk = k[p:p + m].cuda().contiguous()
+        vv = v[p:p + m].cuda().contiguous()
+        dc.chunk_step(0, [0], [m], kk, vv, tk, synth.queries(w, 0, st, m).cuda(), tq)
+        dc.append(0, [1], [m], kk, vv, tk)
+        p += m
+    torch.cuda.synchronize()
+    L = L0 + n
+    assert dc.get_len(0, 0) == dc.get_len(0, 1)
+    for h in range(w.n_kv):
+        a = read_unit(dc, 0, 0, h, L)
+        b = read_unit(dc, 0, 1, h, L)
+        sq = a["squant"]
+        for key in ("kcodes", "vcodes", "ks16", "kz16", "vs16", "vz16"):
+            assert np.array_equal(a[key][4:sq], b[key][4:sq]), key
+        for key in ("kwin", "vwin"):
+            assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
