@@ -367,6 +367,89 @@ def prefill_rate(wid, bits, dev, reps=3):
                     "(selection and quantization), not HBM or MFMA"}
 
 
+def chunk_rate(wid, dev, chunk=16, reps=4):
+    """wushkv_chunk_step on one full-size layer of a workload: every sequence
+    at its full length appends `chunk` positions whose queries attend
+    causally.  Times the step with HIP events and compares it with `chunk`
+    one-position decode steps over the same cache."""
+    import numpy as np
+    import torch
+
+    from decode_attention_wushkv_amd import synth
+    from decode_attention_wushkv_amd.device_cache import DeviceCache
+
+    w = synth.WORKLOADS[wid]
+    targets = w.lengths()
+    B = len(targets)
+    slots = list(range(B))
+    L0 = [t - chunk * (2 * reps + 2) for t in targets]
+    dc = DeviceCache(n_layers=1, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=2, sink=w.sink,
+                     recent=w.recent, flush=w.flush, p_lo=w.p_lo, p_hi=w.p_hi, max_batch=B,
+                     ctx_cap=max(targets), io_dtype=w.torch_io, device=dev)
+    T, Tq = synth.transforms(w, 0)
+    tk, tq = torch.from_numpy(T).to(dev), torch.from_numpy(Tq).to(dev)
+    scales = synth.channel_scales(w, 0)
+    parts = [synth.keys_values(w, 0, s, 0, L0[s], device=dev, scales=scales) for s in slots]
+    dc.append(0, slots, L0, torch.cat([p[0] for p in parts]), torch.cat([p[1] for p in parts]), tk)
+    del parts
+    pos = list(L0)
+
+    def inputs(st, n):
+        ks, vs = [], []
+        for s in slots:
+            k, v = synth.keys_values(w, 0, s, pos[s], n, device=dev, scales=scales)
+            ks.append(k)
+            vs.append(v)
+        q = synth.queries(w, 0, st, B * n, device=dev)
+        return torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), q
+
+    def read_bytes(L):
+        sq = squant(L, w.sink, w.recent, w.flush)
+        win = min(w.sink, L) + max(0, L - sq) + chunk
+        return w.n_kv * ((sq - w.sink) * 72 + win * 512)
+
+    t_chunk, t_dec, nbytes, ops = [], [], 0, 0
+    for st in range(reps + 1):
+        k, v, q = inputs(st, chunk)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dc.chunk_step(0, slots, [chunk] * B, k, v, tk, q, tq)
+        b.record()
+        torch.cuda.synchronize()
+        if st:
+            t_chunk.append(a.elapsed_time(b))
+            nbytes = sum(read_bytes(p) for p in pos)
+            rt = (chunk * w.group + 15) // 16
+            ops = sum(w.n_kv * rt * ((squant(p, w.sink, w.recent, w.flush) + 63) // 64 - w.sink // 64)
+                      * 40 * 16 * 16 * 64 * 2 for p in pos)
+        pos = [p + chunk for p in pos]
+        # the same number of positions as one-position decode steps
+        steps = [inputs(100 + st * chunk + i, 1) for i in range(chunk)]
+        torch.cuda.synchronize()
+        a.record()
+        for i, (k1, v1, q1) in enumerate(steps):
+            dc.decode_step(0, slots, k1, v1, tk, q1, tq)
+        b.record()
+        torch.cuda.synchronize()
+        if st:
+            t_dec.append(a.elapsed_time(b))
+        pos = [p + chunk for p in pos]
+    ms = float(np.median(t_chunk))
+    ms_dec = float(np.median(t_dec))
+    del dc
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "chunk": chunk, "layer_ms": round(ms, 4),
+            "tokens_per_s_per_layer": round(B * chunk / (ms * 1e-3), 1),
+            "cache_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "int8_mfma_tops": round(ops / (ms * 1e-3) / 1e12, 1),
+            "decode_steps_ms": round(ms_dec, 4),
+            "speedup_vs_decode_steps": round(ms_dec / ms, 2),
+            "note": "one layer: one chunk step (prep, attention, merge + flush) vs the same "
+                    "positions as one-position decode steps; cache GB/s counts the cache "
+                    "bytes one chunk reads"}
+
+
 def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
     """Build the workload's cache through the library (prefill appends, layer
     by layer), then time K decode steps (pass A, no instrumentation) and K more
@@ -526,6 +609,8 @@ def main():
                     help="time a paged cache with pages of this many positions (0: contiguous)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the secondary measurement of the same steps on a paged cache")
+    ap.add_argument("--no-chunk", action="store_true",
+                    help="skip the chunked multi-query step measurement")
     ap.add_argument("--no-3bit", action="store_true",
                     help="skip the secondary measurement of the same steps on a 3-bit cache")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-append measurement")
@@ -687,6 +772,9 @@ def main():
         res["bf16_reference"] = ref
     if not args.no_prefill:
         res["prefill"] = prefill_rate(args.prefill_workload, bits, dev)
+    if not args.no_chunk:
+        res["chunk_step"] = [chunk_rate(wid, dev) for wid in sorted({args.workload, 1})
+                             if synth.WORKLOADS[wid].bits[0] == 2]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_seconds, max_units=400)
     print(json.dumps(res), flush=True)

@@ -486,6 +486,8 @@ extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32
     if (nsub > max_sub) max_sub = nsub;
     const int e = (L < S ? L : S) + (L > sq ? L - sq : 0) + n_new[i];
     if (e > win) win = e;
+    const int nf = squant_of(L + n_new[i], S, c->cfg.recent, c->cfg.flush) - sq;
+    if (nf > a.n_flush) a.n_flush = nf;
   }
   a.win_max = win;
   const int cap = chunk_split_cap(n_seq * c->cfg.n_kv_heads * a.RT);

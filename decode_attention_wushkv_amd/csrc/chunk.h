@@ -23,7 +23,7 @@ struct ChunkSeqs {
 struct ChunkArgs {
   Planes pl;
   Geometry g;
-  int layer, n_seq, C, RT, n_splits, xcd_map, n_tok, win_max;
+  int layer, n_seq, C, RT, n_splits, xcd_map, n_tok, win_max, n_flush;
   const void* k;
   const void* v;
   const void* q;
@@ -62,8 +62,9 @@ inline ChunkWs chunk_ws_layout(int n_seq, int n_kv, int G, int C) {
   return w;
 }
 
-// Launches the three kernels of a chunk step (query preparation, attention,
-// merge + flush); a.n_splits is the requested count, capped by occupancy.
+// Launches the four kernels of a chunk step (query preparation, attention,
+// flush, merge + stores); a.n_splits is the requested count, capped by
+// occupancy.
 hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st);
 
 }  // namespace wkv

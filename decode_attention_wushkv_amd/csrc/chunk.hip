@@ -5,7 +5,7 @@
 // evaluation in 16-token chunks; section 4.1 for GQA head sharing; appendix
 // D.1 for the 1/sqrt(d) scale).
 //
-// Three launches per call:
+// Four launches per call:
 //   prep     one workgroup per (chunk position, KV head, sequence): the G
 //            compensated queries q' = T_K^{-T} q (prescaled by log2(e)/sqrt(d),
 //            with sigma = sum_i q'_i) as floats and as 24-bit fixed point in
@@ -24,10 +24,15 @@
 //            the zero point factors out of both sums (q'.(z + s c) = z sigma +
 //            s q'.c).  The window workgroup works in fp32 on bfloat16 rows.
 //            Every wave writes its own partial (o, m, l) per row.
+//   flush    one workgroup per (position leaving the recent window, KV head,
+//            sequence): quantizes it (from the ring, or from the chunk's
+//            entries); value-code bits go into their shared 16-byte rows with
+//            word atomics, since neighbouring positions are flushed by other
+//            workgroups at the same time.
 //   merge    one workgroup per (chunk position, query head): log-sum-exp
 //            merge into the fp32 output; one more per (sequence, KV head)
-//            quantizes the entries leaving the recent window and stores the
-//            chunk's entries (after every read of the ring has finished).
+//            stores the chunk's entries that stay in bfloat16 (after every
+//            read of the ring has finished).
 #include "chunk.h"
 #include "quant.h"
 
@@ -35,6 +40,8 @@ namespace wkv {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kL2eSqrtD = 1.4426950408889634f / 11.313708498984761f;
 // Largest |q| (three balanced base-256 digits, each in [-128, 127]) and
@@ -454,27 +461,53 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
     }
     return a.knew + (((int64_t)si * a.C + (e - ns - nr)) * g.n_kv + h) * 2 * D + which * D;
   };
-  for (int e = tid; e < E; e += 256) {
-    const uint4* kr = (const uint4*)row_ptr(e, 0);
-    float acc[CROWS];
+  // scores on the matrix cores (v_mfma_f32_16x16x32_bf16): q' = hi + lo
+  // as two bfloat16 operands (16 significant bits), keys exact in bfloat16,
+  // fp32 accumulation.  Wave w takes blocks of 16 entries w, w + 4, ...
+  {
+    bf16x8 Ah[4], Al[4];  // [32-dimension step]: row lane % 16, dims 32 ks + 8 (lane / 16) ..
 #pragma unroll
-    for (int r = 0; r < CROWS; ++r) acc[r] = 0.f;
-    for (int x = 0; x < 16; ++x) {
-      const uint4 k4 = kr[x];
-      const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w};
+    for (int ks = 0; ks < 4; ++ks) {
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int y = 0; y < 8; ++y) {
-        const float kv = __uint_as_float((y & 1) ? (kw[y >> 1] & 0xFFFF0000u) : (kw[y >> 1] << 16));
+      for (int q2 = 0; q2 < 4; ++q2) {
+        uint32_t hb[2], lb[2];
 #pragma unroll
-        for (int r = 0; r < CROWS; ++r) acc[r] = fmaf(qs[r * D + 8 * x + y], kv, acc[r]);
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const float x = qs[m16 * D + 32 * ks + 8 * grp + 2 * q2 + t2];
+          const uint16_t h16 = f32_to_bf16(x);
+          hb[t2] = h16;
+          lb[t2] = f32_to_bf16(x - bf2f(h16));
+        }
+        hw[q2] = hb[0] | (hb[1] << 16);
+        lw[q2] = lb[0] | (lb[1] << 16);
       }
+      Ah[ks] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      Al[ks] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
-    const int p = pos_of(e);
+    for (int eb = w; eb * 16 < E; eb += 4) {
+      const int e = eb * 16 + m16;
+      const uint4* kr = (const uint4*)row_ptr(e < E ? e : E - 1, 0);
+      uint4 kb[4];
 #pragma unroll
-    for (int r = 0; r < CROWS; ++r) {
-      const int row = 16 * rt + r;
-      const bool vis = row < M && row / G < nn && p <= L + row / G;
-      sc[r * a.win_max + e] = vis ? acc[r] : -INFINITY;
+      for (int ks = 0; ks < 4; ++ks) kb[ks] = kr[4 * ks + grp];
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 B = __builtin_bit_cast(bf16x8, kb[ks]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah[ks], B, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al[ks], B, acc, 0, 0, 0);
+      }
+      // D: lane, r -> row 4 grp + r, entry e
+      if (e < E) {
+        const int p = pos_of(e);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rt + 4 * grp + r;
+          const bool vis = row < M && row / G < nn && p <= L + row / G;
+          sc[(4 * grp + r) * a.win_max + e] = vis ? acc[r] : -INFINITY;
+        }
+      }
     }
   }
   __syncthreads();
@@ -507,10 +540,17 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
     float acc[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[r] = 0.f;
-    for (int e = 0; e < E; ++e) {
-      const float vv = bf2f(row_ptr(e, 1)[dim]);
+    // value rows in batches of 16 entries, all loads of a batch in flight
+    for (int e0 = 0; e0 < E; e0 += 16) {
+      float vv[16];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r] = fmaf(sc[(8 * hf + r) * a.win_max + e], vv, acc[r]);
+      for (int k = 0; k < 16; ++k) vv[k] = e0 + k < E ? bf2f(row_ptr(e0 + k, 1)[dim]) : 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = e0 + k < E ? e0 + k : E - 1;  // vv is 0 past the end
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] = fmaf(sc[(8 * hf + r) * a.win_max + e], vv[k], acc[r]);
+      }
     }
     float* dst = part + (int64_t)(NP - 1) * CROWS * PS;
 #pragma unroll
@@ -530,7 +570,6 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
 __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
   __shared__ float red[4][D];
   __shared__ float mred[256];
-  __shared__ QLds ql;
   const Geometry& g = a.g;
   const int tid = threadIdx.x;
   const int nmerge = a.n_tok * g.n_q;
@@ -575,41 +614,63 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
     if (tid < D) a.out[((int64_t)tr * g.n_q + jq) * D + tid] = (red[0][tid] + red[1][tid]) / (red[2][tid] + red[3][tid]);
     return;
   }
-  // flush of one (sequence, KV head): entries leaving the recent window are
-  // quantized in position order (old ones from the ring, the chunk's from the
-  // workspace), then the chunk's entries that stay in bfloat16 are stored
+  // stores of one (sequence, KV head): the chunk's entries that stay in
+  // bfloat16 go to the sink or the ring (the flush kernel has read every
+  // ring entry it quantizes)
   const int fb = blockIdx.x - nmerge;
   const int si = fb / g.n_kv, h = fb % g.n_kv;
   const int slot = a.s.slot[si], L = a.s.len[si], nn = a.s.n_new[si];
+  const int sq1 = squant_of(L + nn, g.S, g.R, g.F);
+  const int64_t wunit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
+  const uint16_t* knew = a.knew + ((int64_t)si * a.C * g.n_kv + h) * 2 * D;
+  for (int x = tid; x < nn * 2 * D; x += 256) {
+    const int c = x / (2 * D), which = (x / D) & 1, i = x % D;
+    const int p = L + c;
+    const uint16_t b = knew[(int64_t)c * g.n_kv * 2 * D + which * D + i];
+    if (p < g.S)
+      (which ? a.pl.vsink : a.pl.ksink)[(wunit * g.S + p) * D + i] = b;
+    else if (p >= sq1)
+      (which ? a.pl.vring : a.pl.kring)[(wunit * g.W + (p - g.S) % g.W) * D + i] = b;
+  }
+}
+
+// One position p = squant(L) + blockIdx.x of [squant(L), squant(L + n)):
+// threads 0..127 quantize its key entry, 128..255 its value entry.
+__global__ __launch_bounds__(256) void chunk_flush_kernel(ChunkArgs a) {
+  __shared__ QLds ql;
+  const Geometry& g = a.g;
+  const int si = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
+  const int slot = a.s.slot[si], L = a.s.len[si], nn = a.s.n_new[si];
   const int sq0 = a.s.squant[si], sq1 = squant_of(L + nn, g.S, g.R, g.F);
+  const int p = sq0 + blockIdx.x;
+  if (p >= sq1) return;
   const int i = tid & (D - 1);
   const bool is_v = tid >= D;
   const int64_t wunit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
+  uint16_t b;
+  if (p < L) {
+    const int64_t o = (wunit * g.W + (p - g.S) % g.W) * D + i;
+    b = is_v ? a.pl.vring[o] : a.pl.kring[o];
+  } else {
+    b = a.knew[(((int64_t)si * a.C + (p - L)) * g.n_kv + h) * 2 * D + (is_v ? D : 0) + i];
+  }
+  const float x = bf2f(b);
   const QMap qm = qmap_of(g, a.layer, slot, h);
-  const uint16_t* knew = a.knew + ((int64_t)si * a.C * g.n_kv + h) * 2 * D;  // + c n_kv 2 D
-  auto new_bits = [&](int c) { return knew[(int64_t)c * g.n_kv * 2 * D + (is_v ? D : 0) + i]; };
   VRows vr;
   vrows_init(vr);
-  for (int p = sq0; p < sq1; ++p) {
-    uint16_t b;
-    if (p < L) {
-      const int64_t o = (wunit * g.W + (p - g.S) % g.W) * D + i;
-      b = is_v ? a.pl.vring[o] : a.pl.kring[o];
-    } else {
-      b = new_bits(p - L);
-    }
-    const float x = bf2f(b);
-    store_quantized<false>(p, x, x, ql, vr, a.pl, qm, g);
-  }
-  vrows_flush<false>(vr, a.pl);
-  __syncthreads();  // ring reads above complete before the ring writes below
-  for (int p = L; p < L + nn; ++p) {
-    const uint16_t b = new_bits(p - L);
-    if (p < g.S) {
-      (is_v ? a.pl.vsink : a.pl.ksink)[(wunit * g.S + p) * D + i] = b;
-    } else if (p >= sq1) {
-      (is_v ? a.pl.vring : a.pl.kring)[(wunit * g.W + (p - g.S) % g.W) * D + i] = b;
-    }
+  store_quantized<false>(p, x, x, ql, vr, a.pl, qm, g);
+  // the value code of this position, left in vr.lo: only its own bits of
+  // the dimension's row word change
+  if (is_v && vr.lo.row >= 0) {
+    uint32_t* wd = (uint32_t*)(a.pl.vcode + (vr.lo.row * D + i) * 16);
+    const uint32_t bb[4] = {vr.lo.b0, vr.lo.b1, vr.lo.b2, vr.lo.b3};
+    const uint32_t mm[4] = {vr.lo.m0, vr.lo.m1, vr.lo.m2, vr.lo.m3};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (mm[q]) {
+        atomicAnd(wd + q, ~mm[q]);
+        atomicOr(wd + q, bb[q]);
+      }
   }
 }
 
@@ -640,6 +701,10 @@ hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
   a.xcd_map = (a.n_seq * a.g.n_kv) % 8 == 0;
   hipLaunchKernelGGL(chunk_kernel, dim3(tiles * (a.n_splits + 1)), dim3(256), lds, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.n_flush > 0) {
+    hipLaunchKernelGGL(chunk_flush_kernel, dim3(a.n_flush, a.g.n_kv, a.n_seq), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(chunk_merge_kernel, dim3(a.n_tok * a.g.n_q + a.n_seq * a.g.n_kv), dim3(256), 0,
                      st, a);
   return hipGetLastError();
