@@ -322,11 +322,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) O[db][r] = 0.f;
     }
-    CBuf B0, B1;
-    if (c0 < c_end) cload(B0, a, qm, c0 * CSUB);
-    for (int c = c0; c < c_end; c += nw) {
-      const int cn = c + nw;
-      if (cn < c_end) cload(B1, a, qm, cn * CSUB);
+    const int eb = opnd_byte(m16);
+    auto process = [&](const CBuf& B0, int c) {
       const int pbase = c * CSUB;
       // ---- scores: D layout lane, r -> row 4 grp + r, position 16 cb + m16
       float sc[4][4], vs[4], vz[4];
@@ -374,7 +371,6 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
       // ---- weight codes into this wave's A operand (row, position) layout:
       // lane 4 grp + r + 16 cb, operand byte of m16; lo digit in the low byte
       wave_fence();  // the previous sub-chunk's operand reads are done
-      const int eb = opnd_byte(m16);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float wsc = wmax[r] > 0.f ? (float)W8MAX * __builtin_amdgcn_rcpf(wmax[r]) : 0.f;
@@ -382,9 +378,9 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         for (int cb = 0; cb < 4; ++cb) {
           int wq = (int)rintf(sc[cb][r] * wsc);
           wq = wq > W8MAX ? W8MAX : wq;
-          int dl, dh;
-          digits8(wq, dl, dh);
-          wl[((4 * grp + r) + 16 * cb) * 16 + eb] = (uint16_t)((dl & 255) | ((dh & 255) << 8));
+          // balanced digits lo = ((wq + 128) & 255) - 128, hi = (wq + 128) >> 8
+          // as two's-complement bytes: lo byte = wq & 255
+          wl[((4 * grp + r) + 16 * cb) * 16 + eb] = (uint16_t)(((wq + 128) & 0xFF00) | (wq & 0xFF));
         }
       }
       wave_fence();
@@ -412,15 +408,37 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         Zp[r] = fmaf(Zp[r], fo[r], zsum[r] * fn[r]);
         Mx[r] = Mn;
       }
+      // once the running maxima settle (the common case) no rescale is needed
+      const bool keep = __all(fo[0] == 1.f && fo[1] == 1.f && fo[2] == 1.f && fo[3] == 1.f);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const v4i Bv = unpack2(B0.vc[db]);
         const v4i pL = mfma8(Wl, Bv, v4i{0, 0, 0, 0});
         const v4i pH = mfma8(Wh, Bv, v4i{0, 0, 0, 0});
+        if (keep) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[db][r] = fmaf(O[db][r], fo[r], (float)(pH[r] * 256 + pL[r]) * back[r]);
+          for (int r = 0; r < 4; ++r) O[db][r] = fmaf((float)(pH[r] * 256 + pL[r]), back[r], O[db][r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[db][r] = fmaf(O[db][r], fo[r], (float)(pH[r] * 256 + pL[r]) * back[r]);
+        }
       }
-      B0 = B1;
+    };
+    // two buffers, alternating: the next sub-chunk's codes load during the
+    // current one's arithmetic
+    CBuf B0, B1;
+    int c = c0;
+    if (c < c_end) cload(B0, a, qm, c * CSUB);
+    while (c < c_end) {
+      int cn = c + nw;
+      if (cn < c_end) cload(B1, a, qm, cn * CSUB);
+      process(B0, c);
+      c = cn;
+      if (c >= c_end) break;
+      cn = c + nw;
+      if (cn < c_end) cload(B0, a, qm, cn * CSUB);
+      process(B1, c);
+      c = cn;
     }
     // ---- this wave's partial: o (unnormalized, zero-point term added), m, l
     float* dst = part + (int64_t)(4 * j + w) * CROWS * PS;
