@@ -326,11 +326,30 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
   return WUSHKV_OK;
 }
 
+// Decode steps with groups of 8 query heads on a 2-bit cache run as chunk
+// steps of one position: eight query rows per KV head fill half an int8
+// matrix-core tile, and that beats the integer-dot split kernel, whose vector
+// work grows with the group.
+static bool step_as_chunk(const wushkv_cache* c) {
+  return c->cfg.bits == 2 && c->cfg.n_q_heads == 8 * c->cfg.n_kv_heads;
+}
+
 extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t n_seq) {
   if (!c || n_seq < 0) return 0;
   uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
-  return align256(nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4);
+  uint64_t b = align256(nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4);
+  if (step_as_chunk(c)) {
+    const uint64_t cb = chunk_ws_layout(n_seq, c->cfg.n_kv_heads, 8, 1).total;
+    if (cb > b) b = cb;
+  }
+  return b;
 }
+
+extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                           const int32_t* slots, const int32_t* n_new,
+                                           const void* k, const void* v, const float* tk,
+                                           const void* q, const float* tq, float* out, void* ws,
+                                           uint64_t ws_bytes, void* stream);
 
 // Shared by decode_attn and decode_step: validation of the attention
 // arguments, then the per-sequence plan and the launch.  step = 1 adds the
@@ -354,6 +373,17 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
   if (c->cfg.page_size > 0 && !c->table) return WUSHKV_EINVAL;
   if (ws_bytes < wushkv_decode_workspace_bytes(c, n_seq)) return WUSHKV_EWORKSPACE;
+  if (step) {
+    for (int i = 0; i < n_seq; ++i)
+      if (c->len[(size_t)layer * c->cfg.max_batch + slots[i]] + 1 > c->cfg.ctx_cap)
+        return WUSHKV_ECAPACITY;
+    if (step_as_chunk(c)) {
+      int32_t ones[MAXSEQ];
+      for (int i = 0; i < n_seq; ++i) ones[i] = 1;
+      return wushkv_chunk_step(c, layer, n_seq, slots, ones, k, v, tk, q, tq, out, ws, ws_bytes,
+                               stream);
+    }
+  }
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.pl = planes_of(c);
@@ -436,7 +466,7 @@ extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32
   if (!k || !v || !tk || !q || !tq || !out || !ws) return WUSHKV_EINVAL;
   const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;
   if (((uintptr_t)k % esz) || ((uintptr_t)v % esz) || ((uintptr_t)q % esz) ||
-      ((uintptr_t)tk % 16) || ((uintptr_t)tq % 16) || ((uintptr_t)out % 16) || ((uintptr_t)ws % 256))
+      ((uintptr_t)tk % 16) || ((uintptr_t)tq % 16) || ((uintptr_t)out % 16) || ((uintptr_t)ws % 16))
     return WUSHKV_EINVAL;
   if (!slots_ok(c, n_seq, slots)) return WUSHKV_EINVAL;
   if (c->cfg.page_size > 0 && !c->table) return WUSHKV_EINVAL;
