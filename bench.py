@@ -609,6 +609,8 @@ def main():
                     help="time a paged cache with pages of this many positions (0: contiguous)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the secondary measurement of the same steps on a paged cache")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the decode-step measurement of every workload")
     ap.add_argument("--no-chunk", action="store_true",
                     help="skip the chunked multi-query step measurement")
     ap.add_argument("--no-3bit", action="store_true",
@@ -772,6 +774,21 @@ def main():
         res["bf16_reference"] = ref
     if not args.no_prefill:
         res["prefill"] = prefill_rate(args.prefill_workload, bits, dev)
+    if not args.no_workloads:
+        # every workload's full decode step (all layers, the whole batch), pass A only
+        rows = []
+        for wid, b in ((0, 2), (1, 2), (2, 2), (4, 2), (4, 4)):
+            wl = synth.WORKLOADS[wid]
+            mm = measure_decode(wl, b, 3, 1, dev, True)
+            Bw = len(wl.lengths())
+            rows.append({"workload": wl.name, "bits": b, "ms_per_step": round(mm["ms_per_step"], 4),
+                         "cache_gbs": round(mm["value"], 1),
+                         "hbm_frac": round(mm["value"] / HBM_PEAK_GBS, 4),
+                         "tokens_per_s": round(Bw / (mm["ms_per_step"] * 1e-3), 1),
+                         "layers": wl.n_layers, "batch": Bw,
+                         "attention": "int8 matrix cores (one-position chunk steps)"
+                         if b == 2 and wl.group == 8 else "split kernel (v_dot8)"})
+        res["workloads"] = rows
     if not args.no_chunk:
         res["chunk_step"] = [chunk_rate(wid, dev) for wid in sorted({args.workload, 1})
                              if synth.WORKLOADS[wid].bits[0] == 2]

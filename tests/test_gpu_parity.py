@@ -636,3 +636,36 @@ def test_chunk_step_same_cache_as_append():
             assert np.array_equal(a[key][4:sq], b[key][4:sq]), key
         for key in ("kwin", "vwin"):
             assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
+
+
+def test_decode_step_group8_two_bit():
+    """Groups of 8 query heads on a 2-bit cache: wushkv_decode_step runs as a
+    one-position chunk step (int8 matrix cores); steps from a prefill and from
+    an empty sequence, with flush batches."""
+    w = _gqa_workload(2000, G=8)
+    _run_steps(w, [1500, 0], 20, S=4, R=32, F=4, check_every=4)
+
+
+def test_chunk_step_rms_codec():
+    """The RMS codec through chunk steps: the flush kernel quantizes with the
+    Gaussian-optimal endpoint, leaving the oracle's RMS-codec cache."""
+    w = _bf16_workload(1200)
+    lengths = [1200 + 16 * 3]
+    alpha = oracle.quest_alpha(2)
+    dc = _cache(w, max_batch=1, ctx_cap=lengths[0], rms_alpha=alpha)
+    T, Tq = synth.transforms(w, 0)
+    k, v = _inputs(w, 0, 0, lengths[0])
+    tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
+    dc.append(0, [0], [1200], k[:1200].cuda().contiguous(), v[:1200].cuda().contiguous(), tk)
+    for st in range(3):
+        p = 1200 + 16 * st
+        dc.chunk_step(0, [0], [16], k[p:p + 16].cuda().contiguous(), v[p:p + 16].cuda().contiguous(),
+                      tk, synth.queries(w, 0, st, 16).cuda(), tq)
+    torch.cuda.synchronize()
+    for h in range(w.n_kv):
+        orc = oracle.cache_unit(k[:, h].double().numpy(), v[:, h].double().numpy(), T[h].astype(np.float64),
+                                S=w.sink, R=w.recent, F=w.flush, bits=2, p_lo=w.p_lo, p_hi=w.p_hi,
+                                alpha=alpha)
+        gpu = read_unit(dc, 0, 0, h, lengths[0])
+        check_windows(gpu, orc)
+        check_codes(gpu, orc, 2)
