@@ -167,16 +167,16 @@ def summarize_counters(csvs, kernel, commands, duration_us=None):
     return "\n".join(lines) + "\n"
 
 
-def summarize_trace(stats_csv, commands, top=8):
+def summarize_trace(stats_csv, commands, others=3):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     lines = ["# rocprofv3 --kernel-trace --stats summary (durations in microseconds)",
              "# command (run from /tmp with TMPDIR=/tmp; R = repository root):"]
     lines += [f"#   {c}" for c in commands]
     lines.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>9} {'max_us':>10} {'pct':>6}  kernel")
-    # this library's kernels first, then the largest others (input generation)
-    rows = [r for r in rows if "wkv::" in r["Name"]] + [r for r in rows if "wkv::" not in r["Name"]][:3]
-    for r in rows[:top]:
+    # every kernel of this library, then the largest others (input generation)
+    rows = [r for r in rows if "wkv::" in r["Name"]] + [r for r in rows if "wkv::" not in r["Name"]][:others]
+    for r in rows:
         name = r["Name"].replace("(anonymous namespace)::", "")
         name = name if len(name) < 90 else name[:87] + "..."
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
@@ -654,7 +654,7 @@ def main():
         w = synth.WORKLOADS[args.workload]
         bits = args.bits or w.bits[0]
         if args.summarize_trace:
-            out = os.path.join(PROFILES, f"decode_{args.path}_{w.name}_kernel_stats.txt")
+            out = args.out or os.path.join(PROFILES, f"decode_{args.path}_{w.name}_kernel_stats.txt")
             text = summarize_trace(args.summarize_trace, args.commands)
         else:
             L = max(w.lengths())
