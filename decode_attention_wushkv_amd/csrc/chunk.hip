@@ -276,7 +276,8 @@ __device__ __forceinline__ void cload(CBuf& b, const ChunkArgs& a, const QMap& q
 __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
   extern __shared__ uint4 smem4[];
   const Geometry& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m16 = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, m16 = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
   const int nsp = a.n_splits + 1, per = a.RT * nsp, NP = 4 * a.n_splits + 1;
   int u, rem;
   if (a.xcd_map) {
@@ -427,18 +428,17 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
     // two buffers, alternating: the next sub-chunk's codes load during the
     // current one's arithmetic
     CBuf B0, B1;
-    int c = c0;
-    if (c < c_end) cload(B0, a, qm, c * CSUB);
-    while (c < c_end) {
-      int cn = c + nw;
-      if (cn < c_end) cload(B1, a, qm, cn * CSUB);
-      process(B0, c);
-      c = cn;
-      if (c >= c_end) break;
-      cn = c + nw;
-      if (cn < c_end) cload(B0, a, qm, cn * CSUB);
-      process(B1, c);
-      c = cn;
+    const int n_my = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;  // this wave's sub-chunks
+    if (n_my > 0) cload(B0, a, qm, c0 * CSUB);
+    // next-buffer loads unconditional (past the end they re-read the current
+    // sub-chunk from L2), so that the compiler's wait counts keep them in
+    // flight while the current one is processed
+    for (int it = 0; it < n_my; it += 2) {
+      cload(B1, a, qm, (c0 + (it + 1 < n_my ? it + 1 : it) * nw) * CSUB);
+      process(B0, c0 + it * nw);
+      if (it + 1 >= n_my) break;
+      cload(B0, a, qm, (c0 + (it + 2 < n_my ? it + 2 : it + 1) * nw) * CSUB);
+      process(B1, c0 + (it + 1) * nw);
     }
     // ---- this wave's partial: o (unnormalized, zero-point term added), m, l
     float* dst = part + (int64_t)(4 * j + w) * CROWS * PS;

@@ -573,14 +573,18 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
   }
   SubBuf<BITS, G> B;
   int c = c0;  // A holds sub-chunk c0 (loaded by the caller) when c0 < c_end
+  // The next sub-chunk's loads are issued unconditionally (past the end they
+  // re-read the current one, from L2): a conditional load leaves the
+  // compiler's wait counts conservative at the join, and it would then wait
+  // for the prefetch before processing the current sub-chunk.
   while (c < c_end) {
     int cn = c + stride;
-    if (cn < c_end) load_sub<BITS, G>(B, a, qm, cn * C::TW);
+    load_sub<BITS, G>(B, a, qm, (cn < c_end ? cn : c) * C::TW);
     process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
     if (c >= c_end) break;
     cn = c + stride;
-    if (cn < c_end) load_sub<BITS, G>(A, a, qm, cn * C::TW);
+    load_sub<BITS, G>(A, a, qm, (cn < c_end ? cn : c) * C::TW);
     process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
   }
@@ -895,7 +899,7 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
     } else if constexpr (C::HS) {
       // head split: the four waves walk the same sub-chunks, wave w taking
       // query heads [w GW, w GW + GW)
-      const int w = tid >> 6;
+      const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
       int c0, cstride, cend;
       if (a.contig) {
         c0 = c_first + (int)((nsub * j) / a.n_splits);
@@ -916,7 +920,7 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
                               dst, (int64_t)nsp * PS, A);
       direct = true;
     } else {
-      const int w = tid >> 6, wi = 4 * j + w;
+      const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wi = 4 * j + w;
       int c0, cstride, cend;
       if (a.contig) {
         c0 = c_first + (int)((nsub * wi) / nw);
