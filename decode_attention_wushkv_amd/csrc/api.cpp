@@ -334,10 +334,18 @@ static bool step_as_chunk(const wushkv_cache* c) {
   return c->cfg.bits == 2 && c->cfg.n_q_heads == 8 * c->cfg.n_kv_heads;
 }
 
+// Bytes of the split partials at the start of the decode workspace; the
+// query blocks follow.
+static uint64_t split_ws_partials(const wushkv_cache* c, int32_t n_seq) {
+  const uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
+  return align256(nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4);
+}
+
 extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t n_seq) {
   if (!c || n_seq < 0) return 0;
-  uint64_t nq = (uint64_t)n_seq * c->cfg.n_q_heads;
-  uint64_t b = align256(nq * (uint64_t)(max_chunks(n_seq, c->cfg.n_kv_heads) + 1) * PS * 4);
+  uint64_t b = split_ws_partials(c, n_seq) +
+               align256((uint64_t)n_seq * c->cfg.n_kv_heads *
+                        prep_words(c->cfg.n_q_heads / c->cfg.n_kv_heads) * 4);
   if (step_as_chunk(c)) {
     const uint64_t cb = chunk_ws_layout(n_seq, c->cfg.n_kv_heads, 8, 1).total;
     if (cb > b) b = cb;
@@ -394,6 +402,7 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   a.tq = tq;
   a.out = out;
   a.wsp = (float*)ws;
+  a.prep = (uint32_t*)((char*)ws + split_ws_partials(c, n_seq));
   a.xcd_map = 1;  // used when the unit count is a multiple of 8
   a.contig = 0;
   if (step) {
@@ -403,6 +412,7 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   }
   const int sl = sub_len(c->cfg.bits);
   int max_sub = 0;
+  int64_t total_sub = 0;
   for (int i = 0; i < n_seq; ++i) {
     const int32_t L = c->len[(size_t)layer * c->cfg.max_batch + slots[i]];
     if (step ? L + 1 > c->cfg.ctx_cap : L < 1) return step ? WUSHKV_ECAPACITY : WUSHKV_EINVAL;
@@ -413,10 +423,13 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
     const int sq = a.s.squant[i];
     const int nsub = sq > c->cfg.sink ? (sq + sl - 1) / sl - c->cfg.sink / sl : 0;
     if (nsub > max_sub) max_sub = nsub;
+    total_sub += nsub;
   }
+  a.max_sub = max_sub;
+  a.total_sub = total_sub * c->cfg.n_kv_heads;
   // workgroups per (sequence, KV head): at least one sub-chunk per wave, at
-  // most what fills the GPU once (decided in the launcher), capped by the
-  // workspace bound
+  // most what the launcher's grid policy allows, capped by the workspace
+  // bound
   int cap = max_chunks(n_seq, c->cfg.n_kv_heads);
   // G <= 2: four waves per workgroup on different sub-chunks; G >= 4: the
   // waves of a workgroup share sub-chunks and split the query heads

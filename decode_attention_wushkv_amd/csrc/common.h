@@ -44,6 +44,12 @@ constexpr int QDIG = 4;
 constexpr int WDIG = 4;
 constexpr int DIGP = 8;  // query digit words per group of 8 dimensions (padded for 16-byte loads)
 
+// 32-bit words of one (sequence, KV head) query block: q' [G][D] floats,
+// scales [G][4], digit words [G][16][DIGP] (in the split kernel's LDS order),
+// then the decode step's new key and value as bfloat16 (D words).
+__host__ __device__ constexpr int prep_words(int G) { return G * (D + 4 + 16 * DIGP) + D; }
+
+
 constexpr int PS = 132;          // workspace stride of one split partial: o[128], m, l, pad
 
 // Base addresses of the cache planes (arena + layout offsets).
@@ -168,6 +174,13 @@ struct DecodeArgs {
   const float* tq;
   float* out;
   float* wsp;     // [n_seq][n_q][n_splits + 1][PS]
+  // Per (sequence, KV head) query block written by the prep kernel:
+  // prep_words(G) words (q' floats, scales, digit words, new entry).
+  uint32_t* prep;
+  // Quantized sub-chunks of the launch: most in one unit, and the total over
+  // units (the launcher's choice of query preparation and grid size).
+  int max_sub;
+  int64_t total_sub;
   // Decode step (fused one-token append): the new key and value rows
   // [n_seq][n_kv][D] in the io dtype and T_K [n_kv][D][D].  Null k_new means
   // attention only.  In a step, s.len is the length with the new position and

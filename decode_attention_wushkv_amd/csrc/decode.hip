@@ -189,10 +189,42 @@ struct SplitCfg {
 
 // ---------------------------------------------------------------- query
 
+// A thread's inputs to the query compensation: its elements of the G raw
+// queries (element tid + 256 n) and its half row of T_K^{-T}.
+template <int G>
+struct QueryIn {
+  float q[(G * D + 255) / 256];
+  float t[64];
+};
+
+// Issues the global loads of the compensation inputs.  Callers issue their
+// first code loads after this, so that waiting for these inputs does not wait
+// for the codes as well.
+template <int IO_BF16, int G>
+__device__ __forceinline__ void compensate_load(const DecodeArgs& a, int h, int si, QueryIn<G>& in) {
+  const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
+  const int64_t q0 = ((int64_t)si * a.g.n_q + h * G) * D;
+#pragma unroll
+  for (int n = 0; n < (G * D + 255) / 256; ++n) {
+    const int x = tid + 256 * n;
+    in.q[n] = x < G * D ? load_io<IO_BF16>(a.q, q0 + x) : 0.f;
+  }
+  const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D + 64 * hf);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const float4 t4 = tp[c];
+    in.t[4 * c] = t4.x;
+    in.t[4 * c + 1] = t4.y;
+    in.t[4 * c + 2] = t4.z;
+    in.t[4 * c + 3] = t4.w;
+  }
+}
+
 // q' = T_K^{-T} q for the G query heads of KV head h (all 256 threads):
 // float copy, sigma, and the digit words for the integer dot products.
 template <int IO_BF16, int BITS, int G>
-__device__ void compensate_query(const DecodeArgs& a, int h, int si, uint32_t* sm) {
+__device__ __forceinline__ void compensate_query(const DecodeArgs& a, int h, int si, uint32_t* sm,
+                                                 const QueryIn<G>& in) {
   using C = SplitCfg<BITS, G>;
   float* qf = (float*)(sm + C::O_QF);
   float* qsc = (float*)(sm + C::O_QSC);
@@ -202,20 +234,10 @@ __device__ void compensate_query(const DecodeArgs& a, int h, int si, uint32_t* s
   float* hsum = qv + G * D;                  // [2][G][D] half-row sums
   int8_t* dig = (int8_t*)(hsum + 2 * G * D); // [QDIG][G][D]
   const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
-  const int nq = a.g.n_q;
-  for (int x = tid; x < G * D; x += 256)
-    qv[x] = load_io<IO_BF16>(a.q, ((int64_t)si * nq + h * G) * D + x);
-  // this thread's half row of T_K^{-T}
-  float t[64];
-  const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D + 64 * hf);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const float4 t4 = tp[c];
-    t[4 * c] = t4.x;
-    t[4 * c + 1] = t4.y;
-    t[4 * c + 2] = t4.z;
-    t[4 * c + 3] = t4.w;
-  }
+  for (int n = 0; n < (G * D + 255) / 256; ++n)
+    if (tid + 256 * n < G * D) qv[tid + 256 * n] = in.q[n];
+  const float* t = in.t;
   __syncthreads();
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
@@ -307,40 +329,63 @@ struct SubBuf {
   uint2 vh[2];
 };
 
+// Buffer resource over `bytes` bytes from a wave-uniform address (raw
+// buffer, byte offsets, bounds-checked).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_b128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint2 buf_b64(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// Issues the loads of the sub-chunk at position pbase.  Buffer loads: the
+// sub-chunk's base addresses are wave-uniform (resources in scalar
+// registers) and every lane offset is loop-invariant, so a load needs no
+// per-sub-chunk vector address registers.
 template <int BITS, int G>
 __device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a, const QMap& qm,
                                          int pbase) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
   const int64_t row = qrow_read(qm, pbase);
-  // 3 bits: low plane in bytes [0, 32) of a position, high plane in [32, 48)
-  const uint8_t* kb = a.pl.kcode + (row + tq) * C::CB + half * (BITS == 3 ? 16 : C::CB / 2);
-  const uint32_t* kz = a.pl.ksz + row + tq;
-  const uint32_t* vz = a.pl.vsz + row + tq;
+  // key codes: C::TW positions of C::CB bytes (3 bits: low plane in bytes
+  // [0, 32) of a position, high plane in [32, 48))
+  const auto rk = wave_rsrc(a.pl.kcode + row * C::CB, C::TW * C::CB);
+  const auto rks = wave_rsrc(a.pl.ksz + row, C::TW * 4);
+  const auto rvs = wave_rsrc(a.pl.vsz + row, C::TW * 4);
+  const int ko = tq * C::CB + half * (BITS == 3 ? 16 : C::CB / 2);
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
 #pragma unroll
-    for (int q = 0; q < C::KQ; ++q) b.kc[r][q] = ((const uint4*)(kb + (int64_t)(32 * r) * C::CB))[q];
-    if constexpr (BITS == 3)
-      b.kh[r] = *(const uint2*)(a.pl.kcode + (row + tq + 32 * r) * C::CB + 32 + 8 * half);
-    b.ksz[r] = kz[32 * r];
-    b.vsz[r] = vz[32 * r];
+    for (int q = 0; q < C::KQ; ++q) b.kc[r][q] = buf_b128(rk, ko + 32 * r * C::CB + 16 * q, 0);
+    if constexpr (BITS == 3) b.kh[r] = buf_b64(rk, tq * C::CB + 32 + 8 * half + 32 * r * C::CB, 0);
+    b.ksz[r] = __builtin_amdgcn_raw_buffer_load_b32(rks, 4 * (tq + 32 * r), 0, 0);
+    b.vsz[r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, 4 * (tq + 32 * r), 0, 0);
   }
   // value rows of dimensions lane and lane + 64; at 3 bits the 128-position
   // block holds two low-plane rows (the sub-chunk's is row sel) and the
   // high-plane row (the sub-chunk's half at byte 8 sel)
-  const int sel = BITS == 3 ? (int)((row >> 6) & 1) : 0;
-  const uint8_t* vb = BITS == 3 ? a.pl.vcode + (((row >> 7) * 3 + sel) * D + lane) * 16
-                                : a.pl.vcode + ((row / C::VB) * D + lane) * 16;
-#pragma unroll
-  for (int k = 0; k < C::NBW; ++k) {
-    b.vc[k][0] = *(const uint4*)(vb + (int64_t)k * D * 16);
-    b.vc[k][1] = *(const uint4*)(vb + (int64_t)k * D * 16 + 64 * 16);
-  }
   if constexpr (BITS == 3) {
-    const uint8_t* hb = vb + (2 - sel) * D * 16 + 8 * sel;
-    b.vh[0] = *(const uint2*)hb;
-    b.vh[1] = *(const uint2*)(hb + 64 * 16);
+    const int sel = (int)((row >> 6) & 1);
+    const auto rv = wave_rsrc(a.pl.vcode + (row >> 7) * 3 * D * 16, 3 * D * 16);
+    b.vc[0][0] = buf_b128(rv, lane * 16, sel * D * 16);
+    b.vc[0][1] = buf_b128(rv, lane * 16 + 64 * 16, sel * D * 16);
+    b.vh[0] = buf_b64(rv, lane * 16 + 2 * D * 16, 8 * sel);
+    b.vh[1] = buf_b64(rv, lane * 16 + 2 * D * 16 + 64 * 16, 8 * sel);
+  } else {
+    const auto rv = wave_rsrc(a.pl.vcode + (row / C::VB) * D * 16, C::NBW * D * 16);
+#pragma unroll
+    for (int k = 0; k < C::NBW; ++k) {
+      b.vc[k][0] = buf_b128(rv, lane * 16 + k * D * 16, 0);
+      b.vc[k][1] = buf_b128(rv, lane * 16 + k * D * 16 + 64 * 16, 0);
+    }
   }
 }
 
@@ -540,10 +585,22 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
   }
 }
 
+// Issues the loads of a wave's first sub-chunk c0 into A.  The load is
+// unconditional (a wave without sub-chunks loads sub-chunk 0, inside every
+// unit): a load under a branch would leave the compiler's wait counts
+// conservative where the branch joins, and waiting for the query inputs,
+// issued before, would then wait for these codes too.
+template <int BITS, int G>
+__device__ __forceinline__ void load_first(SubBuf<BITS, G>& A, const DecodeArgs& a, const QMap& qm,
+                                           int c0, int c_end) {
+  using C = SplitCfg<BITS, G>;
+  load_sub<BITS, G>(A, a, qm, (c0 < c_end ? c0 : 0) * C::TW);
+}
+
 // One wave, G query heads (scales qsc, digit words qdw): sub-chunks c0,
 // c0 + stride, ... (< c_end) of the quantized region [lo, hi), two sub-chunks
 // of codes in flight; leaves the partial (o[D], m, l) of head gg at
-// out + gg * hstride.  A already holds sub-chunk c0.
+// out + gg * hstride.  A holds (in flight) sub-chunk c0.
 template <int BITS, int G>
 __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stride, int c_end, int lo,
                            int hi, const float* qsc, const uint32_t* qdw, uint32_t* wsm, float* out,
@@ -572,7 +629,7 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
     O[gg][0] = O[gg][1] = 0.f;
   }
   SubBuf<BITS, G> B;
-  int c = c0;  // A holds sub-chunk c0 (loaded by the caller) when c0 < c_end
+  int c = c0;
   // The next sub-chunk's loads are issued unconditionally (past the end they
   // re-read the current one, from L2): a conditional load leaves the
   // compiler's wait counts conservative at the join, and it would then wait
@@ -580,11 +637,13 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
   while (c < c_end) {
     int cn = c + stride;
     load_sub<BITS, G>(B, a, qm, (cn < c_end ? cn : c) * C::TW);
+    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for A
     process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
     if (c >= c_end) break;
     cn = c + stride;
     load_sub<BITS, G>(A, a, qm, (cn < c_end ? cn : c) * C::TW);
+    __builtin_amdgcn_sched_barrier(0);
     process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
   }
@@ -611,26 +670,51 @@ __device__ __forceinline__ uint16_t io_to_bf16(const void* base, int64_t idx) {
 }
 
 // The new position's entries as bfloat16 bits in LDS: k' = T_K k in fp64
-// (transform_entry, the arithmetic of every append path, so all store
-// identical bits) with one rounding, and v rounded to bfloat16.
+// (the arithmetic of transform_entry, shared by every append path, so all
+// store identical bits) with one rounding, and v rounded to bfloat16.  Thread
+// (i, hf) computes the two chains of row i over dimensions [64 hf, 64 hf + 64)
+// (chains 2 hf and 2 hf + 1) and their sum; row i's entry is then
+// (s0 + s1) + (s2 + s3), the same operations in the same order.  All loads
+// are issued before the first wait.
 template <int IO_BF16, int BITS, int G>
 __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
   using C = SplitCfg<BITS, G>;
   float* kin = (float*)(sm + C::O_UNION);
+  double* hs = (double*)(kin + D);  // [2][D] half sums
   uint16_t* knew = (uint16_t*)(sm + C::O_UNION + C::O_NEW);
   uint16_t* vnew = knew + D;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
   const int64_t row = ((int64_t)si * a.g.n_kv + h) * D;
+  float x;
+  uint16_t vb = 0;
   if (tid < D)
-    kin[tid] = load_io<IO_BF16>(a.k_new, row + tid);
+    x = load_io<IO_BF16>(a.k_new, row + tid);
   else
-    vnew[tid - D] = io_to_bf16<IO_BF16>(a.v_new, row + tid - D);
-  __syncthreads();
-  if (tid < D) {
-    const float* tp = a.tk + ((int64_t)h * D + tid) * D;
-    const double acc = transform_entry([&](int j) { return tp[j]; }, [&](int j) { return kin[j]; });
-    knew[tid] = f64_to_bf16(acc);
+    vb = io_to_bf16<IO_BF16>(a.v_new, row + tid - D);
+  float t[64];
+  const float4* tp = (const float4*)(a.tk + ((int64_t)h * D + i) * D + 64 * hf);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const float4 t4 = tp[c];
+    t[4 * c] = t4.x;
+    t[4 * c + 1] = t4.y;
+    t[4 * c + 2] = t4.z;
+    t[4 * c + 3] = t4.w;
   }
+  if (tid < D)
+    kin[tid] = x;
+  else
+    vnew[tid - D] = vb;
+  __syncthreads();
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int j = 0; j < D / 4; ++j) {
+    s0 = fma((double)t[j], (double)kin[64 * hf + j], s0);
+    s1 = fma((double)t[32 + j], (double)kin[64 * hf + 32 + j], s1);
+  }
+  hs[hf * D + i] = s0 + s1;
+  __syncthreads();
+  if (tid < D) knew[tid] = f64_to_bf16(hs[tid] + hs[D + tid]);
   __syncthreads();
 }
 
@@ -842,9 +926,70 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
   }
 }
 
+// ---------------------------------------------------------------- query block
+
+// A thread's share of one (sequence, KV head) query block (16-byte words).
+template <int G>
+struct PrepIn {
+  uint4 v[(prep_words(G) / 4 + 255) / 256];
+};
+
+// Issues the loads of unit u's query block.  Callers issue their first code
+// loads after this, so that waiting for the block does not wait for the codes.
+template <int G>
+__device__ __forceinline__ void prep_load(const DecodeArgs& a, int u, PrepIn<G>& in) {
+  const uint4* src = (const uint4*)(a.prep + (int64_t)u * prep_words(G));
+#pragma unroll
+  for (int n = 0; n < (prep_words(G) / 4 + 255) / 256; ++n) {
+    const int x = (int)threadIdx.x + 256 * n;
+    in.v[n] = x < prep_words(G) / 4 ? src[x] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Places the block in LDS where the query preparation leaves it: q', scales
+// and digit words from O_QF on, the new entry at O_UNION + O_NEW.
+template <int BITS, int G>
+__device__ __forceinline__ void prep_store(uint32_t* sm, const PrepIn<G>& in) {
+  using C = SplitCfg<BITS, G>;
+  constexpr int NQ4 = (prep_words(G) - D) / 4;
+#pragma unroll
+  for (int n = 0; n < (prep_words(G) / 4 + 255) / 256; ++n) {
+    const int x = (int)threadIdx.x + 256 * n;
+    if (x < NQ4)
+      ((uint4*)(sm + C::O_QF))[x] = in.v[n];
+    else if (x < prep_words(G) / 4)
+      ((uint4*)(sm + C::O_UNION + C::O_NEW))[x - NQ4] = in.v[n];
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- kernels
 
+// One workgroup per (KV head, sequence): the query preparation of the split
+// kernel done once per unit (q' = T_K^{-T} q and its digit words; in a decode
+// step also the new entry, T_K k and v in bfloat16), written to the unit's
+// query block for every split workgroup to copy.
 template <int IO_BF16, int BITS, int G>
+__global__ __launch_bounds__(256) void prep_kernel(DecodeArgs a) {
+  using C = SplitCfg<BITS, G>;
+  extern __shared__ uint4 smem4[];
+  uint32_t* sm = (uint32_t*)smem4;
+  const int h = blockIdx.x, si = blockIdx.y;
+  QueryIn<G> qin;
+  compensate_load<IO_BF16, G>(a, h, si, qin);
+  if (a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
+  compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
+  uint4* dst = (uint4*)(a.prep + (int64_t)(si * a.g.n_kv + h) * prep_words(G));
+  constexpr int NQ4 = (prep_words(G) - D) / 4;
+  for (int x = threadIdx.x; x < prep_words(G) / 4; x += 256)
+    dst[x] = x < NQ4 ? ((const uint4*)(sm + C::O_QF))[x]
+                     : ((const uint4*)(sm + C::O_UNION + C::O_NEW))[x - NQ4];
+}
+
+
+// PREP: the query block comes from the prep kernel (else every workgroup
+// prepares the query itself).
+template <int IO_BF16, int BITS, int G, bool PREP>
 __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
@@ -893,8 +1038,17 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
   bool direct = false;  // head-split workgroups write their partials themselves
   if (!empty) {
     if (j == a.n_splits) {
-      if (a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
-      compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
+      if constexpr (PREP) {
+        PrepIn<G> pin;
+        prep_load<G>(a, u, pin);
+        prep_store<BITS, G>(sm, pin);
+      } else {
+        // the query inputs and the new entry's inputs in flight together
+        QueryIn<G> qin;
+        compensate_load<IO_BF16, G>(a, h, si, qin);
+        if (a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
+        compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
+      }
       window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
     } else if constexpr (C::HS) {
       // head split: the four waves walk the same sub-chunks, wave w taking
@@ -910,9 +1064,19 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
         cend = c_end;
         cstride = a.n_splits;
       }
+      // the query inputs, then the first sub-chunk's codes, in flight together
       SubBuf<BITS, C::GW> A;
-      if (c0 < cend) load_sub<BITS, C::GW>(A, a, qm, c0 * C::TW);
-      compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
+      if constexpr (PREP) {
+        PrepIn<G> pin;
+        prep_load<G>(a, u, pin);
+        load_first<BITS, C::GW>(A, a, qm, c0, cend);
+        prep_store<BITS, G>(sm, pin);
+      } else {
+        QueryIn<G> qin;
+        compensate_load<IO_BF16, G>(a, h, si, qin);
+        load_first<BITS, C::GW>(A, a, qm, c0, cend);
+        compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
+      }
       float* dst = a.wsp + ((int64_t)(qbase + w * C::GW) * nsp + j) * PS;
       quant_wave<BITS, C::GW>(a, qm, c0, cstride, cend, lo, hi,
                               (const float*)(sm + C::O_QSC) + w * C::GW * 4,
@@ -931,10 +1095,19 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
         cend = c_end;
         cstride = nw;
       }
-      // first sub-chunk's codes in flight while the query is compensated
+      // the query inputs, then the first sub-chunk's codes, in flight together
       SubBuf<BITS, G> A;
-      if (c0 < cend) load_sub<BITS, G>(A, a, qm, c0 * C::TW);
-      compensate_query<IO_BF16, BITS, G>(a, h, si, sm);
+      if constexpr (PREP) {
+        PrepIn<G> pin;
+        prep_load<G>(a, u, pin);
+        load_first<BITS, G>(A, a, qm, c0, cend);
+        prep_store<BITS, G>(sm, pin);
+      } else {
+        QueryIn<G> qin;
+        compensate_load<IO_BF16, G>(a, h, si, qin);
+        load_first<BITS, G>(A, a, qm, c0, cend);
+        compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
+      }
       uint32_t* wbase = sm + C::O_UNION;
       float* part = (float*)(wbase + 4 * C::WAVE);  // [4 waves][G][D + 2]
       quant_wave<BITS, G>(a, qm, c0, cstride, cend, lo, hi, (const float*)(sm + C::O_QSC),
@@ -1040,20 +1213,38 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<IO_BF16, BITS, G>, 256, lds);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<IO_BF16, BITS, G, false>, 256,
+                                                       lds);
     if (e != hipSuccess) return e;
     slots = cus * (per > 0 ? per : 1);
   }
+  // Query preparation: in every workgroup for long single launches (it then
+  // hides under the streaming), else once per unit in the prep kernel, with
+  // the grid oversubscribed ~4.5x so that the dispatcher balances workgroups
+  // of unequal length (ragged batches, many units) and the window workgroup's
+  // chain stays short.
+  const int units = a.n_seq * a.g.n_kv;
+  bool prep = false;
   if (a.n_splits > 0) {
-    const int units = a.n_seq * a.g.n_kv;
     int fill = (slots - units) / units;
     if (fill < 1) fill = 1;
+    const double bytes = (double)a.total_sub * SplitCfg<BITS, G>::TW * (32.0 * BITS + 8.0);
+    prep = a.max_sub >= 16 && (bytes < 240e6 || 9 * units > slots);
+    if (prep) {
+      const int target = (9 * slots) / (2 * units) - 1;
+      if (target > fill) fill = target;
+    }
     if (a.n_splits > fill) a.n_splits = fill;
   }
-  const int units = a.n_seq * a.g.n_kv;
   a.xcd_map = a.xcd_map && units % 8 == 0;
-  hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G>), dim3((a.n_splits + 1) * units), dim3(256), lds,
-                     st, a);
+  if (prep) {
+    hipLaunchKernelGGL((prep_kernel<IO_BF16, BITS, G>), dim3(a.g.n_kv, a.n_seq), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G, true>), dim3((a.n_splits + 1) * units), dim3(256),
+                       lds, st, a);
+  } else {
+    hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G, false>), dim3((a.n_splits + 1) * units),
+                       dim3(256), lds, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -352,6 +352,15 @@ def test_decode_step_gqa_ragged(bits):
     _run_steps(synth.WORKLOADS[1], [1500, 0, 777], 5, bits=bits, check_every=2)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_decode_step_prepared_query_blocks(bits):
+    """Contexts past 2K positions with little cache traffic: the launcher
+    prepares each unit's query (and the step's new entry) once in the prep
+    kernel and oversubscribes the split grid; parity as for the in-workgroup
+    preparation."""
+    _run_steps(synth.WORKLOADS[1], [2600, 0, 2301], 3, bits=bits, check_every=1)
+
+
 def test_decode_step_same_cache_as_append():
     """The cache a decode step leaves equals the one wushkv_append (n_new = 1)
     leaves, bit for bit, over steps that quantize and steps that do not."""
