@@ -163,9 +163,10 @@ struct DecodeArgs {
   int layer;
   int n_seq;
   int n_splits;  // workgroups over the quantized region per (sequence, KV head), plus one window workgroup
-  // Block order of the 1-D grid: 0 = unit-major; 1 = XCD-affine (block b
-  // runs on XCD b % 8, so unit u takes the blocks with b % 8 == u % 8 and all
-  // of a unit's workgroups share one L2).  Requires units % 8 == 0.
+  // Block order of the 1-D grid (window workgroups first in both): 0 =
+  // unit-major; 1 = XCD-affine (block b runs on XCD b % 8, so unit u takes the
+  // blocks with b % 8 == u % 8 and all of a unit's workgroups share one L2).
+  // Requires units % 8 == 0.
   int xcd_map;
   // Sub-chunk assignment: 0 = wave k of a unit takes sub-chunks k, k + nw,
   // k + 2 nw, ... (nw waves per unit); 1 = each wave takes one contiguous run.

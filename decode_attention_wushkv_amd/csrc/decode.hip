@@ -999,14 +999,26 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
   const Geometry& g = a.g;
   const int tid = threadIdx.x;
   const int nsp = a.n_splits + 1;  // workgroups per (sequence, KV head)
+  // Block order: the window workgroups first (dispatched first, they are the
+  // oldest waves on their SIMDs and win issue arbitration, which keeps their
+  // serial chain short), then the quantized workgroups unit by unit.
   int j, u;
+  const int units = a.n_seq * a.g.n_kv;
   if (a.xcd_map) {
-    const int r = blockIdx.x >> 3;
-    u = (blockIdx.x & 7) + 8 * (r / nsp);
-    j = r % nsp;
+    const int r = blockIdx.x >> 3, ng = units >> 3;
+    if (r < ng) {
+      u = (blockIdx.x & 7) + 8 * r;
+      j = a.n_splits;
+    } else {
+      u = (blockIdx.x & 7) + 8 * ((r - ng) / a.n_splits);
+      j = (r - ng) % a.n_splits;
+    }
+  } else if ((int)blockIdx.x < units) {
+    u = blockIdx.x;
+    j = a.n_splits;
   } else {
-    u = blockIdx.x / nsp;
-    j = blockIdx.x % nsp;
+    u = (blockIdx.x - units) / a.n_splits;
+    j = (blockIdx.x - units) % a.n_splits;
   }
   const int h = u % g.n_kv, si = u / g.n_kv;
   const int slot = a.s.slot[si], Lq = a.s.len[si], sq = a.s.squant[si];
