@@ -787,7 +787,7 @@ def main():
                          "tokens_per_s": round(Bw / (mm["ms_per_step"] * 1e-3), 1),
                          "layers": wl.n_layers, "batch": Bw,
                          "attention": "int8 matrix cores (one-position chunk steps)"
-                         if b == 2 and wl.group == 8 else "split kernel (v_dot8)"})
+                         if wl.group == 8 else "split kernel (v_dot8)"})
         res["workloads"] = rows
     if not args.no_chunk:
         res["chunk_step"] = [chunk_rate(wid, dev) for wid in sorted({args.workload, 1})

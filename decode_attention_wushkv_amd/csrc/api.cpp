@@ -326,12 +326,12 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
   return WUSHKV_OK;
 }
 
-// Decode steps with groups of 8 query heads on a 2-bit cache run as chunk
-// steps of one position: eight query rows per KV head fill half an int8
-// matrix-core tile, and that beats the integer-dot split kernel, whose vector
-// work grows with the group.
+// Decode steps with groups of 8 query heads run as chunk steps of one
+// position: eight query rows per KV head fill half an int8 matrix-core tile,
+// and that beats the integer-dot split kernel, whose vector work grows with
+// the group (at 2, 3 and 4 bits alike; groups of 4 stay on the split kernel).
 static bool step_as_chunk(const wushkv_cache* c) {
-  return c->cfg.bits == 2 && c->cfg.n_q_heads == 8 * c->cfg.n_kv_heads;
+  return c->cfg.n_q_heads == 8 * c->cfg.n_kv_heads;
 }
 
 // Bytes of the split partials at the start of the decode workspace; the
@@ -474,7 +474,7 @@ extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32
                                            uint64_t ws_bytes, void* stream) {
   if (!c || !slots || !n_new || layer < 0 || layer >= c->cfg.n_layers || n_seq < 0)
     return WUSHKV_EINVAL;
-  if (n_seq > MAXSEQ || c->cfg.bits != 2) return WUSHKV_EUNSUPPORTED;
+  if (n_seq > MAXSEQ) return WUSHKV_EUNSUPPORTED;
   if (n_seq == 0) return WUSHKV_OK;
   if (!k || !v || !tk || !q || !tq || !out || !ws) return WUSHKV_EINVAL;
   const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;

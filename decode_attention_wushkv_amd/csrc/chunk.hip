@@ -19,7 +19,7 @@
 //            The quantized scan is a dense (16 rows) x (64 positions) x (128
 //            dims) contraction per sub-chunk on the int8 matrix cores
 //            (v_mfma_i32_16x16x64_i8): scores from the query digits and the
-//            2-bit codes unpacked to bytes, then o += w c from 15-bit
+//            2-, 3- or 4-bit codes unpacked to bytes, then o += w c from 15-bit
 //            fixed-point softmax weights (two int8 digits) and the value codes;
 //            the zero point factors out of both sums (q'.(z + s c) = z sigma +
 //            s q'.c).  The window workgroup works in fp32 on bfloat16 rows.
@@ -109,6 +109,33 @@ __device__ __forceinline__ v4i unpack2(uint32_t d) {
 
 // Operand byte of element m (0 <= m < 16) in the order of unpack2.
 __device__ __forceinline__ int opnd_byte(int m) { return 4 * (m & 3) + (m >> 2); }
+
+// 16 four-bit codes (two words, element j in nibble j % 8 of word j / 8) as
+// operand bytes: byte 4 q + b holds element 8 (q / 2) + 2 b + q % 2.
+__device__ __forceinline__ v4i unpack4(uint32_t d0, uint32_t d1) {
+  v4i r;
+  r[0] = (int)(d0 & 0x0F0F0F0Fu);
+  r[1] = (int)((d0 >> 4) & 0x0F0F0F0Fu);
+  r[2] = (int)(d1 & 0x0F0F0F0Fu);
+  r[3] = (int)((d1 >> 4) & 0x0F0F0F0Fu);
+  return r;
+}
+
+// Operand byte of element m in the order of unpack4.
+__device__ __forceinline__ int opnd_byte4(int m) { return 4 * (2 * (m >> 3) + (m & 1)) + ((m & 7) >> 1); }
+
+// 16 three-bit codes: the low two bits as unpack2 orders them, the high bits
+// from a high-plane word in which element i sits at bit
+// 4 (i / 2) + sh + i % 2 (sh = 0 or 2, the plane's order of a 16-element group).
+__device__ __forceinline__ v4i unpack3(uint32_t lo, uint32_t hw, int sh) {
+  v4i r = unpack2(lo);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] |= (int)(((hw >> (4 * (q >> 1) + sh + (q & 1))) & 0x01010101u) << 2);
+  return r;
+}
+
+template <int BITS>
+__device__ __forceinline__ int opnd_byte_b(int m) { return BITS == 4 ? opnd_byte4(m) : opnd_byte(m); }
 
 // Two balanced base-256 digits of |x| <= 32639: x = 256 hi + lo.
 __device__ __forceinline__ void digits8(int x, int& lo, int& hi) {
@@ -214,7 +241,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
     digits8x3(qi, d0, d1, d2);
     const int rt = row >> 4, r16 = row & 15;
     const int ks = d >> 6, grp = (d >> 4) & 3;
-    const int lane = r16 + 16 * grp, e = opnd_byte(d & 15);
+    const int lane = r16 + 16 * grp, e = g.bits == 4 ? opnd_byte4(d & 15) : opnd_byte(d & 15);
     int8_t* base = (int8_t*)(a.qa + ((unit * a.RT + rt) * 2 + ks) * 3 * 64);
     base[(0 * 64 + lane) * 16 + e] = (int8_t)d0;
     base[(1 * 64 + lane) * 16 + e] = (int8_t)d1;
@@ -225,7 +252,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
       const int row = M + x / D, d = x % D;
       const int rt = row >> 4, r16 = row & 15;
       const int ks = d >> 6, grp = (d >> 4) & 3;
-      const int lane = r16 + 16 * grp, e = opnd_byte(d & 15);
+      const int lane = r16 + 16 * grp, e = g.bits == 4 ? opnd_byte4(d & 15) : opnd_byte(d & 15);
       int8_t* base = (int8_t*)(a.qa + ((unit * a.RT + rt) * 2 + ks) * 3 * 64);
       base[(0 * 64 + lane) * 16 + e] = 0;
       base[(1 * 64 + lane) * 16 + e] = 0;
@@ -249,30 +276,83 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
 // One sub-chunk of 64 positions for one wave: key-code words (position 16 cb
 // + lane % 16, dimensions 64 ks + 16 (lane / 16) ..), scale/zero words of
 // those positions, value-code words (dimension 16 db + lane % 16, positions
-// 16 (lane / 16) ..).
+// 16 (lane / 16) ..).  Four bits: two words per group of 16; three bits: the
+// low-plane word and the high-plane word holding the group's high bits.
+template <int BITS>
 struct CBuf {
-  uint32_t kc[4][2];
+  static constexpr int NW = BITS == 4 ? 2 : 1;
+  uint32_t kc[4][2][NW];
+  uint32_t kh[BITS == 3 ? 4 : 1][2];
   uint32_t ksz[4], vsz[4];
-  uint32_t vc[8];
+  uint32_t vc[8][NW];
+  uint32_t vh[BITS == 3 ? 8 : 1];
 };
 
-__device__ __forceinline__ void cload(CBuf& b, const ChunkArgs& a, const QMap& qm, int pbase) {
+template <int BITS>
+__device__ __forceinline__ void cload(CBuf<BITS>& b, const ChunkArgs& a, const QMap& qm, int pbase) {
   const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
   const int64_t row = qrow_read(qm, pbase);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int64_t r = row + 16 * cb + m16;
-    const uint32_t* kw = (const uint32_t*)(a.pl.kcode + r * 32) + grp;
-    b.kc[cb][0] = kw[0];
-    b.kc[cb][1] = kw[4];
+    const uint32_t* kw = (const uint32_t*)(a.pl.kcode + r * (16 * BITS));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (BITS == 4) {
+        b.kc[cb][ks][0] = kw[8 * ks + 2 * grp];
+        b.kc[cb][ks][1] = kw[8 * ks + 2 * grp + 1];
+      } else {
+        b.kc[cb][ks][0] = kw[4 * ks + grp];
+      }
+      // three bits: the high plane (bytes [32, 48)) word of this group
+      if constexpr (BITS == 3) b.kh[cb][ks] = kw[8 + 2 * ks + (grp >> 1)];
+    }
     b.ksz[cb] = a.pl.ksz[r];
     b.vsz[cb] = a.pl.vsz[r];
   }
-  const uint32_t* vw = (const uint32_t*)(a.pl.vcode + ((row >> 6) * D + m16) * 16) + grp;
+  if constexpr (BITS == 2) {
+    const uint32_t* vw = (const uint32_t*)(a.pl.vcode + ((row >> 6) * D + m16) * 16) + grp;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) b.vc[db] = vw[db * 16 * 4];
+    for (int db = 0; db < 8; ++db) b.vc[db][0] = vw[db * 16 * 4];
+  } else if constexpr (BITS == 4) {
+    // 32 positions per row: this group's 16 in block (row / 32) + grp / 2
+    const uint32_t* vw =
+        (const uint32_t*)(a.pl.vcode + (((row >> 5) + (grp >> 1)) * D + m16) * 16) + 2 * (grp & 1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      b.vc[db][0] = vw[db * 16 * 4];
+      b.vc[db][1] = vw[db * 16 * 4 + 1];
+    }
+  } else {
+    // 128-position block: low-plane rows sel = 0, 1 and the high-plane row,
+    // whose 8-byte half sel belongs to this sub-chunk
+    const int64_t blk = row >> 7;
+    const int sel = (int)((row >> 6) & 1);
+    const uint32_t* vw = (const uint32_t*)(a.pl.vcode + ((blk * 3 + sel) * D + m16) * 16) + grp;
+    const uint32_t* hw = (const uint32_t*)(a.pl.vcode + ((blk * 3 + 2) * D + m16) * 16 + 8 * sel) + (grp >> 1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      b.vc[db][0] = vw[db * 16 * 4];
+      b.vh[db] = hw[db * 16 * 4];
+    }
+  }
 }
 
+template <int BITS>
+__device__ __forceinline__ v4i key_bytes(const CBuf<BITS>& b, int cb, int ks, int grp) {
+  if constexpr (BITS == 2) return unpack2(b.kc[cb][ks][0]);
+  else if constexpr (BITS == 4) return unpack4(b.kc[cb][ks][0], b.kc[cb][ks][1]);
+  else return unpack3(b.kc[cb][ks][0], b.kh[cb][ks], 2 * (grp & 1));
+}
+
+template <int BITS>
+__device__ __forceinline__ v4i value_bytes(const CBuf<BITS>& b, int db, int grp) {
+  if constexpr (BITS == 2) return unpack2(b.vc[db][0]);
+  else if constexpr (BITS == 4) return unpack4(b.vc[db][0], b.vc[db][1]);
+  else return unpack3(b.vc[db][0], b.vh[db], 2 * (grp & 1));
+}
+
+template <int BITS>
 __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
   extern __shared__ uint4 smem4[];
   const Geometry& g = a.g;
@@ -323,8 +403,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) O[db][r] = 0.f;
     }
-    const int eb = opnd_byte(m16);
-    auto process = [&](const CBuf& B0, int c) {
+    const int eb = opnd_byte_b<BITS>(m16);
+    auto process = [&](const CBuf<BITS>& B0, int c) {
       const int pbase = c * CSUB;
       // ---- scores: D layout lane, r -> row 4 grp + r, position 16 cb + m16
       float sc[4][4], vs[4], vz[4];
@@ -333,7 +413,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const v4i Bk = unpack2(B0.kc[cb][ks]);
+          const v4i Bk = key_bytes<BITS>(B0, cb, ks, grp);
           a0 = mfma8(A[ks][0], Bk, a0);
           a1 = mfma8(A[ks][1], Bk, a1);
           a2 = mfma8(A[ks][2], Bk, a2);
@@ -346,7 +426,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         vz[cb] = h2f(vw >> 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          // 256 d2 + d1 sums stay below 2^24 (exact as floats); one rounding
+          // 256 d2 + d1 fits in 32 bits (below 2^24, exact as a float, at 2
+          // bits; one more rounding of relative size 2^-24 at 3 and 4 bits)
           const float dot = fmaf((float)(a2[r] * 256 + a1[r]), 256.f, (float)a0[r]);
           sc[cb][r] = ok ? fmaf(ksv, dot * inv[r], kzv * sig[r]) : -INFINITY;
         }
@@ -413,7 +494,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
       const bool keep = __all(fo[0] == 1.f && fo[1] == 1.f && fo[2] == 1.f && fo[3] == 1.f);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const v4i Bv = unpack2(B0.vc[db]);
+        const v4i Bv = value_bytes<BITS>(B0, db, grp);
         const v4i pL = mfma8(Wl, Bv, v4i{0, 0, 0, 0});
         const v4i pH = mfma8(Wh, Bv, v4i{0, 0, 0, 0});
         if (keep) {
@@ -427,7 +508,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
     };
     // two buffers, alternating: the next sub-chunk's codes load during the
     // current one's arithmetic
-    CBuf B0, B1;
+    CBuf<BITS> B0, B1;
     const int n_my = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;  // this wave's sub-chunks
     if (n_my > 0) cload(B0, a, qm, c0 * CSUB);
     // next-buffer loads unconditional (past the end they re-read the current
@@ -654,6 +735,7 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
 
 // One position p = squant(L) + blockIdx.x of [squant(L), squant(L + n)):
 // threads 0..127 quantize its key entry, 128..255 its value entry.
+template <bool B3>
 __global__ __launch_bounds__(256) void chunk_flush_kernel(ChunkArgs a) {
   __shared__ QLds ql;
   const Geometry& g = a.g;
@@ -676,19 +758,25 @@ __global__ __launch_bounds__(256) void chunk_flush_kernel(ChunkArgs a) {
   const QMap qm = qmap_of(g, a.layer, slot, h);
   VRows vr;
   vrows_init(vr);
-  store_quantized<false>(p, x, x, ql, vr, a.pl, qm, g);
-  // the value code of this position, left in vr.lo: only its own bits of
-  // the dimension's row word change
-  if (is_v && vr.lo.row >= 0) {
-    uint32_t* wd = (uint32_t*)(a.pl.vcode + (vr.lo.row * D + i) * 16);
-    const uint32_t bb[4] = {vr.lo.b0, vr.lo.b1, vr.lo.b2, vr.lo.b3};
-    const uint32_t mm[4] = {vr.lo.m0, vr.lo.m1, vr.lo.m2, vr.lo.m3};
+  store_quantized<B3>(p, x, x, ql, vr, a.pl, qm, g);
+  // the value code of this position, left in vr (the low plane, and at 3
+  // bits the high plane): only its own bits of the dimension's row words change
+  if (is_v) {
+    const VRow* rows[2] = {&vr.lo, &vr.hi};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (mm[q]) {
-        atomicAnd(wd + q, ~mm[q]);
-        atomicOr(wd + q, bb[q]);
-      }
+    for (int k = 0; k < (B3 ? 2 : 1); ++k) {
+      const VRow& v = *rows[k];
+      if (v.row < 0) continue;
+      uint32_t* wd = (uint32_t*)(a.pl.vcode + (v.row * D + i) * 16);
+      const uint32_t bb[4] = {v.b0, v.b1, v.b2, v.b3};
+      const uint32_t mm[4] = {v.m0, v.m1, v.m2, v.m3};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (mm[q]) {
+          atomicAnd(wd + q, ~mm[q]);
+          atomicOr(wd + q, bb[q]);
+        }
+    }
   }
 }
 
@@ -710,17 +798,29 @@ hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
     int dev = 0, cus = 0, per = 0;
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, chunk_kernel, 256, lds);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per, a.g.bits == 2 ? chunk_kernel<2> : a.g.bits == 3 ? chunk_kernel<3> : chunk_kernel<4>, 256, lds);
     if (e != hipSuccess) return e;
     int fill = (cus * (per > 0 ? per : 1) - tiles) / tiles;
     if (fill < 1) fill = 1;
     if (a.n_splits > fill) a.n_splits = fill;
   }
   a.xcd_map = (a.n_seq * a.g.n_kv) % 8 == 0;
-  hipLaunchKernelGGL(chunk_kernel, dim3(tiles * (a.n_splits + 1)), dim3(256), lds, st, a);
+  const dim3 grid(tiles * (a.n_splits + 1));
+  if (a.g.bits == 2)
+    hipLaunchKernelGGL(chunk_kernel<2>, grid, dim3(256), lds, st, a);
+  else if (a.g.bits == 3)
+    hipLaunchKernelGGL(chunk_kernel<3>, grid, dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL(chunk_kernel<4>, grid, dim3(256), lds, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.n_flush > 0) {
-    hipLaunchKernelGGL(chunk_flush_kernel, dim3(a.n_flush, a.g.n_kv, a.n_seq), dim3(256), 0, st, a);
+    const dim3 fgrid(a.n_flush, a.g.n_kv, a.n_seq);
+    if (a.g.bits == 3)
+      hipLaunchKernelGGL(chunk_flush_kernel<true>, fgrid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(chunk_flush_kernel<false>, fgrid, dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(chunk_merge_kernel, dim3(a.n_tok * a.g.n_q + a.n_seq * a.g.n_kv), dim3(256), 0,

@@ -252,9 +252,9 @@ wushkv_status wushkv_decode_attn(wushkv_cache* cache, int32_t layer, int32_t n_s
  *   q, tq, out, ws  as in wushkv_decode_attn.
  * EUNSUPPORTED if sink + recent + flush > 1024 (the window one workgroup
  * holds); ECAPACITY if any L + 1 > ctx_cap.  Updates the host lengths on
- * success; a failing call changes nothing.  With 2-bit codes and groups of 8
- * query heads per KV head the step runs as a one-position wushkv_chunk_step
- * (int8 matrix cores), which is faster there.
+ * success; a failing call changes nothing.  With groups of 8 query heads per
+ * KV head the step runs as a one-position wushkv_chunk_step (int8 matrix
+ * cores), which is faster there at every bit width.
  */
 wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_seq,
                                  const int32_t* slots, const void* k, const void* v,
@@ -291,10 +291,10 @@ uint64_t wushkv_chunk_workspace_bytes(const wushkv_cache* cache, int32_t n_seq, 
  *           the value-transform basis.
  *   ws      device workspace of ws_bytes >= wushkv_chunk_workspace_bytes(
  *           n_seq, max n_new), 16-byte aligned; contents on entry ignored.
- * The quantized part runs on the int8 matrix cores: the compensated queries
- * and the softmax weights in 24- and 15-bit fixed point against exact code
- * products.  EUNSUPPORTED unless bits == 2.  Updates the host lengths on success; a failing call changes
- * nothing.
+ * The quantized part runs on the int8 matrix cores at every bit width
+ * (2, 3, 4): the compensated queries and the softmax weights in 24- and
+ * 15-bit fixed point against exact code products.  Updates the host lengths
+ * on success; a failing call changes nothing.
  */
 wushkv_status wushkv_chunk_step(wushkv_cache* cache, int32_t layer, int32_t n_seq,
                                 const int32_t* slots, const int32_t* n_new, const void* k,

@@ -300,7 +300,12 @@ def test_chunk_step_errors():
     for s in range(4):
         assert wk.wushkv_get_len(h, 0, s) == (0, 4)
     wk.wushkv_cache_destroy(h)
-    h, _ = _fake_cache(bits=4)
-    assert wk.wushkv_chunk_step(h, 0, [0], [1], P, P, P, P, P, P, P, need, check=False) == \
-        wk.WUSHKV_EUNSUPPORTED
-    wk.wushkv_cache_destroy(h)
+    # 3- and 4-bit caches take the same argument checks (no launch here)
+    for bits in (3, 4):
+        h, _ = _fake_cache(bits=bits)
+        assert wk.wushkv_chunk_step(h, 0, [0], [17], P, P, P, P, P, P, P, need, check=False) == \
+            wk.WUSHKV_EINVAL
+        small = wk.wushkv_chunk_workspace_bytes(h, 1, 1)
+        assert wk.wushkv_chunk_step(h, 0, [0], [1], P, P, P, P, P, P, P, small - 1, check=False) == \
+            wk.WUSHKV_EWORKSPACE
+        wk.wushkv_cache_destroy(h)

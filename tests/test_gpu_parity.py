@@ -591,17 +591,20 @@ def test_chunk_step_fp32_inputs():
     _run_chunks(synth.WORKLOADS[0], [700], [[16]] * 5 + [[7], [1], [16]])
 
 
-def test_chunk_step_gqa_ragged():
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_chunk_step_gqa_ragged(bits):
     """32 query / 8 KV heads, three sequences (one starting empty) with ragged
-    chunk sizes in each call."""
-    _run_chunks(synth.WORKLOADS[1], [1500, 0, 777], [[16, 5, 16], [3, 16, 1], [16, 16, 16], [1, 2, 9]])
+    chunk sizes in each call, at every bit width (3 bits: low and high planes
+    unpacked into one operand byte; 4 bits: two code words per 16 elements)."""
+    _run_chunks(synth.WORKLOADS[1], [1500, 0, 777], [[16, 5, 16], [3, 16, 1], [16, 16, 16], [1, 2, 9]],
+                bits=bits)
 
 
-@pytest.mark.parametrize("G", [1, 2, 8])
-def test_chunk_step_groups(G):
+@pytest.mark.parametrize("G,bits", [(1, 2), (2, 2), (8, 2), (8, 4), (1, 3), (8, 3)])
+def test_chunk_step_groups(G, bits):
     """Row tiles of 16 query rows: 16 positions x G heads (one tile at G = 1,
     eight at G = 8)."""
-    _run_chunks(_gqa_workload(3000, G=G), [2100, 1333], [[16, 16], [16, 11], [4, 16]])
+    _run_chunks(_gqa_workload(3000, G=G), [2100, 1333], [[16, 16], [16, 11], [4, 16]], bits=bits)
 
 
 def test_chunk_step_paper_windows_from_empty():
@@ -612,17 +615,20 @@ def test_chunk_step_paper_windows_from_empty():
                 check_every=3)
 
 
-def test_chunk_step_paged():
-    _run_chunks(synth.WORKLOADS[1], [1100, 300], [[16, 16], [16, 3], [9, 16]], page=128)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_chunk_step_paged(bits):
+    _run_chunks(synth.WORKLOADS[1], [1100, 300], [[16, 16], [16, 3], [9, 16]], page=128, bits=bits)
 
 
-def test_chunk_step_same_cache_as_append():
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_chunk_step_same_cache_as_append(bits):
     """The cache a chunk step leaves equals the one wushkv_append of the same
-    positions leaves, bit for bit."""
+    positions leaves, bit for bit (3 bits: the flush's word atomics on both
+    value planes)."""
     w = synth.WORKLOADS[1]
     L0, steps = 600, [16, 16, 7, 16, 1, 16]
     n = sum(steps)
-    dc = _cache(w, S=4, R=32, F=4, max_batch=2, ctx_cap=L0 + n)
+    dc = _cache(w, bits=bits, S=4, R=32, F=4, max_batch=2, ctx_cap=L0 + n)
     T, Tq = synth.transforms(w, 0)
     k, v = _inputs(w, 0, 0, L0 + n)
     tk, tq = torch.from_numpy(T).cuda(), torch.from_numpy(Tq).cuda()
@@ -647,12 +653,13 @@ def test_chunk_step_same_cache_as_append():
             assert np.array_equal(np.nan_to_num(a[key], nan=7.0), np.nan_to_num(b[key], nan=7.0))
 
 
-def test_decode_step_group8_two_bit():
-    """Groups of 8 query heads on a 2-bit cache: wushkv_decode_step runs as a
-    one-position chunk step (int8 matrix cores); steps from a prefill and from
-    an empty sequence, with flush batches."""
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_decode_step_group8(bits):
+    """Groups of 8 query heads: wushkv_decode_step runs as a one-position
+    chunk step (int8 matrix cores); steps from a prefill and from an empty
+    sequence, with flush batches."""
     w = _gqa_workload(2000, G=8)
-    _run_steps(w, [1500, 0], 20, S=4, R=32, F=4, check_every=4)
+    _run_steps(w, [1500, 0], 20, bits=bits, S=4, R=32, F=4, check_every=4)
 
 
 def test_chunk_step_rms_codec():
