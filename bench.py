@@ -779,7 +779,8 @@ def main():
         rows = []
         for wid, b in ((0, 2), (1, 2), (2, 2), (4, 2), (4, 4)):
             wl = synth.WORKLOADS[wid]
-            mm = measure_decode(wl, b, 3, 1, dev, True)
+            # single-layer workloads: enough steps that launch jitter averages out
+            mm = measure_decode(wl, b, 3 if wl.n_layers > 1 else 40, 1, dev, True)
             Bw = len(wl.lengths())
             rows.append({"workload": wl.name, "bits": b, "ms_per_step": round(mm["ms_per_step"], 4),
                          "cache_gbs": round(mm["value"], 1),
