@@ -151,6 +151,18 @@ __device__ __forceinline__ void digits8x3(int x, int& d0, int& d1, int& d2) {
   d2 = (x - d1) >> 8;
 }
 
+// Lanes l and l ^ 32 combined (v_permlane32_swap gives every lane both
+// values, in the same order on both sides).
+__device__ __forceinline__ float cross_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float cross_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
@@ -352,7 +364,12 @@ __device__ __forceinline__ v4i value_bytes(const CBuf<BITS>& b, int db, int grp)
   else return unpack3(b.vc[db][0], b.vh[db], 2 * (grp & 1));
 }
 
-template <int BITS>
+// PAIR (2 bits, one row tile holding at most 8 query rows, e.g. a decode
+// step with groups of 8): rows 8..15 of the tile carry the same queries as rows 0..7
+// and score the odd 16-position column blocks while rows 0..7 score the even
+// ones, so every lane's softmax and weight work is useful.  The two halves
+// share each row's maximum; their sums and outputs add up at the end.
+template <int BITS, bool PAIR>
 __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
   extern __shared__ uint4 smem4[];
   const Geometry& g = a.g;
@@ -386,10 +403,21 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
     v4i A[2][3];  // [d half][digit]
 #pragma unroll
     for (int x = 0; x < 6; ++x) A[x / 3][x % 3] = qa[x * 64 + lane];
+    // PAIR: the operand with rows 0..7 moved to rows 8..15 (row_shr:8 inside
+    // each 16-lane row; rows 0..7 become 0)
+    v4i Ah[PAIR ? 2 : 1][3];
+    if constexpr (PAIR) {
+#pragma unroll
+      for (int x = 0; x < 6; ++x)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Ah[x / 3][x % 3][q] = __builtin_amdgcn_update_dpp(0, A[x / 3][x % 3][q], 0x118, 0xF, 0xF, false);
+    }
+    constexpr int NC = PAIR ? 2 : 4;  // 16-position column blocks scored per lane
+    const int half = grp >> 1;        // PAIR: lanes 32..63 hold rows 8..15
     float sig[4], inv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * rt + 4 * grp + r;
+      const int row = PAIR ? (4 * grp + r) & 7 : 16 * rt + 4 * grp + r;
       const float* qr = a.qf + ((int64_t)u * M + (row < M ? row : 0)) * (D + 4);
       sig[r] = row < M ? qr[D] : 0.f;
       inv[r] = row < M ? qr[D + 1] : 0.f;
@@ -406,63 +434,82 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
     const int eb = opnd_byte_b<BITS>(m16);
     auto process = [&](const CBuf<BITS>& B0, int c) {
       const int pbase = c * CSUB;
-      // ---- scores: D layout lane, r -> row 4 grp + r, position 16 cb + m16
-      float sc[4][4], vs[4], vz[4];
+      // ---- scores: D layout lane, r -> row 4 grp + r, position 16 cbl + m16
+      // (cbl = cc, or in PAIR 2 cc + half)
+      float sc[NC][4], vs[NC], vz[NC];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cc = 0; cc < NC; ++cc) {
         v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const v4i Bk = key_bytes<BITS>(B0, cb, ks, grp);
-          a0 = mfma8(A[ks][0], Bk, a0);
-          a1 = mfma8(A[ks][1], Bk, a1);
-          a2 = mfma8(A[ks][2], Bk, a2);
+          if constexpr (PAIR) {
+            const v4i Be = key_bytes<BITS>(B0, 2 * cc, ks, grp);
+            const v4i Bo = key_bytes<BITS>(B0, 2 * cc + 1, ks, grp);
+            a0 = mfma8(Ah[ks][0], Bo, mfma8(A[ks][0], Be, a0));
+            a1 = mfma8(Ah[ks][1], Bo, mfma8(A[ks][1], Be, a1));
+            a2 = mfma8(Ah[ks][2], Bo, mfma8(A[ks][2], Be, a2));
+          } else {
+            const v4i Bk = key_bytes<BITS>(B0, cc, ks, grp);
+            a0 = mfma8(A[ks][0], Bk, a0);
+            a1 = mfma8(A[ks][1], Bk, a1);
+            a2 = mfma8(A[ks][2], Bk, a2);
+          }
         }
-        const int p = pbase + 16 * cb + m16;
+        const int cbl = PAIR ? 2 * cc + half : cc;
+        const int p = pbase + 16 * cbl + m16;
         const bool ok = p >= lo && p < hi;
-        const float ksv = h2f(B0.ksz[cb] & 0xFFFFu), kzv = h2f(B0.ksz[cb] >> 16);
-        const uint32_t vw = ok ? B0.vsz[cb] : 0u;  // masked positions: scale and zero 0
-        vs[cb] = h2f(vw & 0xFFFFu);
-        vz[cb] = h2f(vw >> 16);
+        const uint32_t kw = PAIR ? (half ? B0.ksz[2 * cc + 1] : B0.ksz[2 * cc]) : B0.ksz[cc];
+        const uint32_t vr = PAIR ? (half ? B0.vsz[2 * cc + 1] : B0.vsz[2 * cc]) : B0.vsz[cc];
+        const float ksv = h2f(kw & 0xFFFFu), kzv = h2f(kw >> 16);
+        const uint32_t vw = ok ? vr : 0u;  // masked positions: scale and zero 0
+        vs[cc] = h2f(vw & 0xFFFFu);
+        vz[cc] = h2f(vw >> 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           // 256 d2 + d1 fits in 32 bits (below 2^24, exact as a float, at 2
           // bits; one more rounding of relative size 2^-24 at 3 and 4 bits)
           const float dot = fmaf((float)(a2[r] * 256 + a1[r]), 256.f, (float)a0[r]);
-          sc[cb][r] = ok ? fmaf(ksv, dot * inv[r], kzv * sig[r]) : -INFINITY;
+          sc[cc][r] = ok ? fmaf(ksv, dot * inv[r], kzv * sig[r]) : -INFINITY;
         }
       }
       // ---- per row: sub-chunk max, weights p = exp2(s - m), w = p s_v
       float m[4], wmax[4], lsum[4], zsum[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = fmaxf(fmaxf(sc[0][r], sc[1][r]), fmaxf(sc[2][r], sc[3][r]));
+        float x = sc[0][r];
+#pragma unroll
+        for (int cc = 1; cc < NC; ++cc) x = fmaxf(x, sc[cc][r]);
         m[r] = row16_max(x);
+        if constexpr (PAIR) m[r] = cross_max(m[r]);
         float wm = 0.f;
         lsum[r] = zsum[r] = 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const float p = __builtin_amdgcn_exp2f(sc[cb][r] - m[r]);
-          sc[cb][r] = p * vs[cb];
-          lsum[r] += p;
-          zsum[r] = fmaf(p, vz[cb], zsum[r]);
-          wm = fmaxf(wm, sc[cb][r]);
+        for (int cc = 0; cc < NC; ++cc) {
+          const float pp = __builtin_amdgcn_exp2f(sc[cc][r] - m[r]);
+          sc[cc][r] = pp * vs[cc];
+          lsum[r] += pp;
+          zsum[r] = fmaf(pp, vz[cc], zsum[r]);
+          wm = fmaxf(wm, sc[cc][r]);
         }
         wmax[r] = row16_max(wm);
+        if constexpr (PAIR) wmax[r] = cross_max(wmax[r]);
       }
       // ---- weight codes into this wave's A operand (row, position) layout:
-      // lane 4 grp + r + 16 cb, operand byte of m16; lo digit in the low byte
+      // lane 4 grp + r + 16 cbl, operand byte of m16; lo digit in the low
+      // byte.  PAIR: each row's other column blocks get zero weights.
       wave_fence();  // the previous sub-chunk's operand reads are done
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float wsc = wmax[r] > 0.f ? (float)W8MAX * __builtin_amdgcn_rcpf(wmax[r]) : 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          int wq = (int)rintf(sc[cb][r] * wsc);
+        for (int cc = 0; cc < NC; ++cc) {
+          int wq = (int)rintf(sc[cc][r] * wsc);
           wq = wq > W8MAX ? W8MAX : wq;
           // balanced digits lo = ((wq + 128) & 255) - 128, hi = (wq + 128) >> 8
           // as two's-complement bytes: lo byte = wq & 255
-          wl[((4 * grp + r) + 16 * cb) * 16 + eb] = (uint16_t)(((wq + 128) & 0xFF00) | (wq & 0xFF));
+          const int cbl = PAIR ? 2 * cc + half : cc;
+          wl[((4 * grp + r) + 16 * cbl) * 16 + eb] = (uint16_t)(((wq + 128) & 0xFF00) | (wq & 0xFF));
+          if constexpr (PAIR) wl[((4 * grp + r) + 16 * (2 * cc + 1 - half)) * 16 + eb] = 0;
         }
       }
       wave_fence();
@@ -522,15 +569,24 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
       process(B1, c0 + (it + 1) * nw);
     }
     // ---- this wave's partial: o (unnormalized, zero-point term added), m, l
+    // (PAIR: the two halves of each row added; rows 0..7 written)
     float* dst = part + (int64_t)(4 * j + w) * CROWS * PS;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float Lw = row16_sum(Lp[r]);
-      const float Zw = row16_sum(Zp[r]);
+      float Lw = row16_sum(Lp[r]);
+      float Zw = row16_sum(Zp[r]);
+      if constexpr (PAIR) {
+        Lw = cross_sum(Lw);
+        Zw = cross_sum(Zw);
+      }
       float* pr = dst + (4 * grp + r) * PS;
+      const bool wr = !PAIR || half == 0;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) pr[16 * db + m16] = O[db][r] + Zw;
-      if (m16 == 0) {
+      for (int db = 0; db < 8; ++db) {
+        const float o = PAIR ? cross_sum(O[db][r]) : O[db][r];
+        if (wr) pr[16 * db + m16] = o + Zw;
+      }
+      if (wr && m16 == 0) {
         pr[D] = Mx[r];
         pr[D + 1] = Lw;
       }
@@ -800,7 +856,8 @@ hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, a.g.bits == 2 ? chunk_kernel<2> : a.g.bits == 3 ? chunk_kernel<3> : chunk_kernel<4>, 256, lds);
+          &per, a.g.bits == 2 ? chunk_kernel<2, false> : a.g.bits == 3 ? chunk_kernel<3, false> : chunk_kernel<4, false>,
+          256, lds);
     if (e != hipSuccess) return e;
     int fill = (cus * (per > 0 ? per : 1) - tiles) / tiles;
     if (fill < 1) fill = 1;
@@ -808,12 +865,20 @@ hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
   }
   a.xcd_map = (a.n_seq * a.g.n_kv) % 8 == 0;
   const dim3 grid(tiles * (a.n_splits + 1));
-  if (a.g.bits == 2)
-    hipLaunchKernelGGL(chunk_kernel<2>, grid, dim3(256), lds, st, a);
-  else if (a.g.bits == 3)
-    hipLaunchKernelGGL(chunk_kernel<3>, grid, dim3(256), lds, st, a);
-  else
-    hipLaunchKernelGGL(chunk_kernel<4>, grid, dim3(256), lds, st, a);
+  // paired rows at 2 bits (0.178 -> 0.163 ms per layer for a decode step
+  // with groups of 8 on the 64K-prefill cache); at 3 and 4 bits the extra
+  // operand registers cost more than the halved row work saves
+  const bool pair = a.g.bits == 2 && a.RT == 1 && a.C * a.g.G <= 8;
+  if (a.g.bits == 2) {
+    if (pair)
+      hipLaunchKernelGGL((chunk_kernel<2, true>), grid, dim3(256), lds, st, a);
+    else
+      hipLaunchKernelGGL((chunk_kernel<2, false>), grid, dim3(256), lds, st, a);
+  } else if (a.g.bits == 3) {
+    hipLaunchKernelGGL((chunk_kernel<3, false>), grid, dim3(256), lds, st, a);
+  } else {
+    hipLaunchKernelGGL((chunk_kernel<4, false>), grid, dim3(256), lds, st, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.n_flush > 0) {
     const dim3 fgrid(a.n_flush, a.g.n_kv, a.n_seq);

@@ -607,6 +607,17 @@ def test_chunk_step_groups(G, bits):
     _run_chunks(_gqa_workload(3000, G=G), [2100, 1333], [[16, 16], [16, 11], [4, 16]], bits=bits)
 
 
+@pytest.mark.parametrize("G,plan,bits", [(1, [[8, 3], [5, 8], [1, 1]], 2), (2, [[4, 4], [3, 1]], 2),
+                                         (4, [[2, 1], [2, 2]], 2), (2, [[4, 4], [3, 1]], 4),
+                                         (4, [[2, 1], [2, 2]], 3)])
+def test_chunk_step_paired_rows(G, plan, bits):
+    """Chunks of at most 8 query rows per KV head (n_new G <= 8).  At 2 bits
+    the second half of the row tile repeats the queries against the other
+    column blocks of each sub-chunk and the halves merge per row; at 3 and 4
+    bits the same small tiles run unpaired."""
+    _run_chunks(_gqa_workload(3000, G=G), [2100, 1333], plan, bits=bits)
+
+
 def test_chunk_step_paper_windows_from_empty():
     """The paper's evaluation windows (sink 16, recent 128, flush 16) from
     empty sequences in 16-position chunks: the sink fills inside a chunk, the
