@@ -352,13 +352,21 @@ def test_decode_step_gqa_ragged(bits):
     _run_steps(synth.WORKLOADS[1], [1500, 0, 777], 5, bits=bits, check_every=2)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_step_prepared_query_blocks(bits):
     """Contexts past 2K positions with little cache traffic: the launcher
     prepares each unit's query (and the step's new entry) once in the prep
     kernel and oversubscribes the split grid; parity as for the in-workgroup
     preparation."""
     _run_steps(synth.WORKLOADS[1], [2600, 0, 2301], 3, bits=bits, check_every=1)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_decode_step_prepared_query_blocks_fp32_paged(G):
+    """The prep-kernel path with fp32 inputs (query and new entry converted in
+    the prep kernel) and on a paged cache with shuffled pages."""
+    _run_steps(_gqa_workload(4000, G=G, io="fp32"), [3500, 2200], 3, check_every=1)
+    _run_steps(_gqa_workload(4000, G=G), [3500, 2200], 3, check_every=1, page=128)
 
 
 def test_decode_step_same_cache_as_append():
