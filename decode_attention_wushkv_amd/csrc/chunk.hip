@@ -176,6 +176,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
   __shared__ float qs[8][D];
   __shared__ float stat[8][2];
   __shared__ float kin[D];
+  __shared__ double khs[2][D];  // half-row sums of the new key's transform
   const int c = blockIdx.x, h = blockIdx.y, si = blockIdx.z, tid = threadIdx.x;
   const Geometry& g = a.g;
   const int G = g.G, M = a.C * G, i = tid & (D - 1), hf = tid >> 7;
@@ -194,8 +195,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
     t[4 * x + 2] = t4.z;
     t[4 * x + 3] = t4.w;
   }
+  // this thread's half row of T_K for the new key (all loads issued before
+  // the first wait)
+  float tkr[64];
+  {
+    const float4* kp = (const float4*)(a.tk + ((int64_t)h * D + i) * D + 64 * hf);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const float4 t4 = kp[x];
+      tkr[4 * x] = t4.x;
+      tkr[4 * x + 1] = t4.y;
+      tkr[4 * x + 2] = t4.z;
+      tkr[4 * x + 3] = t4.w;
+    }
+  }
   if (tid < D) kin[tid] = valid ? ld_io<IO_BF16>(a.k, (tok * g.n_kv + h) * D + tid) : 0.f;
   __syncthreads();
+  // k' = T_K k in the shared fp64 order: thread (i, hf) sums chains 2 hf and
+  // 2 hf + 1 of row i (dimensions [64 hf, 64 hf + 64)); row i's entry is
+  // (s0 + s1) + (s2 + s3)
+  {
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) {
+      s0 = fma((double)tkr[j], (double)kin[64 * hf + j], s0);
+      s1 = fma((double)tkr[32 + j], (double)kin[64 * hf + 32 + j], s1);
+    }
+    khs[hf][i] = s0 + s1;
+  }
   for (int gg = 0; gg < G; ++gg) {
     float acc = 0.f;
 #pragma unroll
@@ -270,16 +297,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
       base[(1 * 64 + lane) * 16 + e] = 0;
       base[(2 * 64 + lane) * 16 + e] = 0;
     }
-  // the chunk position's new entry: k' = T_K k in fp64, one rounding; v
+  // the chunk position's new entry: k' rounded once to bfloat16; v
+  // (khs was written before the barriers above)
   if (valid) {
     uint16_t* dst = a.knew + (((int64_t)si * a.C + c) * g.n_kv + h) * 2 * D;
-    if (tid < D) {
-      const float* trow = a.tk + ((int64_t)h * D + tid) * D;
-      const double acc = transform_entry([&](int j) { return trow[j]; }, [&](int j) { return kin[j]; });
-      dst[tid] = f64_to_bf16(acc);
-    } else {
+    if (tid < D)
+      dst[tid] = f64_to_bf16(khs[0][tid] + khs[1][tid]);
+    else
       dst[D + i] = io_bf16_bits<IO_BF16>(a.v, (tok * g.n_kv + h) * D + i);
-    }
   }
 }
 
@@ -737,20 +762,20 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
     const int h = jq / g.G, gg = jq % g.G;
     const int row = c * g.G + gg, rt = row >> 4, r16 = row & 15;
     const float* src = a.part + (((int64_t)si * g.n_kv + h) * a.RT + rt) * NP * CROWS * PS + r16 * PS;
-    // maximum over the partials that hold weight
-    float mx = -INFINITY;
-    for (int x = tid; x < NP; x += 256) {
-      const float* px = src + (int64_t)x * CROWS * PS;
-      if (px[D + 1] > 0.f) mx = fmaxf(mx, px[D]);
+    // maximum over the partials that hold weight: the first wave reduces
+    // (NP <= 4 * 64 + 1 partials, strided over its lanes)
+    if (tid < 64) {
+      float mx = -INFINITY;
+      for (int x = tid; x < NP; x += 64) {
+        const float* px = src + (int64_t)x * CROWS * PS;
+        if (px[D + 1] > 0.f) mx = fmaxf(mx, px[D]);
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (tid == 0) mred[0] = mx;
     }
-    mred[tid] = mx;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if (tid < s) mred[tid] = fmaxf(mred[tid], mred[tid + s]);
-      __syncthreads();
-    }
-    mx = mred[0];
-    __syncthreads();
+    const float mx = mred[0];
     // thread = (dimension, partial residue mod 2)
     const int dim = tid & (D - 1), hf = tid >> 7;
     float o = 0.f, l = 0.f;
