@@ -200,10 +200,15 @@ def unit_bytes(L, S, R, F, bits, step=True):
     return quant * (2 * (128 * bits // 8) + 8) + window * 512
 
 
-def cpu_baseline(w, bits, seconds, max_units):
+def cpu_baseline(w, bits, seconds, max_units, threads=1):
     """The CPU reference's decode attention (dequantize + naive softmax attention,
-    fp64, one thread) on a bounded sample of (layer, KV head) units of the same
-    workload, with arbitrary stored contents of the same shape."""
+    fp64) on a bounded sample of (layer, KV head) units of the same workload,
+    with arbitrary stored contents of the same shape.  One thread, then (when
+    threads > 1) one unit stream per thread over the same contents for
+    seconds / 2 of wall time (the oracle's C calls release the interpreter
+    lock)."""
+    import threading
+
     import numpy as np
 
     import oracle
@@ -213,23 +218,52 @@ def cpu_baseline(w, bits, seconds, max_units):
     L = max(w.lengths())
     S, R, F = w.sink, w.recent, w.flush
     sq = squant(L, S, R, F)
+    qp = slice(S, sq)
+
+    def unit(cont, q):
+        K = cont["k_bf16"].astype(np.float64)
+        V = cont["v_bf16"].astype(np.float64)
+        K[qp] = oracle.dequantize(cont["kcodes"][qp], cont["ks16"][qp], cont["kz16"][qp])
+        V[qp] = oracle.dequantize(cont["vcodes"][qp], cont["vs16"][qp], cont["vz16"][qp])
+        oracle.attention(q, K[None], V[None])
+
     done, elapsed = 0, 0.0
     while done < max_units and elapsed < seconds:
         cont = synth.random_cache_contents(rng, L, bits)
         q = rng.standard_normal((w.group, 128))
         t0 = time.perf_counter()
-        K = cont["k_bf16"].astype(np.float64)
-        V = cont["v_bf16"].astype(np.float64)
-        qp = slice(S, sq)
-        K[qp] = oracle.dequantize(cont["kcodes"][qp], cont["ks16"][qp], cont["kz16"][qp])
-        V[qp] = oracle.dequantize(cont["vcodes"][qp], cont["vs16"][qp], cont["vz16"][qp])
-        oracle.attention(q, K[None], V[None])
+        unit(cont, q)
         elapsed += time.perf_counter() - t0
         done += 1
-    gbs = done * unit_bytes(L, S, R, F, bits, step=False) / elapsed / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (layer, KV head) units of {w.group} query head(s) at context {L}, "
-                      f"dequantize + fp64 softmax attention, {elapsed:.1f} s"}
+    ub = unit_bytes(L, S, R, F, bits, step=False)
+    one = done * ub / elapsed / 1e9
+    res = {"value": round(one, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} (layer, KV head) units of {w.group} query head(s) at context {L}, "
+                     f"dequantize + fp64 softmax attention, {elapsed:.1f} s"}
+    if threads > 1:
+        conts = [(synth.random_cache_contents(rng, L, bits), rng.standard_normal((w.group, 128)))
+                 for _ in range(threads)]
+        counts = [0] * threads
+        t_end = time.perf_counter() + seconds / 2
+
+        def run(k):
+            while time.perf_counter() < t_end:
+                unit(*conts[k])
+                counts[k] += 1
+
+        t0 = time.perf_counter()
+        ths = [threading.Thread(target=run, args=(k,)) for k in range(threads)]
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        wall = time.perf_counter() - t0
+        multi = sum(counts) * ub / wall / 1e9
+        res = {"value": round(multi, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{sum(counts)} (layer, KV head) units of {w.group} query head(s) at context "
+                         f"{L} on {threads} threads, {wall:.1f} s wall",
+               "single_thread": res}
+    return res
 
 
 def read_ceiling(window_bytes, dev, copies=6):
@@ -619,7 +653,10 @@ def main():
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the streaming-read ceiling and the bf16-cache comparison")
     ap.add_argument("--prefill-workload", type=int, default=4)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-threads", type=int,
+                    default=min(16, int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1),
+                    help="threads of the oracle's multi-threaded timing (1: single-threaded only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this size first (hardware-counter "
                          "calibration: bytes fetched/written by a copy of known size)")
@@ -794,7 +831,8 @@ def main():
         res["chunk_step"] = [chunk_rate(wid, dev) for wid in sorted({args.workload, 1})
                              if synth.WORKLOADS[wid].bits[0] == 2]
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_seconds, max_units=400)
+        res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_seconds, max_units=400,
+                                           threads=args.cpu_threads)
     print(json.dumps(res), flush=True)
 
 
