@@ -1167,40 +1167,46 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
 // One workgroup per (sequence, query head): log-sum-exp merge of the
 // partials.  Thread = (4 dimensions, partial residue mod 8).
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  __shared__ float scal[256];
+  // partials per residue class mod 8: n_splits <= 64, so at most 65 partials
+  constexpr int KMAX = 9;
   __shared__ __align__(16) float racc[8][D];
   __shared__ float red[64];
   const int jq = blockIdx.x, si = blockIdx.y, tid = threadIdx.x;
   const int nsp = a.n_splits + 1;
   const float* src = a.wsp + ((int64_t)si * a.g.n_q + jq) * nsp * PS;
   const int d4 = (tid & 31) * 4, rsd = tid >> 5;
-  float M[1] = {-INFINITY};
-  for (int x = tid; x < nsp; x += 256)
-    if (src[x * PS + D + 1] > 0.f) M[0] = fmaxf(M[0], src[x * PS + D]);
+  // every load in flight at once: (m, l) of partial tid, and this thread's
+  // four dimensions of partials rsd, rsd + 8, ... with their (m, l)
+  float mt = -INFINITY, lt = 0.f;
+  if (tid < nsp) {
+    mt = src[tid * PS + D];
+    lt = src[tid * PS + D + 1];
+  }
+  float4 v[KMAX];
+  float my[KMAX], ly[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int y = rsd + 8 * k;
+    v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    my[k] = 0.f;
+    ly[k] = 0.f;
+    if (y < nsp) {
+      v[k] = *(const float4*)(src + (int64_t)y * PS + d4);
+      my[k] = src[y * PS + D];
+      ly[k] = src[y * PS + D + 1];
+    }
+  }
+  float M[1] = {lt > 0.f ? mt : -INFINITY};
   block_reduce<1, true>(M, red);
-  float Ls[1] = {0.f};
+  float Ls[1] = {lt > 0.f ? lt * exp2f(mt - M[0]) : 0.f};
   float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < nsp; c0 += 256) {
-    __syncthreads();
-    const int x = c0 + tid;
-    float f = 0.f;
-    if (x < nsp) {
-      const float lx = src[x * PS + D + 1];
-      f = lx > 0.f ? exp2f(src[x * PS + D] - M[0]) : 0.f;
-      Ls[0] = fmaf(lx, f, Ls[0]);
-    }
-    scal[tid] = f;
-    __syncthreads();
-    const int n = nsp - c0 < 256 ? nsp - c0 : 256;
-#pragma unroll 4
-    for (int y = rsd; y < n; y += 8) {
-      const float fy = scal[y];
-      const float4 v = *(const float4*)(src + (int64_t)(c0 + y) * PS + d4);
-      o4.x = fmaf(v.x, fy, o4.x);
-      o4.y = fmaf(v.y, fy, o4.y);
-      o4.z = fmaf(v.z, fy, o4.z);
-      o4.w = fmaf(v.w, fy, o4.w);
-    }
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const float fy = ly[k] > 0.f ? exp2f(my[k] - M[0]) : 0.f;
+    o4.x = fmaf(v[k].x, fy, o4.x);
+    o4.y = fmaf(v[k].y, fy, o4.y);
+    o4.z = fmaf(v[k].z, fy, o4.z);
+    o4.w = fmaf(v[k].w, fy, o4.w);
   }
   block_reduce<1, false>(Ls, red);
   *(float4*)(&racc[rsd][d4]) = o4;
