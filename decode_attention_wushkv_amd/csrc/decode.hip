@@ -725,7 +725,7 @@ __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
 // dimensions.
 template <int BITS, int G>
 __device__ void step_append(const DecodeArgs& a, int64_t unit, const QMap& qm, int Lq, int sq,
-                            uint32_t* sm) {
+                            uint32_t* sm, uint16_t first) {
   using C = SplitCfg<BITS, G>;
   const Geometry& g = a.g;
   const int tid = threadIdx.x, i = tid & (D - 1);
@@ -741,7 +741,8 @@ __device__ void step_append(const DecodeArgs& a, int64_t unit, const QMap& qm, i
   const int e1 = sq1 < L0 ? sq1 : L0;
   for (int p = sq; p < e1; ++p) {
     const int64_t row = (unit * g.W + (p - g.S) % g.W) * D + i;
-    const float x = bf16_bits_to_f32(is_v ? a.pl.vring[row] : a.pl.kring[row]);
+    // the first leaving entry was read at the window workgroup's start
+    const float x = bf16_bits_to_f32(p == sq ? first : (is_v ? a.pl.vring[row] : a.pl.kring[row]));
     store_quantized<BITS == 3>(p, x, x, ql, vr, a.pl, qm, g);
   }
   __syncthreads();  // ring reads above complete before the ring write below
@@ -785,6 +786,20 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
            : tok < ns ? sink + (unit * g.S + p) * D
                       : ring + (unit * g.W + (p - g.S) % g.W) * D;
   };
+
+  // G <= 2: the value rows of the first PV round (tokens 0..127) in flight
+  // with the key rows, so the PV starts without another round trip (with
+  // more heads the registers are needed by the scores)
+  const int dg = tid & 15, tl = tid >> 4;
+  uint4 vb0[G <= 2 ? 8 : 1];
+  if constexpr (G <= 2) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tok = 16 * r + tl;
+      vb0[r] = tok < ntok ? ((const uint4*)row_of(tok, a.pl.vsink, a.pl.vring, vnew))[dg]
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
 
   // ---- scores: a lane pair per token (64 dimensions each)
   if constexpr (G <= 2) {
@@ -871,7 +886,6 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
 
   // ---- o = sum_t p_t v_t: thread = (8 dimensions, token lane of 16); eight
   // rows per thread in flight per round of 128 tokens
-  const int dg = tid & 15, tl = tid >> 4;
   float acc[G][8];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg)
@@ -882,8 +896,11 @@ __device__ void window_chunk(const DecodeArgs& a, int64_t unit, int Lq, int sq, 
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int tok = base + 16 * r + tl;
-      vb[r] = tok < ntok ? ((const uint4*)row_of(tok, a.pl.vsink, a.pl.vring, vnew))[dg]
-                         : make_uint4(0u, 0u, 0u, 0u);
+      if (G <= 2 && base == 0)
+        vb[r] = vb0[G <= 2 ? r : 0];
+      else
+        vb[r] = tok < ntok ? ((const uint4*)row_of(tok, a.pl.vsink, a.pl.vring, vnew))[dg]
+                           : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -1047,9 +1064,20 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
     empty = c_first + 4 * j >= c_end;
   }
   float m[G], l[G];
+  uint16_t first_leaving = 0;
   bool direct = false;  // head-split workgroups write their partials themselves
   if (!empty) {
     if (j == a.n_splits) {
+      // a decode step's first ring entry to quantize after the attention
+      // (position sq when it leaves the window), read now
+      uint16_t first_lv = 0;
+      if (a.k_new) {
+        const int e1 = squant_of(Lq, g.S, g.R, g.F) < Lq - 1 ? squant_of(Lq, g.S, g.R, g.F) : Lq - 1;
+        if (sq < e1) {
+          const int64_t row = (unit * g.W + (sq - g.S) % g.W) * D + (tid & (D - 1));
+          first_lv = tid >= D ? a.pl.vring[row] : a.pl.kring[row];
+        }
+      }
       if constexpr (PREP) {
         PrepIn<G> pin;
         prep_load<G>(a, u, pin);
@@ -1062,6 +1090,7 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
         compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
       }
       window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
+      first_leaving = first_lv;
     } else if constexpr (C::HS) {
       // head split: the four waves walk the same sub-chunks, wave w taking
       // query heads [w GW, w GW + GW)
@@ -1161,7 +1190,7 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
       }
     }
   }
-  if (a.k_new && j == a.n_splits) step_append<BITS, G>(a, unit, qm, Lq, sq, sm);
+  if (a.k_new && j == a.n_splits) step_append<BITS, G>(a, unit, qm, Lq, sq, sm, first_leaving);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the
