@@ -762,8 +762,23 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
     const int h = jq / g.G, gg = jq % g.G;
     const int row = c * g.G + gg, rt = row >> 4, r16 = row & 15;
     const float* src = a.part + (((int64_t)si * g.n_kv + h) * a.RT + rt) * NP * CROWS * PS + r16 * PS;
-    // maximum over the partials that hold weight: the first wave reduces
-    // (NP <= 4 * 64 + 1 partials, strided over its lanes)
+    // thread = (dimension, partial residue mod 2).  Every load of the first
+    // 2 KM partials is issued before the maximum is known (one round trip);
+    // the first wave reduces the maximum over all NP <= 4 * 64 + 1 partials.
+    constexpr int KM = 16;
+    const int dim = tid & (D - 1), hf = tid >> 7;
+    float ov[KM], mv[KM], lv[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      const int x = hf + 2 * k;
+      ov[k] = mv[k] = lv[k] = 0.f;
+      if (x < NP) {
+        const float* px = src + (int64_t)x * CROWS * PS;
+        ov[k] = px[dim];
+        mv[k] = px[D];
+        lv[k] = px[D + 1];
+      }
+    }
     if (tid < 64) {
       float mx = -INFINITY;
       for (int x = tid; x < NP; x += 64) {
@@ -776,10 +791,16 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
     }
     __syncthreads();
     const float mx = mred[0];
-    // thread = (dimension, partial residue mod 2)
-    const int dim = tid & (D - 1), hf = tid >> 7;
     float o = 0.f, l = 0.f;
-    for (int x = hf; x < NP; x += 2) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (lv[k] > 0.f) {
+        const float f = __builtin_amdgcn_exp2f(mv[k] - mx);
+        o = fmaf(ov[k], f, o);
+        l = fmaf(lv[k], f, l);
+      }
+    }
+    for (int x = hf + 2 * KM; x < NP; x += 2) {
       const float* px = src + (int64_t)x * CROWS * PS;
       const float lx = px[D + 1];
       if (lx > 0.f) {
