@@ -169,7 +169,10 @@ struct DecodeArgs {
   // Requires units % 8 == 0.
   int xcd_map;
   // Sub-chunk assignment: 0 = wave k of a unit takes sub-chunks k, k + nw,
-  // k + 2 nw, ... (nw waves per unit); 1 = each wave takes one contiguous run.
+  // k + 2 nw, ... (nw waves per unit); 1 = each wave takes one contiguous run;
+  // 2 = each workgroup takes one contiguous run, which its four waves share
+  // out in turn (k, k + 4, ...).  With the head split (G >= 4) 1 and 2 both
+  // give each workgroup one run.
   int contig;
   const void* q;
   const float* tq;
