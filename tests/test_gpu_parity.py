@@ -362,11 +362,27 @@ def test_decode_step_prepared_query_blocks(bits):
 
 
 @pytest.mark.parametrize("G", [1, 2])
-def test_decode_step_prepared_query_blocks_fp32_paged(G):
-    """The prep-kernel path with fp32 inputs (query and new entry converted in
-    the prep kernel) and on a paged cache with shuffled pages."""
+def test_decode_step_one_workgroup_per_cu_fp32_paged(G):
+    """Few units at G <= 2: one quantized workgroup per CU on a contiguous run
+    (workgroup 0 of each unit lighter), window workgroups last; with fp32
+    inputs and on a paged cache with shuffled pages."""
     _run_steps(_gqa_workload(4000, G=G, io="fp32"), [3500, 2200], 3, check_every=1)
     _run_steps(_gqa_workload(4000, G=G), [3500, 2200], 3, check_every=1, page=128)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_decode_step_one_workgroup_per_cu_short(G):
+    """Short contexts in the one-workgroup-per-CU layout: a single quantized
+    workgroup per unit, and runs of a sub-chunk or none."""
+    _run_steps(_gqa_workload(800, G=G), [400, 130, 0], 4, check_every=1)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_decode_step_prep_kernel_many_units(G):
+    """More units than half the CUs at G <= 2 (72 KV heads x 2 sequences): the
+    query is prepared once per unit in the prep kernel and the grid is
+    oversubscribed instead."""
+    _run_steps(_gqa_workload(3000, G=G, n_kv=72), [2600, 2100], 2, check_every=1)
 
 
 def test_decode_step_same_cache_as_append():
