@@ -529,8 +529,11 @@ extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32
     if (nsub > max_sub) max_sub = nsub;
     const int e = (L < S ? L : S) + (L > sq ? L - sq : 0) + n_new[i];
     if (e > win) win = e;
-    const int nf = squant_of(L + n_new[i], S, c->cfg.recent, c->cfg.flush) - sq;
-    if (nf > a.n_flush) a.n_flush = nf;
+    // positions [sq, sq1) leave the window: ring entries below L, new ones above
+    const int sq1 = squant_of(L + n_new[i], S, c->cfg.recent, c->cfg.flush);
+    const int nr = (sq1 < L ? sq1 : L) - sq, nw = sq1 - (sq > L ? sq : L);
+    if (nr > a.n_flush_ring) a.n_flush_ring = nr;
+    if (nw > a.n_flush_new) a.n_flush_new = nw;
   }
   a.win_max = win;
   const int cap = chunk_split_cap(n_seq * c->cfg.n_kv_heads * a.RT);

@@ -23,7 +23,9 @@ struct ChunkSeqs {
 struct ChunkArgs {
   Planes pl;
   Geometry g;
-  int layer, n_seq, C, RT, n_splits, xcd_map, n_tok, win_max, n_flush;
+  // positions leaving the window per (sequence, KV head), at most: ring entries
+  // (quantized in the prep launch) and new entries (in a launch of their own)
+  int layer, n_seq, C, RT, n_splits, xcd_map, n_tok, win_max, n_flush_ring, n_flush_new;
   const void* k;
   const void* v;
   const void* q;

@@ -169,8 +169,27 @@ __device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
 
 // ---------------------------------------------------------------- prep
 
+template <bool B3>
+__device__ void flush_entry(const ChunkArgs& a, int si, int h, int p);
+
+// Blocks x < C: the queries and the new entry of chunk position x.  Blocks
+// x >= C: ring entry squant(L) + x - C leaves the window in this step and is
+// quantized now; the attention reads the window entries from the ring and
+// masks their positions in the code planes, so this can precede it.
 template <int IO_BF16>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
+  if ((int)blockIdx.x >= a.C) {
+    const int si = blockIdx.z, L = a.s.len[si];
+    const int sq1 = squant_of(L + a.s.n_new[si], a.g.S, a.g.R, a.g.F);
+    const int p = a.s.squant[si] + (int)blockIdx.x - a.C;
+    if (p < (sq1 < L ? sq1 : L)) {
+      if (a.g.bits == 3)
+        flush_entry<true>(a, si, blockIdx.y, p);
+      else
+        flush_entry<false>(a, si, blockIdx.y, p);
+    }
+    return;
+  }
   __shared__ float qv[8][D];
   __shared__ float hs[2][8][D];
   __shared__ float qs[8][D];
@@ -835,17 +854,15 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(ChunkArgs a) {
   }
 }
 
-// One position p = squant(L) + blockIdx.x of [squant(L), squant(L + n)):
-// threads 0..127 quantize its key entry, 128..255 its value entry.
+// Quantizes position p of sequence si, KV head h, as it leaves the window:
+// threads 0..127 its key entry, 128..255 its value entry.  Ring entries
+// (p < L) are read from the ring, new entries from the prep kernel's output.
 template <bool B3>
-__global__ __launch_bounds__(256) void chunk_flush_kernel(ChunkArgs a) {
+__device__ void flush_entry(const ChunkArgs& a, int si, int h, int p) {
   __shared__ QLds ql;
   const Geometry& g = a.g;
-  const int si = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
-  const int slot = a.s.slot[si], L = a.s.len[si], nn = a.s.n_new[si];
-  const int sq0 = a.s.squant[si], sq1 = squant_of(L + nn, g.S, g.R, g.F);
-  const int p = sq0 + blockIdx.x;
-  if (p >= sq1) return;
+  const int tid = threadIdx.x;
+  const int slot = a.s.slot[si], L = a.s.len[si];
   const int i = tid & (D - 1);
   const bool is_v = tid >= D;
   const int64_t wunit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
@@ -882,10 +899,21 @@ __global__ __launch_bounds__(256) void chunk_flush_kernel(ChunkArgs a) {
   }
 }
 
+// One new position p = max(squant(L), L) + blockIdx.x of those that leave the
+// window in this step, after the prep kernel has made its entry.
+template <bool B3>
+__global__ __launch_bounds__(256) void chunk_flush_kernel(ChunkArgs a) {
+  const int si = blockIdx.z, h = blockIdx.y;
+  const int L = a.s.len[si], sq0 = a.s.squant[si];
+  const int sq1 = squant_of(L + a.s.n_new[si], a.g.S, a.g.R, a.g.F);
+  const int p = (sq0 > L ? sq0 : L) + blockIdx.x;
+  if (p < sq1) flush_entry<B3>(a, si, h, p);
+}
+
 }  // namespace
 
 hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
-  dim3 pgrid(a.C, a.g.n_kv, a.n_seq);
+  dim3 pgrid(a.C + a.n_flush_ring, a.g.n_kv, a.n_seq);
   if (io_bf16)
     hipLaunchKernelGGL(chunk_prep_kernel<1>, pgrid, dim3(256), 0, st, a);
   else
@@ -926,8 +954,8 @@ hipError_t launch_chunk(ChunkArgs& a, int io_bf16, hipStream_t st) {
     hipLaunchKernelGGL((chunk_kernel<4, false>), grid, dim3(256), lds, st, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.n_flush > 0) {
-    const dim3 fgrid(a.n_flush, a.g.n_kv, a.n_seq);
+  if (a.n_flush_new > 0) {
+    const dim3 fgrid(a.n_flush_new, a.g.n_kv, a.n_seq);
     if (a.g.bits == 3)
       hipLaunchKernelGGL(chunk_flush_kernel<true>, fgrid, dim3(256), 0, st, a);
     else
