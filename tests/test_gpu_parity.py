@@ -609,6 +609,15 @@ def _gqa_workload(L, *, G, n_kv=2, io="bf16"):
     return synth.Workload(12, "chunk", 1, n_kv * G, n_kv, 1, L, (2,), 4, 128, 1, 0.01, 0.99, io)
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_chunk_step_new_entries_leave_at_once(bits):
+    """A recent window smaller than the chunk (S 4, R 4, F 2): ring entries
+    leave the window in the prep launch, and most of each chunk's own entries
+    are quantized in the same step by the flush launch after the prep."""
+    _run_chunks(synth.WORKLOADS[1], [300, 40], [[16, 16], [16, 9], [5, 16], [1, 2]], S=4, R=4, F=2,
+                bits=bits)
+
+
 def test_chunk_step_fp32_inputs():
     """fp32 inputs, 4 query heads on 1 KV head: prefill 700, then 16-position
     chunks and a short one (every chunk crosses quantized flushes)."""
