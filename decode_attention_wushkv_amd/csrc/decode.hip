@@ -1004,8 +1004,6 @@ __global__ __launch_bounds__(256) void prep_kernel(DecodeArgs a) {
 }
 
 
-// PREP: the query block comes from the prep kernel (else every workgroup
-// prepares the query itself).
 // First sub-chunk (relative) of workgroup j's run when one workgroup per CU
 // shares out nsub sub-chunks: workgroup 0 weighs LIGHT / 16 of the others.
 constexpr int LIGHT = 14;
@@ -1015,6 +1013,8 @@ __device__ __forceinline__ int run_start(int64_t nsub, int j, int n) {
   return (int)((nsub * (LIGHT + 16 * (int64_t)(j - 1))) / total);
 }
 
+// PREP: the query block comes from the prep kernel (else every workgroup
+// prepares the query itself).
 template <int IO_BF16, int BITS, int G, bool PREP>
 __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
