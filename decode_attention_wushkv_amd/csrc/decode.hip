@@ -1300,11 +1300,15 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     slots = cus * (per > 0 ? per : 1);
   }
-  // Query preparation: in every workgroup for long single launches (it then
-  // hides under the streaming), else once per unit in the prep kernel, with
-  // the grid oversubscribed ~4.5x so that the dispatcher balances workgroups
-  // of unequal length (ragged batches, many units) and the window workgroup's
-  // chain stays short.
+  // Three layouts, chosen per launch:
+  //  - G <= 2 with at most half as many units as CUs: one quantized
+  //    workgroup per CU (below), query preparation in every workgroup;
+  //  - otherwise, for long single launches with few units: the grid fills the
+  //    resident capacity once, query preparation in every workgroup;
+  //  - otherwise the query is prepared once per unit in the prep kernel and
+  //    the grid is oversubscribed ~4.5x, so that the dispatcher balances
+  //    workgroups of unequal length (ragged batches, many units) and the
+  //    window workgroup's chain stays short.
   const int units = a.n_seq * a.g.n_kv;
   bool prep = false;
   if (!SplitCfg<BITS, G>::HS && 2 * units <= cus) {
