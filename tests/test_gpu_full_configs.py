@@ -3,7 +3,8 @@ the launch configuration the benchmark times:
 
   * qwen3-8b-36L-b32-ragged4k-16k  36 layers, 32 sequences of lengths
     U[4096, 16384], 32 query / 8 KV heads, 2-bit;
-  * mha-32L-32kv-128k              32 layers x 32 KV heads, 131072 positions;
+  * mha-32L-32kv-128k              32 layers x 32 KV heads, 131072 positions,
+    at 2 bits and (last layer) at 3 and 4 bits;
   * qwen3-32b-64L-b8-prefill64k    64 layers, 8 sequences x 65536 prefill
     positions, 64 query / 8 KV heads, at 2 and 4 bits.
 
@@ -117,6 +118,14 @@ def test_full_mha_128k():
     """32 KV heads at 131072 positions: two layers, two sampled units each."""
     w = synth.WORKLOADS[3]
     _run(3, 2, [0, w.n_layers - 1], 2, seed=31)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_full_mha_128k_wider_codes(bits):
+    """The 128K MHA workload at 3 and 4 bits (64-position sub-chunks, one
+    quantized workgroup per CU): the last layer, two sampled units."""
+    w = synth.WORKLOADS[3]
+    _run(3, bits, [w.n_layers - 1], 2, seed=33 + bits)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
