@@ -344,6 +344,10 @@ struct CBuf {
   uint32_t vh[BITS == 3 ? 8 : 1];
 };
 
+// Non-temporal load of one code-plane word: the codes are read once per
+// step, so they stream past the caches (as in the split kernel).
+__device__ __forceinline__ uint32_t ntl(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
 template <int BITS>
 __device__ __forceinline__ void cload(CBuf<BITS>& b, const ChunkArgs& a, const QMap& qm, int pbase) {
   const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
@@ -355,29 +359,29 @@ __device__ __forceinline__ void cload(CBuf<BITS>& b, const ChunkArgs& a, const Q
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if constexpr (BITS == 4) {
-        b.kc[cb][ks][0] = kw[8 * ks + 2 * grp];
-        b.kc[cb][ks][1] = kw[8 * ks + 2 * grp + 1];
+        b.kc[cb][ks][0] = ntl(kw + (8 * ks + 2 * grp));
+        b.kc[cb][ks][1] = ntl(kw + (8 * ks + 2 * grp + 1));
       } else {
-        b.kc[cb][ks][0] = kw[4 * ks + grp];
+        b.kc[cb][ks][0] = ntl(kw + (4 * ks + grp));
       }
       // three bits: the high plane (bytes [32, 48)) word of this group
-      if constexpr (BITS == 3) b.kh[cb][ks] = kw[8 + 2 * ks + (grp >> 1)];
+      if constexpr (BITS == 3) b.kh[cb][ks] = ntl(kw + (8 + 2 * ks + (grp >> 1)));
     }
-    b.ksz[cb] = a.pl.ksz[r];
-    b.vsz[cb] = a.pl.vsz[r];
+    b.ksz[cb] = ntl(a.pl.ksz + r);
+    b.vsz[cb] = ntl(a.pl.vsz + r);
   }
   if constexpr (BITS == 2) {
     const uint32_t* vw = (const uint32_t*)(a.pl.vcode + ((row >> 6) * D + m16) * 16) + grp;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) b.vc[db][0] = vw[db * 16 * 4];
+    for (int db = 0; db < 8; ++db) b.vc[db][0] = ntl(vw + (db * 16 * 4));
   } else if constexpr (BITS == 4) {
     // 32 positions per row: this group's 16 in block (row / 32) + grp / 2
     const uint32_t* vw =
         (const uint32_t*)(a.pl.vcode + (((row >> 5) + (grp >> 1)) * D + m16) * 16) + 2 * (grp & 1);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      b.vc[db][0] = vw[db * 16 * 4];
-      b.vc[db][1] = vw[db * 16 * 4 + 1];
+      b.vc[db][0] = ntl(vw + (db * 16 * 4));
+      b.vc[db][1] = ntl(vw + (db * 16 * 4 + 1));
     }
   } else {
     // 128-position block: low-plane rows sel = 0, 1 and the high-plane row,
@@ -388,8 +392,8 @@ __device__ __forceinline__ void cload(CBuf<BITS>& b, const ChunkArgs& a, const Q
     const uint32_t* hw = (const uint32_t*)(a.pl.vcode + ((blk * 3 + 2) * D + m16) * 16 + 8 * sel) + (grp >> 1);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      b.vc[db][0] = vw[db * 16 * 4];
-      b.vh[db] = hw[db * 16 * 4];
+      b.vc[db][0] = ntl(vw + (db * 16 * 4));
+      b.vh[db] = ntl(hw + (db * 16 * 4));
     }
   }
 }
