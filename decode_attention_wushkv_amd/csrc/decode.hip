@@ -356,18 +356,22 @@ __device__ __forceinline__ uint2 buf_b64(__amdgpu_buffer_rsrc_t r, int voff, int
 // Issues the loads of the sub-chunk at position pbase.  Buffer loads: the
 // sub-chunk's base addresses are wave-uniform (resources in scalar
 // registers) and every lane offset is loop-invariant, so a load needs no
-// per-sub-chunk vector address registers.
+// per-sub-chunk vector address registers.  pbase < 0 issues the same loads
+// from `spare` instead (any 16-byte aligned 8 KB the workgroup has just read,
+// so served by L2): the prefetch past a wave's last sub-chunk stays
+// unconditional without re-reading codes from HBM.
 template <int BITS, int G, int CP>
 __device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a, const QMap& qm,
-                                         int pbase) {
+                                         int pbase, const uint8_t* spare) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
-  const int64_t row = qrow_read(qm, pbase);
+  const bool past = pbase < 0;
+  const int64_t row = qrow_read(qm, past ? 0 : pbase);
   // key codes: C::TW positions of C::CB bytes (3 bits: low plane in bytes
   // [0, 32) of a position, high plane in [32, 48))
-  const auto rk = wave_rsrc(a.pl.kcode + row * C::CB, C::TW * C::CB);
-  const auto rks = wave_rsrc(a.pl.ksz + row, C::TW * 4);
-  const auto rvs = wave_rsrc(a.pl.vsz + row, C::TW * 4);
+  const auto rk = wave_rsrc(past ? spare : a.pl.kcode + row * C::CB, C::TW * C::CB);
+  const auto rks = wave_rsrc(past ? (const void*)spare : (const void*)(a.pl.ksz + row), C::TW * 4);
+  const auto rvs = wave_rsrc(past ? (const void*)spare : (const void*)(a.pl.vsz + row), C::TW * 4);
   const int ko = tq * C::CB + half * (BITS == 3 ? 16 : C::CB / 2);
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
@@ -382,13 +386,13 @@ __device__ __forceinline__ void load_sub(SubBuf<BITS, G>& b, const DecodeArgs& a
   // high-plane row (the sub-chunk's half at byte 8 sel)
   if constexpr (BITS == 3) {
     const int sel = (int)((row >> 6) & 1);
-    const auto rv = wave_rsrc(a.pl.vcode + (row >> 7) * 3 * D * 16, 3 * D * 16);
+    const auto rv = wave_rsrc(past ? spare : a.pl.vcode + (row >> 7) * 3 * D * 16, 3 * D * 16);
     b.vc[0][0] = buf_b128<CP>(rv, lane * 16, sel * D * 16);
     b.vc[0][1] = buf_b128<CP>(rv, lane * 16 + 64 * 16, sel * D * 16);
     b.vh[0] = buf_b64<CP>(rv, lane * 16 + 2 * D * 16, 8 * sel);
     b.vh[1] = buf_b64<CP>(rv, lane * 16 + 2 * D * 16 + 64 * 16, 8 * sel);
   } else {
-    const auto rv = wave_rsrc(a.pl.vcode + (row / C::VB) * D * 16, C::NBW * D * 16);
+    const auto rv = wave_rsrc(past ? spare : a.pl.vcode + (row / C::VB) * D * 16, C::NBW * D * 16);
 #pragma unroll
     for (int k = 0; k < C::NBW; ++k) {
       b.vc[k][0] = buf_b128<CP>(rv, lane * 16 + k * D * 16, 0);
@@ -600,9 +604,9 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
 // issued before, would then wait for these codes too.
 template <int BITS, int G, int CP = CPOL_NT>
 __device__ __forceinline__ void load_first(SubBuf<BITS, G>& A, const DecodeArgs& a, const QMap& qm,
-                                           int c0, int c_end) {
+                                           int c0, int c_end, const uint8_t* spare) {
   using C = SplitCfg<BITS, G>;
-  load_sub<BITS, G, CP>(A, a, qm, (c0 < c_end ? c0 : 0) * C::TW);
+  load_sub<BITS, G, CP>(A, a, qm, c0 < c_end ? c0 * C::TW : -1, spare);
 }
 
 // One wave, G query heads (scales qsc, digit words qdw): sub-chunks c0,
@@ -612,7 +616,7 @@ __device__ __forceinline__ void load_first(SubBuf<BITS, G>& A, const DecodeArgs&
 template <int BITS, int G, int CP = CPOL_NT>
 __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stride, int c_end, int lo,
                            int hi, const float* qsc, const uint32_t* qdw, uint32_t* wsm, float* out,
-                           int64_t hstride, SubBuf<BITS, G>& A) {
+                           int64_t hstride, SubBuf<BITS, G>& A, const uint8_t* spare) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1;
   uint4 qd[C::QREG ? G : 1][8];
@@ -639,18 +643,18 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
   SubBuf<BITS, G> B;
   int c = c0;
   // The next sub-chunk's loads are issued unconditionally (past the end they
-  // re-read the current one, from L2): a conditional load leaves the
+  // read the spare block, from L2): a conditional load leaves the
   // compiler's wait counts conservative at the join, and it would then wait
   // for the prefetch before processing the current sub-chunk.
   while (c < c_end) {
     int cn = c + stride;
-    load_sub<BITS, G, CP>(B, a, qm, (cn < c_end ? cn : c) * C::TW);
+    load_sub<BITS, G, CP>(B, a, qm, cn < c_end ? cn * C::TW : -1, spare);
     __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for A
     process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
     if (c >= c_end) break;
     cn = c + stride;
-    load_sub<BITS, G, CP>(A, a, qm, (cn < c_end ? cn : c) * C::TW);
+    load_sub<BITS, G, CP>(A, a, qm, cn < c_end ? cn * C::TW : -1, spare);
     __builtin_amdgcn_sched_barrier(0);
     process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     c = cn;
@@ -1078,6 +1082,9 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
   const int64_t unit = ((int64_t)a.layer * g.max_batch + slot) * g.n_kv + h;
   const QMap qm = qmap_of(g, a.layer, slot, h);
   const int qbase = si * g.n_q + h * G;
+  // this head's T_K^{-T} (64 KB, read by the query preparation): the target
+  // of the prefetches past a wave's last sub-chunk
+  const uint8_t* spare = (const uint8_t*)(a.tq + (int64_t)h * D * D);
 
   // the quantized region [S, sq) in sub-chunks of TW positions, spread over
   // the 4 n_splits waves of this (sequence, KV head): interleaved (wave k
@@ -1149,19 +1156,19 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
       if constexpr (PREP) {
         PrepIn<G> pin;
         prep_load<G>(a, u, pin);
-        load_first<BITS, C::GW, 0>(A, a, qm, c0, cend);
+        load_first<BITS, C::GW, 0>(A, a, qm, c0, cend, spare);
         prep_store<BITS, G>(sm, pin);
       } else {
         QueryIn<G> qin;
         compensate_load<IO_BF16, G>(a, h, si, qin);
-        load_first<BITS, C::GW, 0>(A, a, qm, c0, cend);
+        load_first<BITS, C::GW, 0>(A, a, qm, c0, cend, spare);
         compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
       }
       float* dst = a.wsp + ((int64_t)(qbase + w * C::GW) * nsp + j) * PS;
       quant_wave<BITS, C::GW, 0>(a, qm, c0, cstride, cend, lo, hi,
                               (const float*)(sm + C::O_QSC) + w * C::GW * 4,
                               sm + C::O_QD + w * C::GW * 16 * DIGP, sm + C::O_UNION + w * C::WAVE,
-                              dst, (int64_t)nsp * PS, A);
+                              dst, (int64_t)nsp * PS, A, spare);
       direct = true;
     } else {
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wi = 4 * j + w;
@@ -1184,18 +1191,18 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
       if constexpr (PREP) {
         PrepIn<G> pin;
         prep_load<G>(a, u, pin);
-        load_first<BITS, G>(A, a, qm, c0, cend);
+        load_first<BITS, G>(A, a, qm, c0, cend, spare);
         prep_store<BITS, G>(sm, pin);
       } else {
         QueryIn<G> qin;
         compensate_load<IO_BF16, G>(a, h, si, qin);
-        load_first<BITS, G>(A, a, qm, c0, cend);
+        load_first<BITS, G>(A, a, qm, c0, cend, spare);
         compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
       }
       uint32_t* wbase = sm + C::O_UNION;
       float* part = (float*)(wbase + 4 * C::WAVE);  // [4 waves][G][D + 2]
       quant_wave<BITS, G>(a, qm, c0, cstride, cend, lo, hi, (const float*)(sm + C::O_QSC),
-                          sm + C::O_QD, wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A);
+                          sm + C::O_QD, wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A, spare);
       __syncthreads();
       // merge the four wave partials (a wave without sub-chunks has l = 0)
       const int i = tid & (D - 1), hf = tid >> 7;
