@@ -24,7 +24,7 @@ WUSHKV_MAX_SEQ_PER_CALL = 128
 # Symbols the header declares (checked by the test-suite against the .so).
 EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
-    "wushkv_reset_seq", "wushkv_get_len", "wushkv_append", "wushkv_decode_workspace_bytes",
+    "wushkv_reset_seq", "wushkv_get_len", "wushkv_quantized_range", "wushkv_append", "wushkv_decode_workspace_bytes",
     "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events",
     "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_set_block_table",
     "wushkv_chunk_workspace_bytes", "wushkv_chunk_step", "wushkv_status_str",
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_reset_seq.argtypes = [P, i32]
     L.wushkv_get_len.restype = ctypes.c_int
     L.wushkv_get_len.argtypes = [P, i32, i32, i32p, i32p]
+    L.wushkv_quantized_range.restype = ctypes.c_int
+    L.wushkv_quantized_range.argtypes = [P, i32, i32p, i32p]
     L.wushkv_append.restype = ctypes.c_int
     L.wushkv_append.argtypes = [P, i32, i32, i32p, i32p, P, P, P, P]
     L.wushkv_decode_workspace_bytes.restype = _U64
@@ -170,6 +172,15 @@ def wushkv_get_len(cache: int, layer: int, slot: int):
     _check(lib().wushkv_get_len(ctypes.c_void_p(cache), int(layer), int(slot), ctypes.byref(L),
                                 ctypes.byref(sq)), "wushkv_get_len")
     return L.value, sq.value
+
+
+def wushkv_quantized_range(cache: int, length: int):
+    """(begin, end): the positions quantized at sequence length `length`."""
+    b = ctypes.c_int32()
+    e = ctypes.c_int32()
+    _check(lib().wushkv_quantized_range(ctypes.c_void_p(cache), int(length), ctypes.byref(b),
+                                        ctypes.byref(e)), "wushkv_quantized_range")
+    return b.value, e.value
 
 
 def wushkv_append(cache: int, layer: int, slots, n_new, k_ptr: int, v_ptr: int, tk_ptr: int,

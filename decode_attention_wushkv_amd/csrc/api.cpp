@@ -188,6 +188,14 @@ extern "C" wushkv_status wushkv_get_len(const wushkv_cache* c, int32_t layer, in
   return WUSHKV_OK;
 }
 
+extern "C" wushkv_status wushkv_quantized_range(const wushkv_cache* c, int32_t len,
+                                                int32_t* begin, int32_t* end) {
+  if (!c || !begin || !end || len < 0) return WUSHKV_EINVAL;
+  *begin = c->cfg.sink;
+  *end = squant_of(len, c->cfg.sink, c->cfg.recent, c->cfg.flush);
+  return WUSHKV_OK;
+}
+
 static Planes planes_of(const wushkv_cache* c) {
   Planes p;
   uint8_t* a = c->arena;

@@ -46,7 +46,7 @@ typedef enum {
   WUSHKV_EINVAL = 1,       /* null/misaligned pointer, index out of range, duplicate slot, bad config value */
   WUSHKV_ECAPACITY = 2,    /* an append would make a sequence longer than ctx_cap */
   WUSHKV_EWORKSPACE = 3,   /* decode workspace smaller than wushkv_decode_workspace_bytes() */
-  WUSHKV_EUNSUPPORTED = 4, /* valid but not built: head_dim != 128, bits not in {2, 4}, too many sequences per call */
+  WUSHKV_EUNSUPPORTED = 4, /* valid but not built: head_dim != 128, bits not in {2, 3, 4}, too many sequences per call */
   WUSHKV_EDEVICE = 5       /* the HIP runtime reported an error when launching */
 } wushkv_status;
 
@@ -74,7 +74,7 @@ typedef struct {
   int32_t n_q_heads;    /* query heads; query head j reads KV head j / (n_q/n_kv) */
   int32_t n_kv_heads;   /* KV heads (n_q_heads % n_kv_heads == 0)                 */
   int32_t head_dim;     /* d; must be 128                                         */
-  int32_t bits;         /* code width b: 2 or 4                                   */
+  int32_t bits;         /* code width b: 2, 3 or 4                                */
   int32_t sink;         /* S_sink >= 0: first positions kept in bfloat16          */
   int32_t recent;       /* S_keep >= 0: newest positions kept in bfloat16         */
   int32_t flush;        /* S_flush >= 1: quantize in multiples of this            */
@@ -97,12 +97,26 @@ typedef struct {
  * n_kv_heads + head.  Positions p are absolute (0-based) in the sequence.
  *
  *   kcode  uint8  [unit][cpos][code_bytes]         token-major key codes;
- *                 element i of position p sits in byte (i*bits)/8 at bit
- *                 (i*bits)%8 of that position's code_bytes = d*bits/8 bytes.
+ *                 bits 2, 4: element i of position p sits in byte (i*bits)/8
+ *                 at bit (i*bits)%8 of that position's code_bytes = d*bits/8
+ *                 bytes.
  *   vcode  uint8  [unit][ctx_blocks][d][16]        value codes, dim-major per
- *                 block of vblock = 128/bits positions: element i of position
- *                 p sits in row i of block p/vblock, byte ((p%vblock)*bits)/8,
- *                 bit ((p%vblock)*bits)%8.
+ *                 block of vblock = 128/bits positions (bits 2, 4): element i
+ *                 of position p sits in row i of block p/vblock, byte
+ *                 ((p%vblock)*bits)/8, bit ((p%vblock)*bits)%8.
+ *
+ * 3-bit codes (the paper evaluates 2, 3 and 4 bits, section 5.2; appendix
+ * B.3 for the 2^b levels) are stored as two bit planes.  The low plane holds
+ * the low two bits of every code in the 2-bit packing, the high plane the
+ * third bit in the order hi(e) = 32 (e / 32) + 4 ((e % 16) / 2) +
+ * 2 ((e % 32) / 16) + e % 2: element e's bit is bit hi(e) % 32 of 32-bit word
+ * hi(e) / 32 of a 16-byte high-plane row.
+ *   kcode  [unit][cpos][48]: bytes 0..31 the low plane of the 128 elements,
+ *          bytes 32..47 their high plane (code_bytes = 48).
+ *   vcode  [unit][ctx_blocks][3][d][16] with vblock = 128 positions: per
+ *          dimension, low-plane rows of positions 0..63 and 64..127 of the
+ *          block (2-bit packing), then the high-plane row of the block's 128
+ *          positions (element = position in the block).
  *   ksz,vsz uint16[unit][cpos][2]                  binary16 {scale, zero} of
  *                 the key / value group of each quantized position.
  *   ksink,vsink bfloat16 [unit][sink][d]           positions [0, sink).
@@ -193,6 +207,16 @@ wushkv_status wushkv_reset_seq(wushkv_cache* cache, int32_t slot);
 /* Host-side length L of (layer, slot) and its quantized-region end squant(L). */
 wushkv_status wushkv_get_len(const wushkv_cache* cache, int32_t layer, int32_t slot,
                              int32_t* len, int32_t* squant);
+
+/* Host only.  The positions [*begin, *end) that are quantized once a sequence
+ * of this cache reaches length len >= 0 (paper page, section 4.4: the sink
+ * and the newest positions stay in full precision; the region grows in
+ * multiples of S_flush): *begin = sink and *end = squant(len) (*end ==
+ * *begin when nothing is quantized).  A paged cache's caller maps the pages
+ * that hold [*begin, *end) of the length a call leaves before making it (see
+ * wushkv_set_block_table).  EINVAL for a null argument or len < 0. */
+wushkv_status wushkv_quantized_range(const wushkv_cache* cache, int32_t len, int32_t* begin,
+                                     int32_t* end);
 
 /*
  * Append n_new[i] >= 0 positions to sequence slots[i] (distinct, i < n_seq <=

@@ -301,6 +301,11 @@ def cache_unit(keys, values, T, *, S: int, R: int, F: int, bits: int,
     kb = bf16(ktr)
     vb = bf16(values)
     amb = bf16_ambiguous(ktr, kabs)
+    # where the rounding is undecided, the other bfloat16 neighbour of T k is
+    # an equally correct stored value (NaN elsewhere)
+    band = np.ldexp(kabs, AMBIGUITY_BAND_LOG2)
+    lo_b, hi_b = bf16(ktr - band), bf16(ktr + band)
+    k_alt = np.where(amb, np.where(lo_b == kb, hi_b, lo_b), np.nan)
     sq = squant(L, S, R, F)
     qpos = np.arange(S, sq) if positions is None else np.asarray(positions)
     kcodes = np.full((L, d), 255, dtype=np.uint8)
@@ -320,9 +325,10 @@ def cache_unit(keys, values, T, *, S: int, R: int, F: int, bits: int,
             qv = quantize_rms(vb[qpos], bits, alpha)
         kcodes[qpos], ks[qpos], kz[qpos], ku[qpos] = qk["codes"], qk["s16"], qk["z16"], qk["u"]
         vcodes[qpos], vs[qpos], vz[qpos], vu[qpos] = qv["codes"], qv["s16"], qv["z16"], qv["u"]
-    return dict(L=L, S=S, squant=sq, k_bf16=kb, v_bf16=vb, k_ambiguous=amb,
+    return dict(L=L, S=S, squant=sq, k_bf16=kb, v_bf16=vb, k_ambiguous=amb, k_alt=k_alt,
                 kcodes=kcodes, ks16=ks, kz16=kz, ku=ku,
-                vcodes=vcodes, vs16=vs, vz16=vz, vu=vu, qpos=qpos)
+                vcodes=vcodes, vs16=vs, vz16=vz, vu=vu, qpos=qpos,
+                bits=bits, p_lo=p_lo, p_hi=p_hi, alpha=alpha)
 
 
 def readback(unit) -> tuple[np.ndarray, np.ndarray]:

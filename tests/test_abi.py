@@ -309,3 +309,24 @@ def test_chunk_step_errors():
         assert wk.wushkv_chunk_step(h, 0, [0], [1], P, P, P, P, P, P, P, small - 1, check=False) == \
             wk.WUSHKV_EWORKSPACE
         wk.wushkv_cache_destroy(h)
+
+
+def test_quantized_range():
+    """The quantized positions [sink, S_quant(L)) by length, from section 4.4
+    (sink 4, recent 128, flush 1 / 16), computed by hand; the binding and
+    the device plumbing take the window rule from this call."""
+    import ctypes
+    h, _ = _fake_cache()
+    for L, want in [(0, 4), (1, 4), (132, 4), (133, 5), (1000, 872)]:
+        assert wk.wushkv_quantized_range(h, L) == (4, want)
+    b, e = ctypes.c_int32(), ctypes.c_int32()
+    assert wk.lib().wushkv_quantized_range(ctypes.c_void_p(h), -1, ctypes.byref(b),
+                                           ctypes.byref(e)) == wk.WUSHKV_EINVAL
+    assert wk.lib().wushkv_quantized_range(ctypes.c_void_p(h), 5, None,
+                                           ctypes.byref(e)) == wk.WUSHKV_EINVAL
+    wk.wushkv_cache_destroy(h)
+    h, _ = _fake_cache(sink=16, flush=16)
+    # 16 + 16 * floor((L - 128 - 16) / 16)
+    for L, want in [(144, 16), (159, 16), (160, 32), (1000, 864)]:
+        assert wk.wushkv_quantized_range(h, L) == (16, want)
+    wk.wushkv_cache_destroy(h)

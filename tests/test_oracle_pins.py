@@ -430,3 +430,23 @@ def test_quantize_rms_brute_force(bits):
             best = np.flatnonzero(d == d.min())
             want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
             assert r["codes"][g, i] == want
+
+
+def test_quantize_rms_worked_examples():
+    """Clip ends of the RMS codec pinned by hand-worked groups whose RMS is
+    exactly 2 (tests/golden/quantizer_rms.json; appendix B.3's grid from
+    -alpha to alpha scaled by the group's RMS).  A mean-centred deviation, a
+    divisor of n - 1 or a missing square root changes the stored scale of
+    group A; group C puts every even value on a level boundary (ties to the
+    even level)."""
+    import json
+    spec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quantizer_rms.json")))
+    rng = np.random.default_rng(12)
+    for g in spec["groups"]:
+        x = np.concatenate([np.full(n, v) for v, n in g["values"]])
+        assert x.size == 128
+        x = x[rng.permutation(128)]
+        r = oracle.quantize_rms(x, g["bits"], g["alpha"])
+        assert r["s16"] == g["s16"] and r["z16"] == g["z16"], g["name"]
+        want = dict((float(v), c) for v, c in g["codes"])
+        assert all(r["codes"][i] == want[float(x[i])] for i in range(128)), g["name"]
