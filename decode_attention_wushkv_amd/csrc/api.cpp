@@ -243,13 +243,13 @@ static Geometry geometry_of(const wushkv_cache* c) {
   return g;
 }
 
-// Distinct, in-range slots.
+// Distinct, in-range slots (n_seq <= MAXSEQ; no allocation).
 static bool slots_ok(const wushkv_cache* c, int32_t n_seq, const int32_t* slots) {
-  std::vector<char> seen((size_t)c->cfg.max_batch, 0);
   for (int i = 0; i < n_seq; ++i) {
-    int s = slots[i];
-    if (s < 0 || s >= c->cfg.max_batch || seen[s]) return false;
-    seen[s] = 1;
+    const int s = slots[i];
+    if (s < 0 || s >= c->cfg.max_batch) return false;
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == s) return false;
   }
   return true;
 }
@@ -393,6 +393,11 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
     for (int i = 0; i < n_seq; ++i)
       if (c->len[(size_t)layer * c->cfg.max_batch + slots[i]] + 1 > c->cfg.ctx_cap)
         return WUSHKV_ECAPACITY;
+  } else {
+    for (int i = 0; i < n_seq; ++i)
+      if (c->len[(size_t)layer * c->cfg.max_batch + slots[i]] < 1) return WUSHKV_EINVAL;
+  }
+  if (step) {
     if (step_as_chunk(c)) {
       int32_t ones[MAXSEQ];
       for (int i = 0; i < n_seq; ++i) ones[i] = 1;

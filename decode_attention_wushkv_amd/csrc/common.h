@@ -38,9 +38,13 @@ __host__ __device__ inline int max_chunks(int n_seq, int n_kv) {
 }
 
 // Fixed-point precision of the decode dot products: the compensated query
-// is held as QDIG signed base-16 digits and the softmax weights of a
-// 128-position sub-chunk as WDIG unsigned ones (16 bits each).
-constexpr int QDIG = 4;
+// is held as QDIG signed base-16 digits (24 bits) and the softmax weights of
+// a 128-position sub-chunk as WDIG unsigned ones (16 bits).  A score's error
+// is the query's rounding error dotted with the key's codes times its scale,
+// so it grows with the key's range; 16-bit queries exceeded the 2e-3 output
+// bar on keys scaled x30 or holding constant rows of 1024, 24 bits keep it
+// below.
+constexpr int QDIG = 6;
 constexpr int WDIG = 4;
 constexpr int DIGP = 8;  // query digit words per group of 8 dimensions (padded for 16-byte loads)
 

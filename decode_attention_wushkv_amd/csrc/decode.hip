@@ -9,7 +9,7 @@
 //           Every workgroup first compensates the G query heads of its KV
 //           head: q' = T_K^{-T} q, prescaled by log2(e)/sqrt(d); sigma =
 //           sum_i q'_i (the zero point factors out of a score:
-//           q'.(z + s c) = z sigma + s (q'.c)); q' also as a 16-bit
+//           q'.(z + s c) = z sigma + s (q'.c)); q' also as a 24-bit
 //           fixed-point vector in signed base-16 digits for v_dot8.
 //             quantized workgroups: each wave walks 128-position sub-chunks
 //             (64 at 4 bits) with the next sub-chunk's codes in flight.
@@ -161,7 +161,6 @@ struct SplitCfg {
   static constexpr int NG = TW / GS;           // value-row words per sub-chunk (8)
   static constexpr int WGW = SPLIT2 ? 2 * WDIG : WDIG;  // digit words per row word
   static constexpr int WGP = (WGW + 3) / 4 * 4;            // ... padded to 16 bytes
-  static constexpr bool QREG = G <= 2;         // query digits held in registers
   // G >= 4: head split (the four waves of a quantized workgroup walk the same
   // sub-chunks, GW query heads each)
   static constexpr bool HS = G >= 4;
@@ -257,12 +256,12 @@ __device__ __forceinline__ void compensate_query(const DecodeArgs& a, int h, int
   }
   block_reduce_sum_max<G>(v, red);
   // fixed point: qi = rint(q' S_q), |qi| <= QMAX; balanced base-16 digits
-  float qsum_h[G];
+  int qsum_h[G];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     const float maxabs = v[G + gg];
     const float sq = maxabs > 0.f ? (float)QMAX / maxabs : 1.f;
-    int qi = (int)rintf(q[gg] * sq);
+    int qi = (int)rint((double)q[gg] * (double)sq);
     qi = qi > QMAX ? QMAX : (qi < -QMAX ? -QMAX : qi);
     if (hf == 0) {
       qf[gg * D + i] = q[gg];
@@ -275,15 +274,17 @@ __device__ __forceinline__ void compensate_query(const DecodeArgs& a, int h, int
       }
       dig[((QDIG - 1) * G + gg) * D + i] = (int8_t)r;
     }
-    // sums of qi over dimensions [0, 64) and [64, 128): waves 0 and 1
-    qsum_h[gg] = hf ? 0.f : (float)qi;
-    qsum_h[gg] = wave_sum(qsum_h[gg]);
+    // sums of qi over dimensions [0, 64) and [64, 128) (waves 0 and 1), exact
+    // in int32 (|qi| < 2^23), stored as floats for the 4-bit code offset
+    qsum_h[gg] = hf ? 0 : qi;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) qsum_h[gg] += __shfl_xor(qsum_h[gg], o);
     if (tid == 0) {
       qsc[gg * 4] = v[gg];
       qsc[gg * 4 + 1] = 1.f / sq;
     }
-    if (tid == 0) qsc[gg * 4 + 2] = qsum_h[gg];
-    if (tid == 64) qsc[gg * 4 + 3] = qsum_h[gg];
+    if (tid == 0) qsc[gg * 4 + 2] = (float)qsum_h[gg];
+    if (tid == 64) qsc[gg * 4 + 3] = (float)qsum_h[gg];
   }
   __syncthreads();
   // digit words: group x / DIGP of 8 dimensions, digit k = x % DIGP; nibble n
@@ -407,27 +408,83 @@ struct QueryRegs {
 
 // Scores, weights and value accumulation of one sub-chunk; folds the result
 // into the wave's running (M, Lrun, O) (online softmax across sub-chunks).
+// Nibble word x (0..7) of a lane's half position: the codes of the 8
+// dimensions that digit group x of the query covers, as signed or unsigned
+// 4-bit lanes for v_dot8.
 template <int BITS, int G>
+__device__ __forceinline__ int code_nibbles(const SubBuf<BITS, G>& b, int r, int x) {
+  using C = SplitCfg<BITS, G>;
+  const uint4 k0 = b.kc[r][0];
+  const uint32_t d0[4] = {k0.x, k0.y, k0.z, k0.w};
+  if constexpr (BITS == 2) {
+    // x = 2 w + parity: parity 0 takes the even dimensions of code word w
+    const uint32_t dw = d0[x >> 1];
+    return (int)((x & 1) ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u));
+  } else if constexpr (BITS == 3) {
+    // low two bits as at 2 bits, high bit from high-plane word w / 2 at
+    // shift k = 2 (w & 1) + parity (the plane's element order)
+    const uint32_t dw = d0[x >> 1];
+    const uint32_t hw = (x >> 2) ? b.kh[r].y : b.kh[r].x;
+    const int k = (((x >> 1) & 1) << 1) | (x & 1);
+    const uint32_t lo2 = (x & 1) ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u);
+    return (int)(lo2 | (((hw >> k) & 0x11111111u) << 2));
+  } else {
+    static_assert(C::KQ == 2, "4-bit positions take two 16-byte words per lane");
+    const uint4 k1 = b.kc[r][1];
+    const uint32_t d1[4] = {k1.x, k1.y, k1.z, k1.w};
+    return (int)((x < 4 ? d0[x & 3] : d1[x & 3]) ^ 0x88888888u);  // code - 8 as a signed nibble
+  }
+}
+
+// QREG (one query head): the query's digit words are held in registers qd
+// (16 words per lane, loaded once per wave); otherwise read from LDS per
+// digit group.  At one wave per SIMD the LDS reads' latency is not hidden.
+template <int BITS, int G, bool QREG>
 __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase, int lo, int hi,
-                                            const uint4 (*qd)[8], const uint32_t* qdw,
+                                            const uint4 (*qd)[2], const uint32_t* qdw,
                                             const QueryRegs* qr, uint32_t* wsm, float* M,
                                             float* Lrun, float* Zrun, float (*O)[2]) {
   using C = SplitCfg<BITS, G>;
   const int lane = threadIdx.x & 63, half = lane & 1, tq = lane >> 1;
 
-  // ---- scores (log2 domain); -inf outside [lo, hi)
+  // ---- scores (log2 domain); -inf outside [lo, hi).  Per digit group x of 8
+  // dimensions the query's QDIG digit words come from LDS once and meet the
+  // codes of every row; one accumulator per (row, head, digit).
+  int acc[C::ROWS][G][QDIG];
+#pragma unroll
+  for (int r = 0; r < C::ROWS; ++r)
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+      for (int k = 0; k < QDIG; ++k) acc[r][gg][k] = 0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    int X[C::ROWS];
+#pragma unroll
+    for (int r = 0; r < C::ROWS; ++r) X[r] = code_nibbles<BITS, G>(b, r, x);
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      uint4 L0, L1;
+      if constexpr (QREG) {
+        L0 = qd[x][0];
+        L1 = qd[x][1];
+      } else {
+        const uint4* qx = (const uint4*)(qdw + (gg * 16 + half * 8 + x) * DIGP);
+        L0 = qx[0];
+        L1 = qx[1];
+      }
+      const uint32_t Lk[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
+#pragma unroll
+      for (int r = 0; r < C::ROWS; ++r)
+#pragma unroll
+        for (int k = 0; k < QDIG; ++k)
+          acc[r][gg][k] = __builtin_amdgcn_sdot8(X[r], (int)Lk[k], acc[r][gg][k], false);
+    }
+  }
   float sc[C::ROWS][G];
   float vs[C::ROWS], vz[C::ROWS];
 #pragma unroll
   for (int r = 0; r < C::ROWS; ++r) {
-    uint32_t d[4 * C::KQ];
-#pragma unroll
-    for (int q = 0; q < C::KQ; ++q) {
-      d[4 * q] = b.kc[r][q].x;
-      d[4 * q + 1] = b.kc[r][q].y;
-      d[4 * q + 2] = b.kc[r][q].z;
-      d[4 * q + 3] = b.kc[r][q].w;
-    }
     const int p = pbase + 32 * r + tq;
     const bool ok = p >= lo && p < hi;
     const float ks = f16_to_f32(b.ksz[r] & 0xFFFFu), kz = f16_to_f32(b.ksz[r] >> 16);
@@ -436,38 +493,15 @@ __device__ __forceinline__ void process_sub(const SubBuf<BITS, G>& b, int pbase,
     vz[r] = f16_to_f32(vszr >> 16);
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      int acc[QDIG];
-#pragma unroll
-      for (int k = 0; k < QDIG; ++k) acc[k] = 0;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const uint4 L = C::QREG ? qd[gg][x] : *(const uint4*)(qdw + (gg * 16 + half * 8 + x) * DIGP);
-        const uint32_t Lk[4] = {L.x, L.y, L.z, L.w};
-        int X;
-        if constexpr (BITS == 2) {
-          // x = 2 w + parity: parity 0 takes the even dimensions of code word w
-          const uint32_t dw = d[x >> 1];
-          X = (int)((x & 1) ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u));
-        } else if constexpr (BITS == 3) {
-          // low two bits as at 2 bits, high bit from high-plane word w / 2 at
-          // shift k = 2 (w & 1) + parity (the plane's element order)
-          const uint32_t dw = d[x >> 1];
-          const uint32_t hw = (x >> 2) ? b.kh[r].y : b.kh[r].x;
-          const int k = (((x >> 1) & 1) << 1) | (x & 1);
-          const uint32_t lo2 = (x & 1) ? ((dw >> 2) & 0x33333333u) : (dw & 0x33333333u);
-          X = (int)(lo2 | (((hw >> k) & 0x11111111u) << 2));
-        } else {
-          X = (int)(d[x] ^ 0x88888888u);  // code - 8 as a signed nibble
-        }
-#pragma unroll
-        for (int k = 0; k < QDIG; ++k) acc[k] = __builtin_amdgcn_sdot8(X, (int)Lk[k], acc[k], false);
-      }
-      int dot = acc[QDIG - 1];
-#pragma unroll
-      for (int k = QDIG - 2; k >= 0; --k) dot = dot * 16 + acc[k];
-      if constexpr (BITS == 4) dot += 8 * (int)qr[gg].qsum;
-      dot += swap_adjacent(dot);
-      sc[r][gg] = ok ? ks * ((float)dot * qr[gg].inv) + kz * qr[gg].sig : -INFINITY;
+      // sum_k acc_k 16^k in two exact halves of three digits (each below
+      // 2^23), joined in float
+      static_assert(QDIG == 6, "the digit join assumes six digits");
+      const int dlo = acc[r][gg][0] + 16 * acc[r][gg][1] + 256 * acc[r][gg][2];
+      const int dhi = acc[r][gg][3] + 16 * acc[r][gg][4] + 256 * acc[r][gg][5];
+      float dot = fmaf((float)dhi, 4096.f, (float)dlo);
+      if constexpr (BITS == 4) dot += 8.f * qr[gg].qsum;
+      dot += __int_as_float(swap_adjacent(__float_as_int(dot)));
+      sc[r][gg] = ok ? ks * (dot * qr[gg].inv) + kz * qr[gg].sig : -INFINITY;
     }
   }
 
@@ -612,25 +646,33 @@ __device__ __forceinline__ void load_first(SubBuf<BITS, G>& A, const DecodeArgs&
 // One wave, G query heads (scales qsc, digit words qdw): sub-chunks c0,
 // c0 + stride, ... (< c_end) of the quantized region [lo, hi), two sub-chunks
 // of codes in flight; leaves the partial (o[D], m, l) of head gg at
-// out + gg * hstride.  A holds (in flight) sub-chunk c0.
-template <int BITS, int G, int CP = CPOL_NT>
+// out + gg * hstride.  On entry A and B hold (in flight) sub-chunks c0 and
+// c0 + stride, both issued by the caller before the query preparation, so
+// the loop starts with two sub-chunks on their way.  A third buffer measured
+// slower at one wave per SIMD (86 against 79 us per 128K layer): more
+// requests in flight do not pay on this access pattern.
+template <int BITS, int G, int CP = CPOL_NT, bool QREG = false>
 __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stride, int c_end, int lo,
                            int hi, const float* qsc, const uint32_t* qdw, uint32_t* wsm, float* out,
-                           int64_t hstride, SubBuf<BITS, G>& A, const uint8_t* spare) {
+                           int64_t hstride, SubBuf<BITS, G>& A, SubBuf<BITS, G>& B,
+                           const uint8_t* spare) {
   using C = SplitCfg<BITS, G>;
+  static_assert(!QREG || G == 1, "register digits for one head");
   const int lane = threadIdx.x & 63, half = lane & 1;
-  uint4 qd[C::QREG ? G : 1][8];
+  uint4 qd[QREG ? 8 : 1][2];
   QueryRegs qr[G];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     qr[gg].sig = qsc[gg * 4];
     qr[gg].inv = qsc[gg * 4 + 1];
     qr[gg].qsum = qsc[gg * 4 + 2 + half];
-    if (C::QREG)
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-        qd[C::QREG ? gg : 0][x] = *(const uint4*)(qdw + (gg * 16 + half * 8 + x) * DIGP);
   }
+  if constexpr (QREG)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      qd[x][0] = *(const uint4*)(qdw + (half * 8 + x) * DIGP);
+      qd[x][1] = *(const uint4*)(qdw + (half * 8 + x) * DIGP + 4);
+    }
   // running softmax state: M wave-uniform; Lrun and Zrun (sum of p z) per-lane
   // partials, O per dimension
   float M[G], Lrun[G], Zrun[G], O[G][2];
@@ -640,24 +682,22 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
     Lrun[gg] = Zrun[gg] = 0.f;
     O[gg][0] = O[gg][1] = 0.f;
   }
-  SubBuf<BITS, G> B;
   int c = c0;
-  // The next sub-chunk's loads are issued unconditionally (past the end they
-  // read the spare block, from L2): a conditional load leaves the
-  // compiler's wait counts conservative at the join, and it would then wait
-  // for the prefetch before processing the current sub-chunk.
+  // A buffer is refilled with the sub-chunk two steps ahead as soon as it has
+  // been processed.  The loads are issued unconditionally (past the end they
+  // read the spare block, from L2): a conditional load leaves the compiler's
+  // wait counts conservative at the join, and it would then wait for the
+  // prefetch before processing the next sub-chunk.
   while (c < c_end) {
-    int cn = c + stride;
-    load_sub<BITS, G, CP>(B, a, qm, cn < c_end ? cn * C::TW : -1, spare);
-    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before waiting for A
-    process_sub<BITS, G>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
-    c = cn;
-    if (c >= c_end) break;
-    cn = c + stride;
-    load_sub<BITS, G, CP>(A, a, qm, cn < c_end ? cn * C::TW : -1, spare);
+    process_sub<BITS, G, QREG>(A, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
     __builtin_amdgcn_sched_barrier(0);
-    process_sub<BITS, G>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
-    c = cn;
+    load_sub<BITS, G, CP>(A, a, qm, c + 2 * stride < c_end ? (c + 2 * stride) * C::TW : -1, spare);
+    c += stride;
+    if (c >= c_end) break;
+    process_sub<BITS, G, QREG>(B, c * C::TW, lo, hi, qd, qdw, qr, wsm, M, Lrun, Zrun, O);
+    __builtin_amdgcn_sched_barrier(0);
+    load_sub<BITS, G, CP>(B, a, qm, c + 2 * stride < c_end ? (c + 2 * stride) * C::TW : -1, spare);
+    c += stride;
   }
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
@@ -1028,7 +1068,7 @@ __device__ __forceinline__ int run_start(int64_t nsub, int j, int n) {
 // PREP: the query block comes from the prep kernel (else every workgroup
 // prepares the query itself).
 template <int IO_BF16, int BITS, int G, bool PREP>
-__global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, G == 4 ? 3 : 2) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
   uint32_t* sm = (uint32_t*)smem4;
@@ -1152,23 +1192,25 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
         cstride = a.n_splits;
       }
       // the query inputs, then the first sub-chunk's codes, in flight together
-      SubBuf<BITS, C::GW> A;
+      SubBuf<BITS, C::GW> A, B;
       if constexpr (PREP) {
         PrepIn<G> pin;
         prep_load<G>(a, u, pin);
         load_first<BITS, C::GW, 0>(A, a, qm, c0, cend, spare);
+        load_first<BITS, C::GW, 0>(B, a, qm, c0 + cstride, cend, spare);
         prep_store<BITS, G>(sm, pin);
       } else {
         QueryIn<G> qin;
         compensate_load<IO_BF16, G>(a, h, si, qin);
         load_first<BITS, C::GW, 0>(A, a, qm, c0, cend, spare);
+        load_first<BITS, C::GW, 0>(B, a, qm, c0 + cstride, cend, spare);
         compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
       }
       float* dst = a.wsp + ((int64_t)(qbase + w * C::GW) * nsp + j) * PS;
       quant_wave<BITS, C::GW, 0>(a, qm, c0, cstride, cend, lo, hi,
                               (const float*)(sm + C::O_QSC) + w * C::GW * 4,
                               sm + C::O_QD + w * C::GW * 16 * DIGP, sm + C::O_UNION + w * C::WAVE,
-                              dst, (int64_t)nsp * PS, A, spare);
+                              dst, (int64_t)nsp * PS, A, B, spare);
       direct = true;
     } else {
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wi = 4 * j + w;
@@ -1187,22 +1229,26 @@ __global__ __launch_bounds__(256, G == 1 || G == 4 ? 3 : 2) void split_kernel(De
         cstride = nw;
       }
       // the query inputs, then the first sub-chunk's codes, in flight together
-      SubBuf<BITS, G> A;
+      SubBuf<BITS, G> A, B;
       if constexpr (PREP) {
         PrepIn<G> pin;
         prep_load<G>(a, u, pin);
         load_first<BITS, G>(A, a, qm, c0, cend, spare);
+        load_first<BITS, G>(B, a, qm, c0 + cstride, cend, spare);
         prep_store<BITS, G>(sm, pin);
       } else {
         QueryIn<G> qin;
         compensate_load<IO_BF16, G>(a, h, si, qin);
         load_first<BITS, G>(A, a, qm, c0, cend, spare);
+        load_first<BITS, G>(B, a, qm, c0 + cstride, cend, spare);
         compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
       }
       uint32_t* wbase = sm + C::O_UNION;
       float* part = (float*)(wbase + 4 * C::WAVE);  // [4 waves][G][D + 2]
-      quant_wave<BITS, G>(a, qm, c0, cstride, cend, lo, hi, (const float*)(sm + C::O_QSC),
-                          sm + C::O_QD, wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A, spare);
+      quant_wave<BITS, G, CPOL_NT, G == 1>(a, qm, c0, cstride, cend, lo, hi,
+                                           (const float*)(sm + C::O_QSC), sm + C::O_QD,
+                                           wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A,
+                                           B, spare);
       __syncthreads();
       // merge the four wave partials (a wave without sub-chunks has l = 0)
       const int i = tid & (D - 1), hf = tid >> 7;
