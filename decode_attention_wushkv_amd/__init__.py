@@ -25,7 +25,7 @@ WUSHKV_MAX_SEQ_PER_CALL = 128
 EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_quantized_range", "wushkv_append", "wushkv_decode_workspace_bytes",
-    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_set_split_events",
+    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_decode_step_noalloc", "wushkv_set_split_events",
     "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_set_block_table",
     "wushkv_chunk_workspace_bytes", "wushkv_chunk_step", "wushkv_status_str",
 )
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_decode_attn.argtypes = [P, i32, i32, i32p, P, P, P, P, _U64, P]
     L.wushkv_decode_step.restype = ctypes.c_int
     L.wushkv_decode_step.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P, _U64, P]
+    L.wushkv_decode_step_noalloc.restype = ctypes.c_int
+    L.wushkv_decode_step_noalloc.argtypes = [P, i32, i32, i32p, P, P, P, P, P, P, P]
     L.wushkv_chunk_workspace_bytes.restype = _U64
     L.wushkv_chunk_workspace_bytes.argtypes = [P, i32, i32]
     L.wushkv_chunk_step.restype = ctypes.c_int
@@ -220,6 +222,24 @@ def wushkv_decode_step(cache: int, layer: int, slots, k_ptr: int, v_ptr: int, tk
                                   vp(stream))
     if check:
         _check(st, "wushkv_decode_step")
+    return st
+
+
+WUSHKV_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def wushkv_decode_step_noalloc(cache: int, layer: int, slots, k_ptr: int, v_ptr: int, tk_ptr: int,
+                               q_ptr: int, tq_ptr: int, out_ptr: int, stream: int = 0, *,
+                               check: bool = True) -> int:
+    """wushkv_decode_step with the library's own per-GPU scratch as workspace
+    (no allocation); calls that overlap on one GPU race."""
+    s, n = _i32_array(slots)
+    vp = ctypes.c_void_p
+    st = lib().wushkv_decode_step_noalloc(vp(cache), int(layer), n, s, vp(k_ptr), vp(v_ptr),
+                                          vp(tk_ptr), vp(q_ptr), vp(tq_ptr), vp(out_ptr),
+                                          vp(stream))
+    if check:
+        _check(st, "wushkv_decode_step_noalloc")
     return st
 
 

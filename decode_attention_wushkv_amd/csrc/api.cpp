@@ -370,14 +370,23 @@ extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32
 // Shared by decode_attn and decode_step: validation of the attention
 // arguments, then the per-sequence plan and the launch.  step = 1 adds the
 // fused one-token append (k, v, tk non-null).
+// scratch: the workspace is the library's per-device scratch array (ws and
+// ws_bytes are ignored and looked up after the argument checks).
 static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq,
                                    const int32_t* slots, const void* k, const void* v,
                                    const float* tk, const void* q, const float* tq, float* out,
-                                   void* ws, uint64_t ws_bytes, void* stream, bool step) {
+                                   void* ws, uint64_t ws_bytes, void* stream, bool step,
+                                   bool scratch = false) {
   if (!c || !slots || layer < 0 || layer >= c->cfg.n_layers || n_seq < 0) return WUSHKV_EINVAL;
   if (n_seq > MAXSEQ) return WUSHKV_EUNSUPPORTED;
   if (step && c->cfg.sink + c->cfg.recent + c->cfg.flush > WINDOW_MAX) return WUSHKV_EUNSUPPORTED;
   if (n_seq == 0) return WUSHKV_OK;
+  if (scratch) {
+    if (wushkv_decode_workspace_bytes(c, n_seq) > WUSHKV_NOALLOC_SCRATCH_BYTES)
+      return WUSHKV_EWORKSPACE;
+    ws = out;  // stands in until the checks pass (alignment of out is checked)
+    ws_bytes = WUSHKV_NOALLOC_SCRATCH_BYTES;
+  }
   if (!q || !tq || !out || !ws) return WUSHKV_EINVAL;
   if (step && (!k || !v || !tk)) return WUSHKV_EINVAL;
   const size_t esz = c->cfg.io_dtype == WUSHKV_IO_FP32 ? 4 : 2;
@@ -396,6 +405,12 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   } else {
     for (int i = 0; i < n_seq; ++i)
       if (c->len[(size_t)layer * c->cfg.max_batch + slots[i]] < 1) return WUSHKV_EINVAL;
+  }
+  if (scratch) {
+    uint64_t bytes = 0;
+    if (noalloc_scratch(&ws, &bytes) != hipSuccess) return WUSHKV_EDEVICE;
+    if (bytes < wushkv_decode_workspace_bytes(c, n_seq)) return WUSHKV_EWORKSPACE;
+    ws_bytes = bytes;
   }
   if (step) {
     if (step_as_chunk(c)) {
@@ -471,6 +486,14 @@ extern "C" wushkv_status wushkv_decode_step(wushkv_cache* c, int32_t layer, int3
                                             float* out, void* ws, uint64_t ws_bytes,
                                             void* stream) {
   return decode_common(c, layer, n_seq, slots, k, v, tk, q, tq, out, ws, ws_bytes, stream, true);
+}
+
+extern "C" wushkv_status wushkv_decode_step_noalloc(wushkv_cache* c, int32_t layer, int32_t n_seq,
+                                                    const int32_t* slots, const void* k,
+                                                    const void* v, const float* tk, const void* q,
+                                                    const float* tq, float* out, void* stream) {
+  return decode_common(c, layer, n_seq, slots, k, v, tk, q, tq, out, nullptr, 0, stream, true,
+                       true);
 }
 
 extern "C" uint64_t wushkv_chunk_workspace_bytes(const wushkv_cache* c, int32_t n_seq,

@@ -214,5 +214,8 @@ bool prefill_supported(int codec, double p_lo, double p_hi);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int blocks, void* out, hipStream_t st);
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
+// Device address and size of the current device's file-scope scratch array
+// (wushkv_decode_step_noalloc's workspace).
+hipError_t noalloc_scratch(void** ptr, uint64_t* bytes);
 
 }  // namespace wkv

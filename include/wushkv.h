@@ -285,6 +285,25 @@ wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_s
                                  const float* tk, const void* q, const float* tq, float* out,
                                  void* ws, uint64_t ws_bytes, void* stream);
 
+/*
+ * wushkv_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as wushkv_decode_step,
+ * without the workspace: the library keeps it in a file-scope device array
+ * of WUSHKV_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  A
+ * call whose workspace (wushkv_decode_workspace_bytes) exceeds that returns
+ * WUSHKV_EWORKSPACE before any launch (e.g. the G = 8 decode step of 8
+ * sequences, whose chunk-step workspace is larger).  No call allocates or
+ * frees memory.  Every call on one GPU shares its array: calls that overlap
+ * on one GPU (two streams, two threads) race and must be serialized by the
+ * caller.  Nothing in the array needs to start at zero.
+ */
+#define WUSHKV_NOALLOC_SCRATCH_BYTES (16ull << 20)
+wushkv_status wushkv_decode_step_noalloc(wushkv_cache* cache, int32_t layer, int32_t n_seq,
+                                         const int32_t* slots, const void* k, const void* v,
+                                         const float* tk, const void* q, const float* tq,
+                                         float* out, void* stream);
+
 /* Largest number of new positions per sequence in one wushkv_chunk_step. */
 #define WUSHKV_MAX_CHUNK 16
 

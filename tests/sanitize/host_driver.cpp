@@ -80,6 +80,13 @@ hipError_t launch_chunk(ChunkArgs& a, int, hipStream_t) {
   CHECK(a.n_splits >= 0 && a.n_splits <= chunk_split_cap(a.n_seq * a.g.n_kv * a.RT));
   return hipSuccess;
 }
+// The no-allocation entry point's scratch: a host buffer stands in.
+static uint8_t* g_scratch;
+hipError_t noalloc_scratch(void** ptr, uint64_t* bytes) {
+  *ptr = g_scratch;
+  *bytes = WUSHKV_NOALLOC_SCRATCH_BYTES;
+  return hipSuccess;
+}
 }  // namespace wkv
 
 static wushkv_config cfg_of(int bits, int G, int page) {
@@ -141,6 +148,19 @@ static void run(int bits, int G, int page) {
     CHECK(wushkv_decode_step(h, 1, 3, slots, g_arena, g_arena, tk, g_arena, tk, out, g_ws, ws,
                              0) == WUSHKV_OK);
   CHECK(wushkv_get_len(h, 1, 2, &L, &sq) == WUSHKV_OK && L == 40);
+  // the same steps with the library's scratch as workspace
+  std::vector<uint8_t> scratch(WUSHKV_NOALLOC_SCRATCH_BYTES + 256);
+  g_scratch = (uint8_t*)(((uintptr_t)scratch.data() + 255) & ~(uintptr_t)255);
+  g_ws = g_scratch;
+  g_ws_bytes = WUSHKV_NOALLOC_SCRATCH_BYTES;
+  CHECK(wushkv_decode_step_noalloc(h, 1, 3, slots, g_arena, g_arena, tk, g_arena, tk, out, 0) ==
+        WUSHKV_OK);
+  CHECK(wushkv_get_len(h, 1, 2, &L, &sq) == WUSHKV_OK && L == 41);
+  int32_t dup[2] = {2, 2};
+  CHECK(wushkv_decode_step_noalloc(h, 1, 2, dup, g_arena, g_arena, tk, g_arena, tk, out, 0) ==
+        WUSHKV_EINVAL);
+  CHECK(wushkv_decode_step_noalloc(h, 1, 3, slots, g_arena, g_arena, tk, nullptr, tk, out, 0) ==
+        WUSHKV_EINVAL);
   // chunk steps
   const uint64_t cws = wushkv_chunk_workspace_bytes(h, 3, 16);
   std::vector<uint8_t> cbuf(cws + 16);

@@ -330,3 +330,32 @@ def test_quantized_range():
     for L, want in [(144, 16), (159, 16), (160, 32), (1000, 864)]:
         assert wk.wushkv_quantized_range(h, L) == (16, want)
     wk.wushkv_cache_destroy(h)
+
+
+def test_decode_step_noalloc_limits():
+    """The no-allocation decode step checks its arguments and the size of the
+    workspace it needs against its fixed scratch before touching the device:
+    a step whose workspace exceeds the scratch (groups of 8 query heads over 8
+    sequences run as chunk steps with a larger workspace) is refused with
+    EWORKSPACE, invalid arguments with EINVAL, and lengths stay unchanged."""
+    P = 1 << 41
+    cfg = _cfg(n_layers=1, n_q_heads=64, n_kv_heads=8, max_batch=8, ctx_cap=1000)
+    lay = wk.wushkv_layout(cfg)
+    h = wk.wushkv_cache_create(cfg, FAKE_ARENA, lay.total_bytes)
+    assert wk.wushkv_decode_workspace_bytes(h, 8) > wk.WUSHKV_NOALLOC_SCRATCH_BYTES
+    step = lambda slots, q=P: wk.wushkv_decode_step_noalloc(h, 0, slots, P, P, P, q, P, P,
+                                                            check=False)
+    assert step(list(range(8))) == wk.WUSHKV_EWORKSPACE
+    assert step([]) == wk.WUSHKV_OK
+    for s in range(8):
+        assert wk.wushkv_get_len(h, 0, s) == (0, 4)
+    wk.wushkv_cache_destroy(h)
+    h, _ = _fake_cache()   # groups of 4: a small workspace
+    step = lambda slots, q=P: wk.wushkv_decode_step_noalloc(h, 0, slots, P, P, P, q, P, P,
+                                                            check=False)
+    assert step([0, 0]) == wk.WUSHKV_EINVAL       # duplicate slot
+    assert step([0], q=0) == wk.WUSHKV_EINVAL     # null query
+    assert step([7]) == wk.WUSHKV_EINVAL          # slot out of range
+    for s in range(4):
+        assert wk.wushkv_get_len(h, 0, s) == (0, 4)
+    wk.wushkv_cache_destroy(h)
