@@ -10,12 +10,13 @@
 // [128 x 128] product.  T_K (fp32) is split exactly into three bfloat16 parts,
 // T = T1 + T2 + T3 (8 + 8 + 8 significant bits), held as MFMA operands in
 // registers for the whole workgroup; bfloat16 keys times bfloat16 parts are
-// exact products, summed by v_mfma_f32_16x16x32_bf16 in fp32: T1 products in
-// four MFMAs of 32 folded into one fp32 sum, T2 and T3 products in one chain.
-// The fp32 error of the sum is below 36 ulp (2^-23 each) of
+// exact products, summed by the matrix cores in fp32: T1 products in eight
+// v_mfma_f32_16x16x16_bf16 of 16 folded into one fp32 sum, T2 and T3 products
+// in one v_mfma_f32_16x16x32_bf16 chain.  The fp32 error of the sum is below
+// 20 ulp (2^-23 each) of
 // A = sum_j |k_j| |T_ij|, which a fourth MFMA chain (|k| times |T1|) bounds.
 // An entry whose fp32 value lies within that bound of a bfloat16 rounding
-// boundary is recomputed in fp64 with the arithmetic of the one-position paths (transform_entry; about 3 per cent of the entries,
+// boundary is recomputed in fp64 with the arithmetic of the one-position paths (transform_entry; about 2 per cent of the entries,
 // by the four key waves while the four value waves quantize the values), so
 // the stored bfloat16 keys are identical to theirs.
 //
@@ -41,6 +42,7 @@ namespace wkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int PT = PREFILL_TILE;  // positions per tile
@@ -52,15 +54,16 @@ constexpr int VCS = 132;          // LDS row stride (bytes) of the value-code by
 constexpr int FIXMAX = PT * D;    // recomputation list capacity (every entry of a tile)
 // fp32 summation error bound of the transform relative to sum_j |k_j| |T_ij|,
 // counting one ulp (2^-23) per rounding whatever order and rounding the
-// matrix core uses inside an instruction: 31 roundings inside each 32-product
-// T1 MFMA, 3 from folding the four results together, the T2 + T3 chain below
-// 2^-8 of T (about half an ulp overall), the final addition: 35.5 ulp, taken
-// as 36.
-constexpr float kTransformErr = 36.0f * 0x1p-23f;
+// matrix core uses inside an instruction: 15 roundings inside each 16-product
+// T1 MFMA, 3 from the fold tree of the eight results, the T2 + T3 chain
+// below 2^-8 of T (about half an ulp overall), the final additions: under 20
+// ulp.
+constexpr float kTransformErr = 20.0f * 0x1p-23f;
 
 struct __align__(16) PLds {
   float t[D * TS];        // T_K rows (fp32)
   uint16_t k[PT * RS];    // input keys (bf16)
+  uint16_t ka[PT * RS];   // their magnitudes |k|
   uint16_t v[PT * RS];    // values (bf16)
   uint16_t kq[PT * RS];   // transformed keys (bf16)
   uint16_t fix[FIXMAX];   // entries to recompute: row << 7 | dimension
@@ -73,6 +76,9 @@ __device__ __forceinline__ __bf16 bf16_of_bits(uint32_t b) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x4 as_bf16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(bf16x4, make_uint2(lo, hi));
+}
 
 // |x| of eight bfloat16 values, recomputed where it is used (a volatile
 // v_and_b32 per dword, so that the compiler does not keep a copy of the
@@ -413,6 +419,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
       const int x = tid + NT * u;
       const int which = x >> 10, r = (x >> 4) & 63, c = x & 15;
       *(uint4*)((which ? L.v : L.k) + r * RS + c * 8) = pre[u];
+      if (u < NPRE / 2)
+        *(uint4*)(L.ka + r * RS + c * 8) =
+            make_uint4(pre[u].x & 0x7FFF7FFFu, pre[u].y & 0x7FFF7FFFu, pre[u].z & 0x7FFF7FFFu,
+                       pre[u].w & 0x7FFF7FFFu);
     }
     if (tid == 0) L.nfix = 0;
     __syncthreads();
@@ -421,29 +431,54 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
     // ---- transform on the matrix cores (all waves); flag entries near a
     // rounding boundary
     {
+      // the row blocks of 16 rows are computed two at a time (independent
+      // MFMA chains keep the matrix core busy).  T1 products: two MFMAs of 16
+      // products per 32-step (the lane's eight k values split in halves),
+      // each from zero, folded in fp32 in a tree of depth 3; T2 and T3
+      // products (below 2^-8 of T1's) in one chain; cab: |k| |T1| products
+      // (|k| staged in LDS with the tile), which bound the partial sums
+      f32x4 s01[4], q2[4], c23[4], cab[4];
+#pragma unroll
+      for (int rp = 0; rp < 4; rp += 2) {  // two row blocks at a time
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint4 bv = __builtin_bit_cast(uint4, b1[ks]);
+          const bf16x8 b1a = abs_bf16x8(b1[ks]);
+#pragma unroll
+          for (int rb = rp; rb < rp + 2; ++rb) {
+            const int ao = (16 * rb + (lane & 15)) * RS + 32 * ks + 8 * (lane >> 4);
+            const uint4 av = *(const uint4*)(L.k + ao);
+            const bf16x8 A = as_bf16x8(av);
+            const bf16x8 Aab = as_bf16x8(*(const uint4*)(L.ka + ao));
+            const f32x4 plo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                as_bf16x4(av.x, av.y), as_bf16x4(bv.x, bv.y), f32x4{}, 0, 0, 0);
+            const f32x4 phi = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                as_bf16x4(av.z, av.w), as_bf16x4(bv.z, bv.w), f32x4{}, 0, 0, 0);
+            c23[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b2[ks], ks == 0 ? f32x4{} : c23[rb], 0, 0, 0);
+            c23[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b3[ks], c23[rb], 0, 0, 0);
+            cab[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aab, b1a, ks == 0 ? f32x4{} : cab[rb], 0, 0, 0);
+            const f32x4 qk = plo + phi;
+            if (ks == 0) s01[rb] = qk;
+            else if (ks == 1) s01[rb] = s01[rb] + qk;
+            else if (ks == 2) q2[rb] = qk;
+            else s01[rb] = s01[rb] + (q2[rb] + qk);
+          }
+        }
+      }
+      // rows of this lane's entries inside [c0, c1): bit 4 rb + r
+      uint32_t inr = 0u;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int t = 16 * (n >> 2) + 4 * (lane >> 4) + (n & 3);
+        inr |= (uint32_t)((unsigned)(p0 + t - c0) < (unsigned)(c1 - c0)) << n;
+      }
       uint32_t flags = 0u;  // bit 4 rb + r: entry (16 rb + 4 (lane / 16) + r, i) lies near a boundary
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        // T1 products: one MFMA per 32-step from zero, folded into s1 in fp32;
-        // the T2 and T3 products (below 2^-8 of T1's) in one chain; cab:
-        // |k| |T1| products, which bound the partial sums
-        f32x4 s1 = f32x4{}, c23 = f32x4{}, cab = f32x4{};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const uint4 av = *(const uint4*)(L.k + (16 * rb + (lane & 15)) * RS + 32 * ks + 8 * (lane >> 4));
-          const bf16x8 A = as_bf16x8(av);
-          const bf16x8 Aab = as_bf16x8(make_uint4(av.x & 0x7FFF7FFFu, av.y & 0x7FFF7FFFu,
-                                                  av.z & 0x7FFF7FFFu, av.w & 0x7FFF7FFFu));
-          const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b1[ks], f32x4{}, 0, 0, 0);
-          c23 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b2[ks], c23, 0, 0, 0);
-          c23 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b3[ks], c23, 0, 0, 0);
-          cab = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aab, abs_bf16x8(b1[ks]), cab, 0, 0, 0);
-          s1 = ks == 0 ? p1 : s1 + p1;
-        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * rb + 4 * (lane >> 4) + r;
-          const float y = s1[r] + c23[r];
+          const float y = s01[rb][r] + c23[rb][r];
           const uint32_t bits = __float_as_uint(y);
           L.kq[t * RS + i_out] = (uint16_t)((bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16);
           // distance of y to the rounding boundary of its bfloat16 cell
@@ -453,11 +488,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
           // |T| <= |T1| (1 + 2^-8): cab (1 + 2^-7) bounds sum_j |k_j| |T_ij|
           // with room for the rounding of cab itself; 2^-110 covers products
           // below the smallest normal float
-          const float err = fmaf(kTransformErr * 1.0079f, cab[r], 0x1p-110f);
-          const bool near = dist <= err || err >= 16384.0f * ulp;
-          flags |= (near && p0 + t >= c0 && p0 + t < c1) ? 1u << (4 * rb + r) : 0u;
+          const float err = fmaf(kTransformErr * 1.0079f, cab[rb][r], 0x1p-110f);
+          flags |= (uint32_t)(fminf(dist, 16384.0f * ulp) <= err) << (4 * rb + r);
         }
       }
+      flags &= inr;
       // compaction of the wave's flagged entries into the list: exclusive
       // prefix of the per-lane counts from one ballot per count bit
       const int cnt = __popc(flags);
@@ -494,13 +529,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
         double s[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 1
         for (int c = 0; c < 4; ++c) {
+          // the chunk's T_K and key values of all four chains, then the FMAs
+          float4 ta[4], tb[4];
+          uint4 kk[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 ta = *(const float4*)(tr + 32 * q + 8 * c);
-            const float4 tb = *(const float4*)(tr + 32 * q + 8 * c + 4);
-            const uint4 kk = *(const uint4*)(kr + 32 * q + 8 * c);
-            const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-            const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+            ta[q] = *(const float4*)(tr + 32 * q + 8 * c);
+            tb[q] = *(const float4*)(tr + 32 * q + 8 * c + 4);
+            kk[q] = *(const uint4*)(kr + 32 * q + 8 * c);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float tv[8] = {ta[q].x, ta[q].y, ta[q].z, ta[q].w, tb[q].x, tb[q].y, tb[q].z, tb[q].w};
+            const uint32_t kw[4] = {kk[q].x, kk[q].y, kk[q].z, kk[q].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[q] = fma((double)tv[e], (double)bf16_lane(kw, e), s[q]);
           }

@@ -61,23 +61,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // fp64 -> binary16 bits, round to nearest even, saturating at +-65504.
 __device__ __forceinline__ uint16_t f64_to_f16_sat(double x) {
-  uint64_t b = (uint64_t)__double_as_longlong(x);
-  uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
-  int ef = (int)((b >> 52) & 0x7FF);
-  uint64_t mant = b & 0xFFFFFFFFFFFFFull;
-  if (ef == 0x7FF) return mant ? (uint16_t)0x7E00 : (uint16_t)(sign | 0x7BFF);
-  if (ef == 0) return sign;
-  int e = ef - 1023;
-  uint64_t m = mant | (1ull << 52);
-  if (e >= -14) {
-    uint64_t r = shift_rne(m, 42);  // keep 11 significant bits
-    if (r == 2048) { r = 1024; e += 1; }
-    if (e > 15) return sign | 0x7BFF;
-    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r & 0x3FF);
+  if (x != x) return 0x7E00;
+  // round to odd into fp32 (13 more significant bits than binary16 and a wider
+  // exponent range), so that the hardware round-to-nearest-even conversion to
+  // binary16 gives the binary16 rounding of x itself
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != x) {
+    if (fabs(back) > fabs(x)) u -= 1u;  // toward zero (f is not zero here)
+    u |= 1u;
   }
-  int s = 28 - e;  // value in units of 2^-24 is m * 2^(e - 28)
-  if (s > 63) return sign;
-  return sign | (uint16_t)shift_rne(m, s);  // r <= 1024; 1024 encodes 2^-14
+  const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(u));
+  return (h & 0x7FFFu) == 0x7C00u ? (uint16_t)((h & 0x8000u) | 0x7BFFu) : h;  // saturate
 }
 
 __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
