@@ -266,6 +266,66 @@ def cpu_baseline(w, bits, seconds, max_units, threads=1):
     return res
 
 
+def oracle_per_config(seconds=1.5):
+    """The oracle timed on this host for every workload, one thread: decode
+    attention (dequantize + fp64 softmax attention) of sampled (layer, KV head)
+    units at the workload's longest context, and the append side (transform,
+    percentile clip, quantization of keys and values) of sampled positions.
+    Whole-step and whole-prefill times are extrapolated from these samples:
+    attention linear in each sequence's context, append linear in positions."""
+    import numpy as np
+
+    import oracle
+    from decode_attention_wushkv_amd import synth
+
+    rng = np.random.default_rng(4321)
+    rows = []
+    for wid in sorted(synth.WORKLOADS):
+        w = synth.WORKLOADS[wid]
+        bits = w.bits[0]
+        lens = w.lengths()
+        L = max(lens)
+        S, R, F = w.sink, w.recent, w.flush
+        qp = slice(S, squant(L, S, R, F))
+        # attention units
+        n_att, t_att = 0, 0.0
+        while n_att < 1 or (t_att < seconds and n_att < 16):
+            cont = synth.random_cache_contents(rng, L, bits)
+            q = rng.standard_normal((w.group, 128))
+            t0 = time.perf_counter()
+            K = cont["k_bf16"].astype(np.float64)
+            V = cont["v_bf16"].astype(np.float64)
+            K[qp] = oracle.dequantize(cont["kcodes"][qp], cont["ks16"][qp], cont["kz16"][qp])
+            V[qp] = oracle.dequantize(cont["vcodes"][qp], cont["vs16"][qp], cont["vz16"][qp])
+            oracle.attention(q, K[None], V[None])
+            t_att += time.perf_counter() - t0
+            n_att += 1
+        s_unit = t_att / n_att
+        # append side: transform + quantization of sampled positions
+        T, _ = synth.transforms(w, 0)
+        npos = 2048
+        keys = rng.standard_normal((npos, 128)).astype(np.float32)
+        vals = rng.standard_normal((npos, 128)).astype(np.float32)
+        t0 = time.perf_counter()
+        kt, _ = oracle.transform(T[0], keys)
+        oracle.quantize(oracle.bf16(kt), bits, w.p_lo, w.p_hi)
+        oracle.quantize(oracle.bf16(vals), bits, w.p_lo, w.p_hi)
+        s_pos = (time.perf_counter() - t0) / npos
+        units_step = w.n_layers * w.n_kv * len(lens)
+        step_s = w.n_layers * w.n_kv * sum(s_unit * l / L for l in lens) + units_step * s_pos
+        prefill_s = w.n_layers * w.n_kv * sum(lens) * s_pos
+        rows.append({"workload": w.name, "bits": bits, "threads": 1,
+                     "attention_units_timed": n_att, "attention_context": L,
+                     "attention_s_per_unit": round(s_unit, 5),
+                     "append_positions_timed": npos, "append_s_per_position": round(s_pos, 8),
+                     "decode_step_s_extrapolated": round(step_s, 3),
+                     "prefill_s_extrapolated": round(prefill_s, 2),
+                     "note": "extrapolated: sampled attention units x the step's units (linear "
+                             "in each sequence's context) + sampled appends x the step's "
+                             "appends; prefill: sampled appends x every position"})
+    return rows
+
+
 def read_ceiling(window_bytes, dev, copies=6):
     """Practical HBM read ceiling on this GPU: the library's streaming-read
     kernel over windows of the split launch's size, rotated through `copies`
@@ -484,12 +544,15 @@ def chunk_rate(wid, dev, chunk=16, reps=4):
                     "bytes one chunk reads"}
 
 
-def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
+def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None, copies=1):
     """Build the workload's cache through the library (prefill appends, layer
     by layer), then time K decode steps (pass A, no instrumentation) and K more
-    with HIP events around every split launch (pass B).  page_size > 0 builds a
-    paged cache whose pool holds exactly the pages the sequences need, handed
-    out in a seeded shuffled order."""
+    with HIP events around every split launch and every combine launch (pass
+    B).  page_size > 0 builds a paged cache whose pool holds exactly the pages
+    the sequences need, handed out in a seeded shuffled order.  copies > 1
+    builds that many copies of the workload's layers (the same contents) and
+    step st runs on copy st % copies, so that a cache smaller than the GPU's
+    256 MB last-level cache is read from HBM rather than from that cache."""
     import numpy as np
     import torch
 
@@ -508,14 +571,16 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
         n_pages = sum((squant(t, S, R, F) - 1) // page_size + 1 - S // page_size for t in targets)
         paging = dict(page_size=page_size, n_pages=n_pages,
                       page_seed=page_seed if page_seed is not None else 7 + page_size)
-    dc = DeviceCache(n_layers=w.n_layers, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits, sink=S,
+    NL = w.n_layers * copies
+    dc = DeviceCache(n_layers=NL, n_q_heads=w.n_q, n_kv_heads=w.n_kv, bits=bits, sink=S,
                      recent=R, flush=F, p_lo=w.p_lo, p_hi=w.p_hi, max_batch=B,
                      ctx_cap=max(targets), io_dtype=w.torch_io, device=dev, **paging)
 
     # ---- build the cache through the library (prefill appends), layer by layer
     t_build = time.perf_counter()
     tks, tqs = [], []
-    for layer in range(w.n_layers):
+    for cl in range(NL):
+        layer = cl % w.n_layers
         T, Tq = synth.transforms(w, layer)
         tks.append(torch.from_numpy(T).to(dev))
         tqs.append(torch.from_numpy(Tq).to(dev))
@@ -528,7 +593,7 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
         kk = torch.cat(parts_k) if B > 1 else parts_k[0]
         vv = torch.cat(parts_v) if B > 1 else parts_v[0]
         del parts_k, parts_v
-        dc.append(layer, slots, L0, kk, vv, tks[layer])
+        dc.append(cl, slots, L0, kk, vv, tks[cl])
         del kk, vv
     torch.cuda.synchronize()
     build_s = time.perf_counter() - t_build
@@ -557,17 +622,21 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
 
     def layer_call(st, layer):
         k1, v1, q = steps_in[st][layer]
+        cl = (st % copies) * w.n_layers + layer   # the copy this step runs on
         if fused:
-            dc.decode_step(layer, slots, k1, v1, tks[layer], q, tqs[layer], out)
+            dc.decode_step(cl, slots, k1, v1, tks[cl], q, tqs[cl], out)
         else:
-            dc.append(layer, slots, [1] * B, k1, v1, tks[layer])
-            dc.decode_attn(layer, slots, q, tqs[layer], out)
+            dc.append(cl, slots, [1] * B, k1, v1, tks[cl])
+            dc.decode_attn(cl, slots, q, tqs[cl], out)
 
-    # HIP events bracketing every split launch of pass B, created and recorded
-    # once beforehand so that the timed loop only records them
-    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # HIP events bracketing every split launch and every combine launch of
+    # pass B, created and recorded once beforehand so that the timed loop only
+    # records them
+    def event_pairs():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(K * w.n_layers)]
-    for e0, e1 in ev_pairs:
+    ev_pairs, ev_comb = event_pairs(), event_pairs()
+    for e0, e1 in ev_pairs + ev_comb:
         e0.record(stream)
         e1.record(stream)
     torch.cuda.synchronize()
@@ -586,11 +655,14 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
             for layer in range(w.n_layers):
                 if instrument:
                     e0, e1 = ev_pairs[i]
+                    c0, c1 = ev_comb[i]
                     i += 1
                     wk.wushkv_set_split_events(dc.handle, e0.cuda_event, e1.cuda_event)
+                    wk.wushkv_set_combine_events(dc.handle, c0.cuda_event, c1.cuda_event)
                 layer_call(st, layer)
                 if instrument:
                     wk.wushkv_set_split_events(dc.handle, None, None)
+                    wk.wushkv_set_combine_events(dc.handle, None, None)
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
@@ -598,15 +670,17 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
     # pass A: the step metric, no instrumentation in the stream
     total_ms = timed_pass(W, False)
     ms_per_step = total_ms / K
-    # pass B: the same steps continued, split kernel bracketed by HIP events
+    # pass B: the same steps continued, split and combine kernels bracketed by
+    # HIP events
     total_b_ms = timed_pass(W + K, True)
     split_ms = [a.elapsed_time(b) for a, b in ev_pairs]
+    comb_ms = [a.elapsed_time(b) for a, b in ev_comb]
 
     # algorithmic bytes of the attention reads over the timed steps of pass A
     bytes_total = 0
     for st in range(W, W + K):
         for s in range(B):
-            Lnow = L0[s] + st + 1
+            Lnow = L0[s] + st // copies + 1   # length of the copy step st runs on
             bytes_total += w.n_layers * w.n_kv * unit_bytes(Lnow, S, R, F, bits, fused)
     bytes_per_step = bytes_total / K
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
@@ -614,9 +688,19 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
     bytes_b = 0
     for st in range(W + K, W + 2 * K):
         for s in range(B):
-            bytes_b += w.n_layers * w.n_kv * unit_bytes(L0[s] + st + 1, S, R, F, bits, fused)
+            bytes_b += w.n_layers * w.n_kv * unit_bytes(L0[s] + st // copies + 1, S, R, F, bits,
+                                                       fused)
     bytes_per_launch = bytes_b / (K * w.n_layers)
-    split_avg_ms = float(np.mean(split_ms))
+    # An event bracket adds its own dispatch gap to the kernel it surrounds.
+    # The excess of the two bracketed means over the uninstrumented layer time
+    # of pass A is split evenly between the two brackets, so that the two
+    # kernels' figures add up to the layer time of pass A.
+    split_ev_ms = float(np.mean(split_ms))
+    comb_ev_ms = float(np.mean(comb_ms))
+    layer_ms = ms_per_step / w.n_layers
+    excess = max(0.0, (split_ev_ms + comb_ev_ms - layer_ms) / 2) if comb_ev_ms > 0 else 0.0
+    split_avg_ms = split_ev_ms - excess
+    comb_avg_ms = max(0.0, comb_ev_ms - excess)
     achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
     append_tok_s = B * w.n_layers * K / (total_ms * 1e-3)
 
@@ -624,6 +708,7 @@ def measure_decode(w, bits, K, W, dev, fused, page_size=0, page_seed=None):
     del dc, steps_in, out
     torch.cuda.empty_cache()
     return dict(ms_per_step=ms_per_step, value=value, achieved=achieved, split_avg_ms=split_avg_ms,
+                split_ev_ms=split_ev_ms, comb_ev_ms=comb_ev_ms, comb_avg_ms=comb_avg_ms,
                 bytes_per_launch=bytes_per_launch, total_b_ms=total_b_ms,
                 append_tok_s=append_tok_s, build_s=build_s, launches=n_launches,
                 n_pages=paging.get("n_pages"))
@@ -760,7 +845,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "int4-digit dot8, fp32 softmax",
         "data": "synthetic",
         "config": {"workload": w.name, "n_layers": w.n_layers, "n_q_heads": w.n_q,
                    "n_kv_heads": w.n_kv, "head_dim": 128, "batch": B,
@@ -777,8 +862,16 @@ def main():
                                + (", fused one-token append)" if fused else ")"),
                      "bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(split_avg_ms, 5), "launches": n_launches,
-                     "timing": "HIP events around every split launch of a second timed pass of "
-                               f"{K} steps ({round(total_b_ms / K, 4)} ms/step with the events)"},
+                     "events_avg_ms": round(m["split_ev_ms"], 5),
+                     "combine_avg_ms": round(m["comb_avg_ms"], 5),
+                     "combine_events_avg_ms": round(m["comb_ev_ms"], 5),
+                     "layers_x_split_plus_combine_ms": round(
+                         w.n_layers * (split_avg_ms + m["comb_avg_ms"]), 4),
+                     "timing": "HIP events around every split launch and every combine launch of "
+                               f"a second timed pass of {K} steps ({round(total_b_ms / K, 4)} "
+                               "ms/step with the events); the excess of the two bracketed means "
+                               "over the layer time of the uninstrumented pass is taken off both "
+                               "evenly (events_avg_ms is the split launch's bracketed mean)"},
         "cache_build_s": round(build_s, 2),
     }
     def variant(m, note, **extra):
@@ -814,18 +907,28 @@ def main():
     if not args.no_workloads:
         # every workload's full decode step (all layers, the whole batch), pass A only
         rows = []
-        for wid, b in ((0, 2), (1, 2), (2, 2), (4, 2), (4, 4)):
+        for wid, b, copies in ((0, 2, 1), (1, 2, 1), (1, 2, 24), (2, 2, 1), (4, 2, 1), (4, 4, 1)):
             wl = synth.WORKLOADS[wid]
             # single-layer workloads: enough steps that launch jitter averages out
-            mm = measure_decode(wl, b, 3 if wl.n_layers > 1 else 40, 1, dev, True)
+            mm = measure_decode(wl, b, 3 if wl.n_layers > 1 else 48, 1, dev, True, copies=copies)
             Bw = len(wl.lengths())
-            rows.append({"workload": wl.name, "bits": b, "ms_per_step": round(mm["ms_per_step"], 4),
-                         "cache_gbs": round(mm["value"], 1),
-                         "hbm_frac": round(mm["value"] / HBM_PEAK_GBS, 4),
-                         "tokens_per_s": round(Bw / (mm["ms_per_step"] * 1e-3), 1),
-                         "layers": wl.n_layers, "batch": Bw,
-                         "attention": "int8 matrix cores (one-position chunk steps)"
-                         if wl.group == 8 else "split kernel (v_dot8)"})
+            cache_mb = sum(wl.n_kv * unit_bytes(t, wl.sink, wl.recent, wl.flush, b)
+                           for t in wl.lengths()) * wl.n_layers / 1e6
+            row = {"workload": wl.name, "bits": b, "ms_per_step": round(mm["ms_per_step"], 4),
+                   "cache_gbs": round(mm["value"], 1),
+                   "hbm_frac": round(mm["value"] / HBM_PEAK_GBS, 4),
+                   "tokens_per_s": round(Bw / (mm["ms_per_step"] * 1e-3), 1),
+                   "layers": wl.n_layers, "batch": Bw, "cache_mb_read_per_step": round(cache_mb, 2),
+                   "attention": "int8 matrix cores (one-position chunk steps)"
+                   if wl.group == 8 else "split kernel (v_dot8)"}
+            if cache_mb * copies < 256:
+                row["residency"] = ("last-level-cache resident: the whole cache fits the 256 MB "
+                                    "Infinity Cache and is re-read from it every step; not an "
+                                    "HBM figure")
+            elif copies > 1:
+                row["residency"] = (f"HBM: steps rotate over {copies} copies of the cache "
+                                    f"({cache_mb * copies:.0f} MB, above the 256 MB Infinity Cache)")
+            rows.append(row)
         res["workloads"] = rows
     if not args.no_chunk:
         res["chunk_step"] = [chunk_rate(wid, dev) for wid in sorted({args.workload, 1})
@@ -833,6 +936,9 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_seconds, max_units=400,
                                            threads=args.cpu_threads)
+        res["cpu_baseline"]["host_cores"] = os.cpu_count()
+        res["cpu_baseline"]["host_cores_usable"] = len(os.sched_getaffinity(0))
+        res["cpu_baseline"]["per_config"] = oracle_per_config()
     print(json.dumps(res), flush=True)
 
 

@@ -25,7 +25,7 @@ WUSHKV_MAX_SEQ_PER_CALL = 128
 EXPORTS = (
     "wushkv_config_check", "wushkv_layout", "wushkv_cache_create", "wushkv_cache_destroy",
     "wushkv_reset_seq", "wushkv_get_len", "wushkv_quantized_range", "wushkv_append", "wushkv_decode_workspace_bytes",
-    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_decode_step_noalloc", "wushkv_set_split_events",
+    "wushkv_decode_attn", "wushkv_decode_step", "wushkv_decode_step_noalloc", "wushkv_set_split_events", "wushkv_set_combine_events",
     "wushkv_stream_read_probe", "wushkv_gaussian_alpha", "wushkv_set_block_table",
     "wushkv_chunk_workspace_bytes", "wushkv_chunk_step", "wushkv_status_str",
 )
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.wushkv_set_block_table.argtypes = [P, P]
     L.wushkv_set_split_events.restype = ctypes.c_int
     L.wushkv_set_split_events.argtypes = [P, P, P]
+    L.wushkv_set_combine_events.restype = ctypes.c_int
+    L.wushkv_set_combine_events.argtypes = [P, P, P]
     L.wushkv_gaussian_alpha.restype = ctypes.c_double
     L.wushkv_gaussian_alpha.argtypes = [i32]
     L.wushkv_stream_read_probe.restype = ctypes.c_int
@@ -282,3 +284,8 @@ def wushkv_set_block_table(cache: int, table_ptr: int) -> None:
 def wushkv_set_split_events(cache: int, ev_start: int | None, ev_stop: int | None) -> None:
     _check(lib().wushkv_set_split_events(ctypes.c_void_p(cache), ctypes.c_void_p(ev_start or 0),
                                          ctypes.c_void_p(ev_stop or 0)), "wushkv_set_split_events")
+
+
+def wushkv_set_combine_events(cache: int, ev_start: int | None, ev_stop: int | None) -> None:
+    _check(lib().wushkv_set_combine_events(ctypes.c_void_p(cache), ctypes.c_void_p(ev_start or 0),
+                                           ctypes.c_void_p(ev_stop or 0)), "wushkv_set_combine_events")

@@ -18,7 +18,8 @@ struct wushkv_cache {
   uint8_t* arena;
   const int32_t* table = nullptr;  // paged caches: device block table [max_batch][pages_per_seq]
   std::vector<int32_t> len;  // [n_layers][max_batch]
-  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;    // around the split-K scan launch
+  hipEvent_t ev_cstart = nullptr, ev_cstop = nullptr;  // around the combine launch
 };
 
 static uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -465,7 +466,7 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   int need = G >= 4 ? max_sub : (max_sub + 3) / 4;
   a.n_splits = need < cap ? need : cap;
   hipError_t e = launch_decode(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream,
-                               c->ev_start, c->ev_stop);
+                               c->ev_start, c->ev_stop, c->ev_cstart, c->ev_cstop);
   if (e != hipSuccess) return WUSHKV_EDEVICE;
   if (step)
     for (int i = 0; i < n_seq; ++i) c->len[(size_t)layer * c->cfg.max_batch + slots[i]] += 1;
@@ -591,6 +592,13 @@ extern "C" wushkv_status wushkv_set_split_events(wushkv_cache* c, void* ev_start
   if (!c || (!ev_start) != (!ev_stop)) return WUSHKV_EINVAL;
   c->ev_start = (hipEvent_t)ev_start;
   c->ev_stop = (hipEvent_t)ev_stop;
+  return WUSHKV_OK;
+}
+
+extern "C" wushkv_status wushkv_set_combine_events(wushkv_cache* c, void* ev_start, void* ev_stop) {
+  if (!c || (!ev_start) != (!ev_stop)) return WUSHKV_EINVAL;
+  c->ev_cstart = (hipEvent_t)ev_start;
+  c->ev_cstop = (hipEvent_t)ev_stop;
   return WUSHKV_OK;
 }
 

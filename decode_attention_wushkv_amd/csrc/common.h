@@ -42,8 +42,9 @@ __host__ __device__ inline int max_chunks(int n_seq, int n_kv) {
 // a 128-position sub-chunk as WDIG unsigned ones (16 bits).  A score's error
 // is the query's rounding error dotted with the key's codes times its scale,
 // so it grows with the key's range; 16-bit queries exceeded the 2e-3 output
-// bar on keys scaled x30 or holding constant rows of 1024, 24 bits keep it
-// below.
+// bar on keys scaled x30 or holding constant rows of 1024, and 20-bit ones on
+// 4-bit RMS-coded groups around 1024 (2.1 times the bar); 24 bits keep every
+// tested case below a third of it.
 constexpr int QDIG = 6;
 constexpr int WDIG = 4;
 constexpr int DIGP = 8;  // query digit words per group of 8 dimensions (padded for 16-byte loads)
@@ -213,7 +214,7 @@ hipError_t launch_prefill(const AppendArgs& a, int grid_x, int n_seq, hipStream_
 bool prefill_supported(int codec, double p_lo, double p_hi);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int blocks, void* out, hipStream_t st);
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
-                         hipEvent_t ev_stop);
+                         hipEvent_t ev_stop, hipEvent_t ev_cstart, hipEvent_t ev_cstop);
 // Device address and size of the current device's file-scope scratch array
 // (wushkv_decode_step_noalloc's workspace).
 hipError_t noalloc_scratch(void** ptr, uint64_t* bytes);

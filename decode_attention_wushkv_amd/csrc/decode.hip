@@ -1066,9 +1066,11 @@ __device__ __forceinline__ int run_start(int64_t nsub, int j, int n) {
 }
 
 // PREP: the query block comes from the prep kernel (else every workgroup
-// prepares the query itself).
+// prepares the query itself).  Three waves per SIMD at G = 4 for 3- and 4-bit
+// codes; at 2 bits the head split needs more than 168 registers per lane
+// (it spilled, 40% slower), so two.
 template <int IO_BF16, int BITS, int G, bool PREP>
-__global__ __launch_bounds__(256, G == 4 ? 3 : 2) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
   uint32_t* sm = (uint32_t*)smem4;
@@ -1418,7 +1420,7 @@ hipError_t launch_split_g(DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t ev_start,
-                         hipEvent_t ev_stop) {
+                         hipEvent_t ev_stop, hipEvent_t ev_cstart, hipEvent_t ev_cstop) {
   hipError_t e;
   if (ev_start && (e = hipEventRecord(ev_start, st)) != hipSuccess) return e;
   if (io_bf16)
@@ -1429,8 +1431,11 @@ hipError_t launch_decode(DecodeArgs& a, int io_bf16, hipStream_t st, hipEvent_t 
       : a.g.bits == 3 ? launch_split_g<0, 3>(a, st) : launch_split_g<0, 4>(a, st);
   if (e != hipSuccess) return e;
   if (ev_stop && (e = hipEventRecord(ev_stop, st)) != hipSuccess) return e;
+  if (ev_cstart && (e = hipEventRecord(ev_cstart, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.g.n_q, a.n_seq), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev_cstop && (e = hipEventRecord(ev_cstop, st)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace wkv

@@ -351,6 +351,13 @@ wushkv_status wushkv_chunk_step(wushkv_cache* cache, int32_t layer, int32_t n_se
  * time that kernel alone.  Pass NULL, NULL to stop.  Host only. */
 wushkv_status wushkv_set_split_events(wushkv_cache* cache, void* ev_start, void* ev_stop);
 
+/* Instrumentation, not part of the method: as wushkv_set_split_events, for
+ * the log-sum-exp combine kernel that follows the split-K scan in
+ * wushkv_decode_attn and wushkv_decode_step (ev_start immediately before its
+ * launch, ev_stop immediately after).  Pass NULL, NULL to stop.  Host only;
+ * EINVAL when exactly one of the two is NULL. */
+wushkv_status wushkv_set_combine_events(wushkv_cache* cache, void* ev_start, void* ev_stop);
+
 /* Instrumentation, not part of the method: read bytes (a multiple of 16) of
  * the 16-byte-aligned device buffer buf once with a grid-stride kernel of
  * `blocks` workgroups of 256 threads, writing one word per thread to out

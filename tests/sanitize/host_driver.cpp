@@ -57,7 +57,7 @@ hipError_t launch_stream_read(const void*, uint64_t, int, void*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_decode(DecodeArgs& a, int, hipStream_t, hipEvent_t, hipEvent_t) {
+hipError_t launch_decode(DecodeArgs& a, int, hipStream_t, hipEvent_t, hipEvent_t, hipEvent_t, hipEvent_t) {
   ++g_launches;
   CHECK(a.n_seq >= 1 && a.n_seq <= MAXSEQ);
   CHECK(a.n_splits >= 0 && a.n_splits <= max_chunks(a.n_seq, a.g.n_kv));

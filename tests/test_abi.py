@@ -359,3 +359,19 @@ def test_decode_step_noalloc_limits():
     for s in range(4):
         assert wk.wushkv_get_len(h, 0, s) == (0, 4)
     wk.wushkv_cache_destroy(h)
+
+
+def test_event_hooks_check_arguments():
+    """Both instrumentation hooks take two events or none (host-only calls)."""
+    h, _ = _fake_cache()
+    E = 1 << 41
+    for fn in (wk.wushkv_set_split_events, wk.wushkv_set_combine_events):
+        with pytest.raises(wk.WushkvError):
+            fn(h, E, None)
+        with pytest.raises(wk.WushkvError):
+            fn(h, None, E)
+        with pytest.raises(wk.WushkvError):
+            fn(0, E, E)
+        fn(h, E, E)
+        fn(h, None, None)
+    wk.wushkv_cache_destroy(h)
