@@ -29,11 +29,12 @@
 // p_hi (n - 1) >= 125; the host falls back to the rank-sort kernel otherwise).
 // With the RMS codec the clip ends are -alpha rms, +alpha rms instead (sum of
 // squares per half-group in fp64, as in quant.h).  Scale, zero and levels
-// follow quant.h exactly.  Key codes are stored by the group's lanes; value
-// codes go to LDS as bytes, and while the key waves quantize the keys, one
-// value-wave thread per 16-byte value-code row assembles its words from them
-// and writes the row whole (no atomics: 16 lanes OR-ing into one word
-// serialize).
+// follow quant.h exactly.  The four key waves quantize the tile's key groups
+// while the four value waves quantize its value groups.  Key codes are stored
+// by the group's lanes; value codes go to LDS as bytes, and during the next
+// tile's transform one thread per 16-byte value-code row assembles its words
+// from them and writes the row whole (no atomics: 16 lanes OR-ing into one
+// word serialize).  Three barriers per tile.
 #include <type_traits>
 
 #include "quant.h"
@@ -52,6 +53,7 @@ constexpr int RS = 136;           // LDS row stride (bf16 elements) of the key /
 constexpr int TS = 132;           // LDS row stride (floats) of T_K
 constexpr int VCS = 132;          // LDS row stride (bytes) of the value-code bytes
 constexpr int FIXMAX = PT * D;    // recomputation list capacity (every entry of a tile)
+constexpr int FIXW = FIXMAX / (NT / 64);  // one wave's segment (its 16 dimensions of 64 rows)
 // fp32 summation error bound of the transform relative to sum_j |k_j| |T_ij|,
 // counting one ulp (2^-23) per rounding whatever order and rounding the
 // matrix core uses inside an instruction: 15 roundings inside each 16-product
@@ -66,9 +68,8 @@ struct __align__(16) PLds {
   uint16_t ka[PT * RS];   // their magnitudes |k|
   uint16_t v[PT * RS];    // values (bf16)
   uint16_t kq[PT * RS];   // transformed keys (bf16)
-  uint16_t fix[FIXMAX];   // entries to recompute: row << 7 | dimension
+  uint16_t fix[FIXMAX];   // entries to recompute, one segment per wave: row << 7 | dimension
   uint8_t vc[PT * VCS];   // value codes of the tile, [position][dimension]
-  int nfix;
 };
 
 __device__ __forceinline__ __bf16 bf16_of_bits(uint32_t b) {
@@ -410,6 +411,92 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
     }
   };
 
+  // value-code rows of the tile at p0 (codes as bytes in L.vc), one thread
+  // per row of 16 bytes (2 and 4 bits: block row of one dimension; 3 bits:
+  // the tile's low-plane row, or its half of the block's high-plane row);
+  // codes of positions outside the tile's quantized range are masked out
+  auto rows = [&](int p0, int64_t trow) {
+    constexpr int NROW = BITS == 3 ? 2 * D : (PT / VB) * D;
+    for (int x = tid; x < NROW; x += NT) {
+      if (trow < 0) break;
+      const int dim = x & (D - 1), blk = x >> 7;  // blk: block (2, 4 bits) or plane (3 bits)
+      if (BITS != 3 || blk == 0) {
+        constexpr int WPOS = BITS == 4 ? 8 : 16;  // positions per word
+        constexpr int SH = BITS == 4 ? 4 : 2;
+        const int b0 = p0 + (BITS == 3 ? 0 : blk * VB);
+        const int nb = BITS == 3 ? PT : VB;
+        const int lo = max(b0, max(c0, qlo)), hi = min(b0 + nb, min(c1, qhi));
+        if (lo >= hi) continue;
+        uint32_t wd[4], m[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t word = 0u;
+#pragma unroll
+          for (int n = 0; n < WPOS; ++n) {
+            const int t = (b0 - p0) + q * WPOS + n;
+            const uint32_t code = L.vc[t * VCS + dim];
+            word |= (BITS == 3 ? (code & 3u) : code) << (n * SH);
+          }
+          wd[q] = word;
+          const int bl = (lo - b0) * SH - 32 * q, bh = (hi - b0) * SH - 32 * q;
+          const int l2 = bl < 0 ? 0 : (bl > 32 ? 32 : bl), h2 = bh < 0 ? 0 : (bh > 32 ? 32 : bh);
+          m[q] = h2 <= l2 ? 0u : ((h2 - l2 >= 32 ? 0xFFFFFFFFu : ((1u << (h2 - l2)) - 1u)) << l2);
+        }
+        uint4* dst;
+        if constexpr (BITS == 3)
+          dst = (uint4*)(a.pl.vcode + ((3 * (trow >> 7) + ((trow & 127) >> 6)) * D + dim) * 16);
+        else
+          dst = (uint4*)(a.pl.vcode + ((trow / VB + blk) * D + dim) * 16);
+        uint4 row = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        if ((m[0] & m[1] & m[2] & m[3]) != 0xFFFFFFFFu) {
+          const uint4 old = *dst;
+          row.x = (old.x & ~m[0]) | (row.x & m[0]);
+          row.y = (old.y & ~m[1]) | (row.y & m[1]);
+          row.z = (old.z & ~m[2]) | (row.z & m[2]);
+          row.w = (old.w & ~m[3]) | (row.w & m[3]);
+        }
+        *dst = row;
+      } else {
+        // 3 bits: high-plane words of the tile (positions 32 hw .. 32 hw + 31
+        // at bit hi_bit(t)); 8 bytes, no other tile writes them
+        const int lo = max(p0, max(c0, qlo)), hi = min(p0 + PT, min(c1, qhi));
+        if (lo >= hi) continue;
+        uint32_t wd[2];
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+          uint32_t word = 0u;
+#pragma unroll
+          for (int n = 0; n < 32; ++n) {
+            const int t = 32 * hw + n;
+            const uint32_t code = L.vc[t * VCS + dim];
+            word |= (code >> 2) << (hi_bit(t) & 31);
+          }
+          wd[hw] = word;
+        }
+        uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
+        if (lo > p0 || hi < p0 + PT) {
+          m0 = m1 = 0u;
+          for (int t = lo - p0; t < hi - p0; ++t) {
+            const int hb = hi_bit(t);
+            if (hb < 32) m0 |= 1u << hb;
+            else m1 |= 1u << (hb - 32);
+          }
+        }
+        const int sel = (int)((trow & 127) >> 6);
+        uint2* dst = (uint2*)(a.pl.vcode + ((3 * (trow >> 7) + 2) * D + dim) * 16 + 8 * sel);
+        uint2 row = make_uint2(wd[0], wd[1]);
+        if ((m0 & m1) != 0xFFFFFFFFu) {
+          const uint2 old = *dst;
+          row.x = (old.x & ~m0) | (row.x & m0);
+          row.y = (old.y & ~m1) | (row.y & m1);
+        }
+        *dst = row;
+      }
+    }
+  };
+
+  int64_t prev_trow = -1;  // the previous tile, whose value-code rows are still to be written
+  int prev_p0 = -1;
   for (; p0 < c1; p0 += PT) {
     // quantized-plane row of the tile's first position (a tile never crosses
     // a page); -1 when its page is unmapped, and then no code is stored
@@ -424,9 +511,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
             make_uint4(pre[u].x & 0x7FFF7FFFu, pre[u].y & 0x7FFF7FFFu, pre[u].z & 0x7FFF7FFFu,
                        pre[u].w & 0x7FFF7FFFu);
     }
-    if (tid == 0) L.nfix = 0;
     __syncthreads();
     if (p0 + PT < c1) load_tile(p0 + PT);
+    if (prev_p0 >= 0) rows(prev_p0, prev_trow);  // L.vc still holds the previous tile's codes
 
     // ---- transform on the matrix cores (all waves); flag entries near a
     // rounding boundary
@@ -493,8 +580,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
         }
       }
       flags &= inr;
-      // compaction of the wave's flagged entries into the list: exclusive
-      // prefix of the per-lane counts from one ballot per count bit
+      // the wave's flagged entries into its own segment of the list (exclusive
+      // prefix of the per-lane counts from one ballot per count bit), then
+      // recomputed four lanes to an entry, lane q running chain q
       const int cnt = __popc(flags);
       int before = 0, total = 0;
 #pragma unroll
@@ -503,147 +591,57 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
         before += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
         total += __popcll(m) << b;
       }
-      if (total > 0) {
-        int slot = 0;
-        if (lane == 0) slot = atomicAdd(&L.nfix, total);
-        slot = __shfl(slot, 0) + before;
-        while (flags) {
-          const int r = __ffs(flags) - 1;
-          flags &= flags - 1u;
-          const int t = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
-          L.fix[slot++] = (uint16_t)((t << 7) | i_out);
-        }
+      uint16_t* fl = L.fix + w * FIXW;
+      while (flags) {
+        const int r = __ffs(flags) - 1;
+        flags &= flags - 1u;
+        const int t = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
+        fl[before++] = (uint16_t)((t << 7) | i_out);
       }
-    }
-    __syncthreads();
-
-    if (!vwave) {
-      // ---- key waves: recompute flagged entries with transform_entry's
-      // arithmetic (four fp64 FMA chains over dimensions [32 q, 32 q + 32)
-      // in order, joined as (s0 + s1) + (s2 + s3))
-      const int nf = L.nfix;
-      for (int x = rt; x < nf; x += NT / 2) {
-        const int t = L.fix[x] >> 7, i = L.fix[x] & (D - 1);
-        const uint16_t* kr = L.k + t * RS;
-        const float* tr = L.t + i * TS;
-        double s[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
+      // the list's writes before any lane of the wave reads it
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // transform_entry's arithmetic: four fp64 FMA chains over dimensions
+      // [32 q, 32 q + 32) in order, joined as (s0 + s1) + (s2 + s3)
+      for (int base = 0; base < total; base += 16) {
+        const int k = base + (lane >> 2), q = lane & 3;
+        const int e = k < total ? fl[k] : 0;
+        const int t = e >> 7, i = e & (D - 1);
+        const float* tr = L.t + i * TS + 32 * q;
+        const uint16_t* kr = L.k + t * RS + 32 * q;
+        double sq = 0.0;
+#pragma unroll
         for (int c = 0; c < 4; ++c) {
-          // the chunk's T_K and key values of all four chains, then the FMAs
-          float4 ta[4], tb[4];
-          uint4 kk[4];
+          const float4 ta = *(const float4*)(tr + 8 * c);
+          const float4 tb = *(const float4*)(tr + 8 * c + 4);
+          const uint4 kk = *(const uint4*)(kr + 8 * c);
+          const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+          const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            ta[q] = *(const float4*)(tr + 32 * q + 8 * c);
-            tb[q] = *(const float4*)(tr + 32 * q + 8 * c + 4);
-            kk[q] = *(const uint4*)(kr + 32 * q + 8 * c);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float tv[8] = {ta[q].x, ta[q].y, ta[q].z, ta[q].w, tb[q].x, tb[q].y, tb[q].z, tb[q].w};
-            const uint32_t kw[4] = {kk[q].x, kk[q].y, kk[q].z, kk[q].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[q] = fma((double)tv[e], (double)bf16_lane(kw, e), s[q]);
-          }
+          for (int j = 0; j < 8; ++j) sq = fma((double)tv[j], (double)bf16_lane(kw, j), sq);
         }
-        L.kq[t * RS + i] = f64_to_bf16((s[0] + s[1]) + (s[2] + s[3]));
+        const double pair = sq + partner_d<0xB1>(sq);  // lanes q = 0, 2: s0 + s1, s2 + s3
+        const double y = pair + partner_d<0x4E>(pair);  // lane q = 0: (s0 + s1) + (s2 + s3)
+        if (q == 0 && k < total) L.kq[t * RS + i] = f64_to_bf16(y);
       }
-    } else {
-      // ---- value waves: windows and quantization of the values
-      windows(true, p0);
-      quant_group(std::integral_constant<bool, true>{}, p0, trow);
     }
     __syncthreads();
 
+    // ---- windows and quantization: the key waves take the 64 key groups,
+    // the value waves the 64 value groups
     if (!vwave) {
-      // ---- key waves: windows and quantization of the keys
       windows(false, p0);
       quant_group(std::integral_constant<bool, false>{}, p0, trow);
     } else {
-      // ---- value waves: value-code rows, one thread per row of 16 bytes
-      // (2 and 4 bits: block row of one dimension; 3 bits: the tile's
-      // low-plane row, or its half of the block's high-plane row); codes of
-      // positions outside the tile's quantized range are masked out
-      constexpr int NROW = BITS == 3 ? 2 * D : (PT / VB) * D;
-      for (int x = rt; x < NROW; x += NT / 2) {
-        if (trow < 0) break;
-        const int dim = x & (D - 1), blk = x >> 7;  // blk: block (2, 4 bits) or plane (3 bits)
-        if (BITS != 3 || blk == 0) {
-          constexpr int WPOS = BITS == 4 ? 8 : 16;  // positions per word
-          constexpr int SH = BITS == 4 ? 4 : 2;
-          const int b0 = p0 + (BITS == 3 ? 0 : blk * VB);
-          const int nb = BITS == 3 ? PT : VB;
-          const int lo = max(b0, max(c0, qlo)), hi = min(b0 + nb, min(c1, qhi));
-          if (lo >= hi) continue;
-          uint32_t wd[4], m[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t word = 0u;
-#pragma unroll
-            for (int n = 0; n < WPOS; ++n) {
-              const int t = (b0 - p0) + q * WPOS + n;
-              const uint32_t code = L.vc[t * VCS + dim];
-              word |= (BITS == 3 ? (code & 3u) : code) << (n * SH);
-            }
-            wd[q] = word;
-            const int bl = (lo - b0) * SH - 32 * q, bh = (hi - b0) * SH - 32 * q;
-            const int l2 = bl < 0 ? 0 : (bl > 32 ? 32 : bl), h2 = bh < 0 ? 0 : (bh > 32 ? 32 : bh);
-            m[q] = h2 <= l2 ? 0u : ((h2 - l2 >= 32 ? 0xFFFFFFFFu : ((1u << (h2 - l2)) - 1u)) << l2);
-          }
-          uint4* dst;
-          if constexpr (BITS == 3)
-            dst = (uint4*)(a.pl.vcode + ((3 * (trow >> 7) + ((trow & 127) >> 6)) * D + dim) * 16);
-          else
-            dst = (uint4*)(a.pl.vcode + ((trow / VB + blk) * D + dim) * 16);
-          uint4 row = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-          if ((m[0] & m[1] & m[2] & m[3]) != 0xFFFFFFFFu) {
-            const uint4 old = *dst;
-            row.x = (old.x & ~m[0]) | (row.x & m[0]);
-            row.y = (old.y & ~m[1]) | (row.y & m[1]);
-            row.z = (old.z & ~m[2]) | (row.z & m[2]);
-            row.w = (old.w & ~m[3]) | (row.w & m[3]);
-          }
-          *dst = row;
-        } else {
-          // 3 bits: high-plane words of the tile (positions 32 hw .. 32 hw + 31
-          // at bit hi_bit(t)); 8 bytes, no other tile writes them
-          const int lo = max(p0, max(c0, qlo)), hi = min(p0 + PT, min(c1, qhi));
-          if (lo >= hi) continue;
-          uint32_t wd[2];
-#pragma unroll
-          for (int hw = 0; hw < 2; ++hw) {
-            uint32_t word = 0u;
-#pragma unroll
-            for (int n = 0; n < 32; ++n) {
-              const int t = 32 * hw + n;
-              const uint32_t code = L.vc[t * VCS + dim];
-              word |= (code >> 2) << (hi_bit(t) & 31);
-            }
-            wd[hw] = word;
-          }
-          uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
-          if (lo > p0 || hi < p0 + PT) {
-            m0 = m1 = 0u;
-            for (int t = lo - p0; t < hi - p0; ++t) {
-              const int hb = hi_bit(t);
-              if (hb < 32) m0 |= 1u << hb;
-              else m1 |= 1u << (hb - 32);
-            }
-          }
-          const int sel = (int)((trow & 127) >> 6);
-          uint2* dst = (uint2*)(a.pl.vcode + ((3 * (trow >> 7) + 2) * D + dim) * 16 + 8 * sel);
-          uint2 row = make_uint2(wd[0], wd[1]);
-          if ((m0 & m1) != 0xFFFFFFFFu) {
-            const uint2 old = *dst;
-            row.x = (old.x & ~m0) | (row.x & m0);
-            row.y = (old.y & ~m1) | (row.y & m1);
-          }
-          *dst = row;
-        }
-      }
+      windows(true, p0);
+      quant_group(std::integral_constant<bool, true>{}, p0, trow);
     }
     __syncthreads();  // LDS tiles are rewritten by the next iteration
+    prev_p0 = p0;
+    prev_trow = trow;
   }
+  if (prev_p0 >= 0) rows(prev_p0, prev_trow);
 }
 
 }  // namespace
