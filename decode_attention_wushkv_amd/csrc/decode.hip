@@ -1369,7 +1369,7 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
   //  - otherwise, for long single launches with few units: the grid fills the
   //    resident capacity once, query preparation in every workgroup;
   //  - otherwise the query is prepared once per unit in the prep kernel and
-  //    the grid is oversubscribed ~4.5x, so that the dispatcher balances
+  //    the grid is oversubscribed ~6x, so that the dispatcher balances
   //    workgroups of unequal length (ragged batches, many units) and the
   //    window workgroup's chain stays short.
   const int units = a.n_seq * a.g.n_kv;
@@ -1390,7 +1390,7 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     const double bytes = (double)a.total_sub * SplitCfg<BITS, G>::TW * (32.0 * BITS + 8.0);
     prep = a.max_sub >= 16 && (bytes < 240e6 || 9 * units > slots);
     if (prep) {
-      const int target = (9 * slots) / (2 * units) - 1;
+      const int target = (6 * slots) / units - 1;
       if (target > fill) fill = target;
     }
     if (a.n_splits > fill) a.n_splits = fill;
