@@ -13,20 +13,21 @@
 // exact products, summed by the matrix cores in fp32: T1 products in eight
 // v_mfma_f32_16x16x16_bf16 of 16 folded into one fp32 sum, T2 and T3 products
 // in one v_mfma_f32_16x16x32_bf16 chain.  The fp32 error of the sum is below
-// 20 ulp (2^-23 each) of
-// A = sum_j |k_j| |T_ij|, which a fourth MFMA chain (|k| times |T1|) bounds.
-// An entry whose fp32 value lies within that bound of a bfloat16 rounding
-// boundary is recomputed in fp64 with the arithmetic of the one-position paths (transform_entry; about 2 per cent of the entries,
-// by the four key waves while the four value waves quantize the values), so
-// the stored bfloat16 keys are identical to theirs.
+// 20 ulp (2^-23 each) of A = sum_j |k_j| |T_ij|, which a fourth MFMA chain
+// (|k| times |T1|) bounds.  An entry whose fp32 value lies within that bound of
+// a bfloat16 rounding boundary is recomputed in fp64 with the arithmetic of the
+// one-position paths (transform_entry; about 2 per cent of the entries, each by
+// the wave that flagged it, four lanes to an entry), so the stored bfloat16
+// keys are identical to theirs.
 //
 // Quantization.  Each group (one position's 128 key or value entries) is
 // split over four lanes.  A lane scans its 32 entries keeping the three
 // smallest and three largest (v_med3 insertion), the four merge them in two
 // DPP rounds, and the order statistics around h = p (n - 1) give the
 // linear-interpolation percentiles.  This covers clip percentiles whose
-// interpolation needs only the three smallest and three largest values (p_lo (n - 1) < 2 and
-// p_hi (n - 1) >= 125; the host falls back to the rank-sort kernel otherwise).
+// interpolation needs only the three smallest and three largest values
+// (p_lo (n - 1) < 2 and p_hi (n - 1) >= 125; the host falls back to the
+// rank-sort kernel otherwise).
 // With the RMS codec the clip ends are -alpha rms, +alpha rms instead (sum of
 // squares per half-group in fp64, as in quant.h).  Scale, zero and levels
 // follow quant.h exactly.  The four key waves quantize the tile's key groups
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(AppendArgs a) {
   const int jlo = (int)floor(hlo), jhi = (int)floor(hhi);
   const double flo = hlo - floor(hlo), fhi = hhi - floor(hhi);
 
-  // ---- T_K of this head into LDS; MFMA operands of this wave's 32 output dims
+  // ---- T_K of this head into LDS; MFMA operands of this wave's 16 output dims
   {
     const float4* tg = (const float4*)(a.tk + (int64_t)h * D * D);
     for (int x = tid; x < D * D / 4; x += NT) {
