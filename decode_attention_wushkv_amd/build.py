@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libwushkv.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "append.hip", "decode.hip", "prefill.hip", "chunk.hip", "probe.hip", "noalloc.hip")]
-HEADERS = [os.path.join(HERE, "csrc", h) for h in ("common.h", "quant.h", "chunk.h")] + [
+HEADERS = [os.path.join(HERE, "csrc", h) for h in ("common.h", "quant.h", "chunk.h", "i8ops.h")] + [
     os.path.join(ROOT, "include", "wushkv.h")]
 
 HIPCC_FLAGS = [

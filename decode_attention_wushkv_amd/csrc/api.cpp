@@ -335,12 +335,11 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
   return WUSHKV_OK;
 }
 
-// Decode steps with groups of 8 query heads run as chunk steps of one
-// position: eight query rows per KV head fill half an int8 matrix-core tile,
-// and that beats the integer-dot split kernel, whose vector work grows with
-// the group (at 2, 3 and 4 bits alike; groups of 4 stay on the split kernel).
+// Decode steps run on the split kernel at every group size (groups of 4 and
+// 8 on its int8 matrix-core path).
 static bool step_as_chunk(const wushkv_cache* c) {
-  return c->cfg.n_q_heads == 8 * c->cfg.n_kv_heads;
+  (void)c;
+  return false;
 }
 
 // Bytes of the split partials at the start of the decode workspace; the
@@ -460,10 +459,10 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
   // most what the launcher's grid policy allows, capped by the workspace
   // bound
   int cap = max_chunks(n_seq, c->cfg.n_kv_heads);
-  // G <= 2: four waves per workgroup on different sub-chunks; G >= 4: the
-  // waves of a workgroup share sub-chunks and split the query heads
+  // four waves per workgroup on different sub-chunks (G >= 4: of 64
+  // positions, for the int8 matrix cores)
   const int G = c->cfg.n_q_heads / c->cfg.n_kv_heads;
-  int need = G >= 4 ? max_sub : (max_sub + 3) / 4;
+  int need = G >= 4 ? (max_sub * (sl / 64) + 3) / 4 : (max_sub + 3) / 4;
   a.n_splits = need < cap ? need : cap;
   hipError_t e = launch_decode(a, c->cfg.io_dtype == WUSHKV_IO_BF16, (hipStream_t)stream,
                                c->ev_start, c->ev_stop, c->ev_cstart, c->ev_cstop);

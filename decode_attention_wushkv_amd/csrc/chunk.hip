@@ -34,12 +34,12 @@
 //            stores the chunk's entries that stay in bfloat16 (after every
 //            read of the ring has finished).
 #include "chunk.h"
+#include "i8ops.h"
 #include "quant.h"
 
 namespace wkv {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -96,47 +96,6 @@ __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// 16 two-bit codes (a 32-bit word) as 16 int8 MFMA operand bytes: byte e
-// holds element 4 (e % 4) + e / 4.
-__device__ __forceinline__ v4i unpack2(uint32_t d) {
-  v4i r;
-  r[0] = (int)(d & 0x03030303u);
-  r[1] = (int)((d >> 2) & 0x03030303u);
-  r[2] = (int)((d >> 4) & 0x03030303u);
-  r[3] = (int)((d >> 6) & 0x03030303u);
-  return r;
-}
-
-// Operand byte of element m (0 <= m < 16) in the order of unpack2.
-__device__ __forceinline__ int opnd_byte(int m) { return 4 * (m & 3) + (m >> 2); }
-
-// 16 four-bit codes (two words, element j in nibble j % 8 of word j / 8) as
-// operand bytes: byte 4 q + b holds element 8 (q / 2) + 2 b + q % 2.
-__device__ __forceinline__ v4i unpack4(uint32_t d0, uint32_t d1) {
-  v4i r;
-  r[0] = (int)(d0 & 0x0F0F0F0Fu);
-  r[1] = (int)((d0 >> 4) & 0x0F0F0F0Fu);
-  r[2] = (int)(d1 & 0x0F0F0F0Fu);
-  r[3] = (int)((d1 >> 4) & 0x0F0F0F0Fu);
-  return r;
-}
-
-// Operand byte of element m in the order of unpack4.
-__device__ __forceinline__ int opnd_byte4(int m) { return 4 * (2 * (m >> 3) + (m & 1)) + ((m & 7) >> 1); }
-
-// 16 three-bit codes: the low two bits as unpack2 orders them, the high bits
-// from a high-plane word in which element i sits at bit
-// 4 (i / 2) + sh + i % 2 (sh = 0 or 2, the plane's order of a 16-element group).
-__device__ __forceinline__ v4i unpack3(uint32_t lo, uint32_t hw, int sh) {
-  v4i r = unpack2(lo);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) r[q] |= (int)(((hw >> (4 * (q >> 1) + sh + (q & 1))) & 0x01010101u) << 2);
-  return r;
-}
-
-template <int BITS>
-__device__ __forceinline__ int opnd_byte_b(int m) { return BITS == 4 ? opnd_byte4(m) : opnd_byte(m); }
-
 // Two balanced base-256 digits of |x| <= 32639: x = 256 hi + lo.
 __device__ __forceinline__ void digits8(int x, int& lo, int& hi) {
   lo = ((x + 128) & 255) - 128;
@@ -163,9 +122,6 @@ __device__ __forceinline__ float cross_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ v4i mfma8(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
 
 // ---------------------------------------------------------------- prep
 

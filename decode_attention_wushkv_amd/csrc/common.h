@@ -160,6 +160,10 @@ struct DecodeSeqs {
   int32_t slot[MAXSEQ];
   int32_t len[MAXSEQ];
   int32_t squant[MAXSEQ];
+  // Balanced grid (DecodeArgs::balanced): the quantized workgroups of
+  // sequence i are grid blocks units + [wg0[i], wg0[i + 1]), KV head by KV
+  // head, (wg0[i + 1] - wg0[i]) / n_kv per head
+  int32_t wg0[MAXSEQ + 1];
 };
 
 struct DecodeArgs {
@@ -179,6 +183,11 @@ struct DecodeArgs {
   // out in turn (k, k + 4, ...).  With the head split (G >= 4) 1 and 2 both
   // give each workgroup one run.
   int contig;
+  // Groups of 4 and 8 (the matrix-core path): window workgroups first, then
+  // each sequence's KV heads get quantized workgroups in proportion to their
+  // sub-chunks (s.wg0); n_splits is the largest count per head, and also the
+  // window partial's index
+  int balanced;
   const void* q;
   const float* tq;
   float* out;

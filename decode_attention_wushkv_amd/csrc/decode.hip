@@ -32,6 +32,7 @@
 // ring entries that leave the recent window and stores the new entry.  The
 // quantized workgroups read positions below the old boundary only, so the
 // codes it writes (at or above that boundary) never race with them.
+#include "i8ops.h"
 #include "quant.h"
 
 namespace wkv {
@@ -161,10 +162,11 @@ struct SplitCfg {
   static constexpr int NG = TW / GS;           // value-row words per sub-chunk (8)
   static constexpr int WGW = SPLIT2 ? 2 * WDIG : WDIG;  // digit words per row word
   static constexpr int WGP = (WGW + 3) / 4 * 4;            // ... padded to 16 bytes
-  // G >= 4: head split (the four waves of a quantized workgroup walk the same
-  // sub-chunks, GW query heads each)
+  // G >= 4: the quantized waves run on the int8 matrix cores, each wave on
+  // its own MT-position sub-chunks for all G heads, in NTL tiles of four
   static constexpr bool HS = G >= 4;
-  static constexpr int GW = HS ? G / 4 : G;
+  static constexpr int MT = 64;
+  static constexpr int NTL = HS ? G / 4 : 1;
   // LDS (32-bit words).  Persistent part:
   static constexpr int O_OBUF = 0;                          // [G][D] partial o
   static constexpr int O_RED = O_OBUF + G * D;              // [64] reductions
@@ -174,7 +176,9 @@ struct SplitCfg {
   static constexpr int O_UNION = O_QD + G * 16 * DIGP;
   // Union: query setup | quantized waves | window.
   static constexpr int SETUP = G * D + 2 * G * D + QDIG * G * D / 4;   // qv, halves, digits (bytes/4)
-  static constexpr int WAVE = G * TW + G * NG * WGP;                    // per wave
+  // per wave: weight staging (16-bit codes; [tile][head][group][16] on the
+  // matrix-core path)
+  static constexpr int WAVE = HS ? NTL * 128 : G * TW + G * NG * WGP;
   static constexpr int QUANT = 4 * WAVE + 4 * G * (D + 2);
   // window workgroup, in the union: scores [G][WINDOW_MAX], the decode-step
   // new key and value (bfloat16, D words), per-wave PV partials [4][G][D]
@@ -203,10 +207,13 @@ template <int IO_BF16, int G>
 __device__ __forceinline__ void compensate_load(const DecodeArgs& a, int h, int si, QueryIn<G>& in) {
   const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
   const int64_t q0 = ((int64_t)si * a.g.n_q + h * G) * D;
+  // (every thread loads, past the end a repeat of the last element that the
+  // caller ignores: a load under a branch would be waited for at the branch
+  // join, before the loads that follow are issued)
 #pragma unroll
   for (int n = 0; n < (G * D + 255) / 256; ++n) {
     const int x = tid + 256 * n;
-    in.q[n] = x < G * D ? load_io<IO_BF16>(a.q, q0 + x) : 0.f;
+    in.q[n] = load_io<IO_BF16>(a.q, q0 + (x < G * D ? x : G * D - 1));
   }
   const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D + 64 * hf);
 #pragma unroll
@@ -238,12 +245,19 @@ __device__ __forceinline__ void compensate_query(const DecodeArgs& a, int h, int
     if (tid + 256 * n < G * D) qv[tid + 256 * n] = in.q[n];
   const float* t = in.t;
   __syncthreads();
+  // half-row sums in four interleaved chains (independent FMAs in flight)
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    float acc = 0.f;
+    float c4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 64; ++j) acc = fmaf(t[j], qv[gg * D + 64 * hf + j], acc);
-    hsum[(hf * G + gg) * D + i] = acc;
+    for (int j = 0; j < 64; j += 4) {
+      const float4 q4 = *(const float4*)(qv + gg * D + 64 * hf + j);
+      c4[0] = fmaf(t[j], q4.x, c4[0]);
+      c4[1] = fmaf(t[j + 1], q4.y, c4[1]);
+      c4[2] = fmaf(t[j + 2], q4.z, c4[2]);
+      c4[3] = fmaf(t[j + 3], q4.w, c4[3]);
+    }
+    hsum[(hf * G + gg) * D + i] = (c4[0] + c4[1]) + (c4[2] + c4[3]);
   }
   __syncthreads();
   float v[2 * G];
@@ -266,27 +280,64 @@ __device__ __forceinline__ void compensate_query(const DecodeArgs& a, int h, int
     if (hf == 0) {
       qf[gg * D + i] = q[gg];
       int r = qi;
+      if constexpr (C::HS) {
+        // three balanced base-256 digits (|qi| <= QMAX < 2^23, so the top one
+        // stays within [-128, 127]) for the int8 matrix cores
 #pragma unroll
-      for (int k = 0; k < QDIG - 1; ++k) {
-        const int d = ((r + 8) & 15) - 8;
-        dig[(k * G + gg) * D + i] = (int8_t)d;
-        r = (r - d) >> 4;
+        for (int k = 0; k < 2; ++k) {
+          const int d = ((r + 128) & 255) - 128;
+          dig[(k * G + gg) * D + i] = (int8_t)d;
+          r = (r - d) >> 8;
+        }
+        dig[(2 * G + gg) * D + i] = (int8_t)r;
+      } else {
+#pragma unroll
+        for (int k = 0; k < QDIG - 1; ++k) {
+          const int d = ((r + 8) & 15) - 8;
+          dig[(k * G + gg) * D + i] = (int8_t)d;
+          r = (r - d) >> 4;
+        }
+        dig[((QDIG - 1) * G + gg) * D + i] = (int8_t)r;
       }
-      dig[((QDIG - 1) * G + gg) * D + i] = (int8_t)r;
     }
-    // sums of qi over dimensions [0, 64) and [64, 128) (waves 0 and 1), exact
-    // in int32 (|qi| < 2^23), stored as floats for the 4-bit code offset
-    qsum_h[gg] = hf ? 0 : qi;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) qsum_h[gg] += __shfl_xor(qsum_h[gg], o);
     if (tid == 0) {
       qsc[gg * 4] = v[gg];
       qsc[gg * 4 + 1] = 1.f / sq;
     }
-    if (tid == 0) qsc[gg * 4 + 2] = (float)qsum_h[gg];
-    if (tid == 64) qsc[gg * 4 + 3] = (float)qsum_h[gg];
+    if constexpr (!C::HS) {
+      // sums of qi over dimensions [0, 64) and [64, 128) (waves 0 and 1),
+      // exact in int32 (|qi| < 2^23), stored as floats for the 4-bit code
+      // offset of the integer-dot path
+      qsum_h[gg] = hf ? 0 : qi;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) qsum_h[gg] += __shfl_xor(qsum_h[gg], o);
+      if (tid == 0) qsc[gg * 4 + 2] = (float)qsum_h[gg];
+      if (tid == 64) qsc[gg * 4 + 3] = (float)qsum_h[gg];
+    }
   }
   __syncthreads();
+  if constexpr (C::HS) {
+    // A operands of the int8 matrix cores, [tile][ks][lane] 16 bytes each:
+    // lane = (row = lane % 16, group = lane / 16), row 4 h + k holds digit k of
+    // head 4 tile + h (k = 3: zero); operand byte e of the lane holds dimension
+    // 32 group + 16 ks + m with e the operand byte of m in the order the key
+    // codes unpack to (the same dimensions the lane's key words hold).
+    for (int x = tid; x < C::NTL * 2 * 64 * 4; x += 256) {
+      const int qw = x & 3, ln = (x >> 2) & 63, ks = (x >> 8) & 1, t = x >> 9;
+      const int row = ln & 15, grp = ln >> 4, hh = 4 * t + (row >> 2), dg = row & 3;
+      uint32_t word = 0;
+      if (dg < 3)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          // element m with operand byte 4 qw + jb
+          const int m = BITS == 4 ? 8 * (qw >> 1) + 2 * jb + (qw & 1) : 4 * jb + qw;
+          word |= (uint32_t)(uint8_t)dig[(dg * G + hh) * D + 32 * grp + 16 * ks + m] << (8 * jb);
+        }
+      qdw[x] = word;
+    }
+    __syncthreads();
+    return;
+  }
   // digit words: group x / DIGP of 8 dimensions, digit k = x % DIGP; nibble n
   // holds that digit of one dimension of the group.
   //   2, 3 bits: group = half * 8 + w * 2 + parity, dims 64 half + 16 w + 2 n + parity
@@ -713,6 +764,392 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
   }
 }
 
+// ---------------------------------------------------------------- quantized, int8 matrix cores
+
+// Groups of 4 and 8 query heads.  A wave takes 64-position sub-chunks for
+// all G heads of its KV head and contracts them on v_mfma_i32_16x16x64_i8:
+//   scores  A = query digits, row 4 h + k holding digit k of head h's 24-bit
+//           fixed-point query (three balanced base-256 digits, the same
+//           integer query as the integer-dot path); B = key codes, column =
+//           position.  Lane (m16, group) of the result then holds the three
+//           digit sums of head `group` at position 16 cb + m16, joined in the
+//           lane, and the 16 lanes of a row group share a head.
+//   values  A = softmax-weight digits, row 4 h + k holding digit k of head h's
+//           15-bit weight codes; B = value codes, column = dimension.  Lane
+//           (m16, group) of the result holds both digit sums of head `group`
+//           at dimension 16 db + m16.
+// Per 64 positions and four heads that is 8 + 8 matrix-core instructions;
+// the vector work left is the code unpacking (shared by the heads), one
+// softmax per (head, position) in the lanes that hold it, and the weights'
+// transposition into the A layout through 512 bytes of LDS.
+
+// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
+__device__ __forceinline__ float group16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  x = fmaxf(x, dpp_f<0x128>(x));
+  return x;
+}
+
+// Max over the 16 lanes of a DPP row of a non-negative float: its bits as an
+// unsigned integer are ordered the same, and an unsigned max (identity 0)
+// folds each DPP move into the max (a float max needs two more operations per
+// step to canonicalize its operand).
+__device__ __forceinline__ float group16_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  return __uint_as_float(v);
+}
+
+__device__ __forceinline__ float group16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x128>(x);
+  return x;
+}
+
+// Largest softmax-weight code: two balanced base-256 digits.
+constexpr int W8MAX = 32639;
+
+// Registers of one 64-position sub-chunk, lane = (m16 = lane % 16, group =
+// lane / 16):
+//   kc[cb]   key codes of position 16 cb + m16, dimensions 32 group .. + 31:
+//            2 bits words 2 group, 2 group + 1 of the position's code row;
+//            3 bits those low-plane words, and kh[cb] = high-plane word group;
+//            4 bits words 4 group .. 4 group + 3
+//   ksz, vsz scale/zero words of those four positions
+//   vc[db]   value codes of dimension 16 db + m16, positions 16 group .. + 15
+//            (3 bits: vh[db] = the high-plane word holding their high bits)
+template <int BITS>
+struct MBuf {
+  static constexpr int KW = BITS == 4 ? 4 : 2;
+  static constexpr int VW = BITS == 4 ? 2 : 1;
+  uint32_t kc[4][KW];
+  uint32_t kh[BITS == 3 ? 4 : 1];
+  uint32_t ksz[4], vsz[4];
+  uint32_t vc[8][VW];
+  uint32_t vh[BITS == 3 ? 8 : 1];
+};
+
+// Issues the loads of the sub-chunk at position pbase (a multiple of 64, so
+// its rows are consecutive and its value codes whole 16-byte row words);
+// pbase < 0 loads from `spare` instead, as load_sub does.  One wave reads
+// each sub-chunk, so the loads carry the non-temporal hint.
+template <int BITS>
+__device__ __forceinline__ void mload(MBuf<BITS>& b, const DecodeArgs& a, const QMap& qm, int pbase,
+                                      const uint8_t* spare) {
+  constexpr int CB = 16 * BITS;
+  const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
+  const bool past = pbase < 0;
+  const int64_t row = qrow_read(qm, past ? 0 : pbase);
+  const auto rk = wave_rsrc(past ? spare : a.pl.kcode + row * CB, 64 * CB);
+  const auto rks = wave_rsrc(past ? (const void*)spare : (const void*)(a.pl.ksz + row), 64 * 4);
+  const auto rvs = wave_rsrc(past ? (const void*)spare : (const void*)(a.pl.vsz + row), 64 * 4);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int ko = (16 * cb + m16) * CB;
+    if constexpr (BITS == 4) {
+      const uint4 v = buf_b128<CPOL_NT>(rk, ko + 16 * grp, 0);
+      b.kc[cb][0] = v.x;
+      b.kc[cb][1] = v.y;
+      b.kc[cb][2] = v.z;
+      b.kc[cb][3] = v.w;
+    } else {
+      const uint2 v = buf_b64<CPOL_NT>(rk, ko + 8 * grp, 0);
+      b.kc[cb][0] = v.x;
+      b.kc[cb][1] = v.y;
+      if constexpr (BITS == 3) b.kh[cb] = __builtin_amdgcn_raw_buffer_load_b32(rk, ko + 32 + 4 * grp, 0, CPOL_NT);
+    }
+    b.ksz[cb] = __builtin_amdgcn_raw_buffer_load_b32(rks, 4 * (16 * cb + m16), 0, CPOL_NT);
+    b.vsz[cb] = __builtin_amdgcn_raw_buffer_load_b32(rvs, 4 * (16 * cb + m16), 0, CPOL_NT);
+  }
+  if constexpr (BITS == 2) {
+    // one 64-position row per dimension
+    const auto rv = wave_rsrc(past ? spare : a.pl.vcode + (row >> 6) * D * 16, D * 16);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      b.vc[db][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (16 * db + m16) * 16 + 4 * grp, 0, CPOL_NT);
+  } else if constexpr (BITS == 4) {
+    // two 32-position rows per dimension: this group's 16 positions are words
+    // 2 (group % 2), + 1 of row group / 2
+    const auto rv = wave_rsrc(past ? spare : a.pl.vcode + (row >> 5) * D * 16, 2 * D * 16);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint2 v = buf_b64<CPOL_NT>(rv, (grp >> 1) * D * 16 + (16 * db + m16) * 16 + 8 * (grp & 1), 0);
+      b.vc[db][0] = v.x;
+      b.vc[db][1] = v.y;
+    }
+  } else {
+    // 128-position block: low-plane row sel (the sub-chunk's half) and the
+    // high-plane row, whose bytes [8 sel, 8 sel + 8) belong to this half
+    const int sel = (int)((row >> 6) & 1);
+    const auto rv = wave_rsrc(past ? spare : a.pl.vcode + (row >> 7) * 3 * D * 16, 3 * D * 16);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      b.vc[db][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (16 * db + m16) * 16 + 4 * grp, sel * D * 16, CPOL_NT);
+      b.vh[db] = __builtin_amdgcn_raw_buffer_load_b32(rv, 2 * D * 16 + (16 * db + m16) * 16 + 4 * (grp >> 1),
+                                                      8 * sel, CPOL_NT);
+    }
+  }
+}
+
+// One sub-chunk for NTL tiles of four heads: scores, weights and value sums,
+// folded into the running state (M wave-uniform per row group, Lp and Zp
+// per-lane partials, O per lane's dimensions 16 db + m16).  wl is the wave's
+// weight staging ([tile][head][group][16] 16-bit codes), wsel the byte
+// selector that takes this lane's digit (row % 4) of four codes.
+template <int BITS, int NTL>
+__device__ __forceinline__ void mprocess(const MBuf<BITS>& b, int pbase, int lo, int hi,
+                                         const v4i (&Aq)[NTL][2], const float (&sig)[NTL],
+                                         const float (&inv)[NTL], uint16_t* wl, uint32_t wsel,
+                                         float (&M)[NTL], float (&Lp)[NTL], float (&Zp)[NTL],
+                                         float (&O)[NTL][8]) {
+  const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
+  // ---- scores (log2 domain), -inf outside [lo, hi).  Every matrix-core
+  // product is issued before the first result is read, and the mask is
+  // arithmetic (a branch per position would make the scheduler wait out
+  // each product's latency in turn).
+  v4i acc[NTL][4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    v4i k0, k1;  // dimensions 32 group + [0, 16) and + [16, 32)
+    if constexpr (BITS == 2) {
+      k0 = unpack2(b.kc[cb][0]);
+      k1 = unpack2(b.kc[cb][1]);
+    } else if constexpr (BITS == 3) {
+      k0 = unpack3(b.kc[cb][0], b.kh[cb], 0);
+      k1 = unpack3(b.kc[cb][1], b.kh[cb], 2);
+    } else {
+      k0 = unpack4(b.kc[cb][0], b.kc[cb][1]);
+      k1 = unpack4(b.kc[cb][2], b.kc[cb][3]);
+    }
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) acc[t][cb] = mfma8(Aq[t][1], k1, mfma8(Aq[t][0], k0, v4i{0, 0, 0, 0}));
+  }
+  float ksv[4], kzv[4], vsv[4], vzv[4], lim[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int p = pbase + 16 * cb + m16;
+    const bool ok = p >= lo && p < hi;
+    lim[cb] = ok ? INFINITY : -INFINITY;
+    ksv[cb] = f16_to_f32(b.ksz[cb] & 0xFFFFu);
+    kzv[cb] = f16_to_f32(b.ksz[cb] >> 16);
+    const uint32_t vw = ok ? b.vsz[cb] : 0u;  // masked positions: scale and zero 0
+    vsv[cb] = f16_to_f32(vw & 0xFFFFu);
+    vzv[cb] = f16_to_f32(vw >> 16);
+  }
+  float s[NTL][4];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      // 256 d2 + d1 fits in 32 bits (below 2^24, exact as a float, at 2
+      // bits; one more rounding of relative size 2^-24 at 3 and 4 bits)
+      const v4i& d = acc[t][cb];
+      const float dot = fmaf((float)(d[2] * 256 + d[1]), 256.f, (float)d[0]);
+      // fminf with -inf masks (also a NaN score from a masked position's
+      // stale scale/zero), with +inf keeps the score
+      s[t][cb] = fminf(fmaf(ksv[cb], dot * inv[t], kzv[cb] * sig[t]), lim[cb]);
+    }
+  // ---- per head: the new running maximum M' = max(M, sub-chunk max) is the
+  // reference, p = exp2(s - M'), w = p s_v.  Once the running maxima settle
+  // no score exceeds them, M' = M, and the reduction over the head's lanes
+  // is skipped.
+  float fo[NTL], wm[NTL], ls[NTL], zs[NTL], w[NTL][4];
+  {
+    float lm[NTL];
+    bool above = false;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      lm[t] = fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3]));
+      above = above || lm[t] > M[t];
+    }
+    if (__any(above)) {
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const float Mn = fmaxf(M[t], group16_max(lm[t]));
+        fo[t] = exp2_nonpos(M[t] - Mn);
+        M[t] = Mn;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) fo[t] = 1.f;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    wm[t] = ls[t] = zs[t] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const float p = exp2_nonpos(s[t][cb] - M[t]);
+      w[t][cb] = p * vsv[cb];
+      ls[t] += p;
+      zs[t] = fmaf(p, vzv[cb], zs[t]);
+      wm[t] = fmaxf(wm[t], w[t][cb]);
+    }
+    wm[t] = group16_max_nonneg(wm[t]);
+  }
+  // ---- weight codes into the A layout: this lane's code of (head group,
+  // position 16 cb + m16) goes to slot (operand byte of m16) of block
+  // [tile][group][cb]; lane (row, group) then reads block [tile][row / 4]
+  // [group] and keeps digit row % 4 (low byte: low digit)
+  const int eb = opnd_byte_b<BITS>(m16);
+  wave_sync();  // the previous sub-chunk's reads of wl are done
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    const float wsc = wm[t] > 0.f ? (float)W8MAX * __builtin_amdgcn_rcpf(wm[t]) : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      int wq = (int)rintf(w[t][cb] * wsc);
+      wq = wq > W8MAX ? W8MAX : wq;
+      // balanced digits lo = ((wq + 128) & 255) - 128, hi = (wq + 128) >> 8
+      // as two's-complement bytes: the low byte is wq & 255
+      wl[((t * 4 + grp) * 4 + cb) * 16 + eb] = (uint16_t)(((wq + 128) & 0xFF00) | (wq & 0xFF));
+    }
+  }
+  wave_sync();
+  v4i W[NTL];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    const uint4* src = (const uint4*)(wl + ((t * 4 + (m16 >> 2)) * 4 + grp) * 16);
+    const uint4 x0 = src[0], x1 = src[1];
+    W[t][0] = (int)__builtin_amdgcn_perm(x0.y, x0.x, wsel);
+    W[t][1] = (int)__builtin_amdgcn_perm(x0.w, x0.z, wsel);
+    W[t][2] = (int)__builtin_amdgcn_perm(x1.y, x1.x, wsel);
+    W[t][3] = (int)__builtin_amdgcn_perm(x1.w, x1.z, wsel);
+  }
+  // ---- online softmax fold and o += w c
+  float back[NTL];
+  bool settled = true;
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    back[t] = wm[t] * (1.f / (float)W8MAX);
+    Lp[t] = fmaf(Lp[t], fo[t], ls[t]);
+    Zp[t] = fmaf(Zp[t], fo[t], zs[t]);
+    settled = settled && fo[t] == 1.f;
+  }
+  // once the running maxima settle (the common case) no rescale is needed
+  if (!__all(settled)) {
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) O[t][db] *= fo[t];
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    v4i vb;
+    if constexpr (BITS == 2) vb = unpack2(b.vc[db][0]);
+    else if constexpr (BITS == 3) vb = unpack3(b.vc[db][0], b.vh[db], 2 * (grp & 1));
+    else vb = unpack4(b.vc[db][0], b.vc[db][1]);
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const v4i pv = mfma8(W[t], vb, v4i{0, 0, 0, 0});
+      O[t][db] = fmaf((float)(pv[1] * 256 + pv[0]), back[t], O[t][db]);
+    }
+  }
+}
+
+// One wave, all G = 4 NTL heads: sub-chunks c0, c0 + 4, ... (< c_end) of the
+// quantized region [lo, hi), two in flight (A and B hold c0 and c0 + 4 on
+// entry, issued by the caller before the query preparation); leaves the
+// partial (o[D], m, l) of head gg at out + gg (D + 2).
+// A lane's query operands (NTL tiles x 2 halves of the dimensions) and its
+// head's sigma and 1/S_q, from a query block's scales qsc and operand words
+// qop (in LDS, or in global memory as the prep kernel wrote them).
+template <int NTL>
+struct MQuery {
+  v4i A[NTL][2];
+  float sig[NTL], inv[NTL];
+};
+
+template <int NTL>
+__device__ __forceinline__ void mquery_load(MQuery<NTL>& q, const float* qsc, const uint32_t* qop) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) q.A[t][ks] = ((const v4i*)qop)[(2 * t + ks) * 64 + lane];
+    q.sig[t] = qsc[(4 * t + grp) * 4];
+    q.inv[t] = qsc[(4 * t + grp) * 4 + 1];
+  }
+}
+
+template <int BITS, int NTL>
+__device__ void mquant_wave(const DecodeArgs& a, const QMap& qm, int c0, int c_end, int lo, int hi,
+                            const MQuery<NTL>& qy, uint16_t* wl, float* out, MBuf<BITS>& A,
+                            MBuf<BITS>& B, const uint8_t* spare) {
+  constexpr int MT = 64;
+  const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
+  const int wd = m16 & 3;
+  const uint32_t wsel = wd == 0 ? 0x06040200u : (wd == 1 ? 0x07050301u : 0x0C0C0C0Cu);
+  float M[NTL], Lp[NTL], Zp[NTL], O[NTL][8];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    M[t] = -INFINITY;
+    Lp[t] = Zp[t] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) O[t][db] = 0.f;
+  }
+  // as in quant_wave: a buffer is refilled with the sub-chunk two steps
+  // ahead as soon as it has been processed, unconditionally
+  int c = c0;
+  while (c < c_end) {
+    mprocess<BITS, NTL>(A, c * MT, lo, hi, qy.A, qy.sig, qy.inv, wl, wsel, M, Lp, Zp, O);
+    __builtin_amdgcn_sched_barrier(0);
+    mload<BITS>(A, a, qm, c + 8 < c_end ? (c + 8) * MT : -1, spare);
+    c += 4;
+    if (c >= c_end) break;
+    mprocess<BITS, NTL>(B, c * MT, lo, hi, qy.A, qy.sig, qy.inv, wl, wsel, M, Lp, Zp, O);
+    __builtin_amdgcn_sched_barrier(0);
+    mload<BITS>(B, a, qm, c + 8 < c_end ? (c + 8) * MT : -1, spare);
+    c += 4;
+  }
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    const float Lw = group16_sum(Lp[t]);
+    const float Zw = group16_sum(Zp[t]);  // zero-point term, the same for every dimension
+    float* po = out + (4 * t + grp) * (D + 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) po[16 * db + m16] = O[t][db] + Zw;
+    if (m16 == 0) {
+      po[D] = M[t];
+      po[D + 1] = Lw;
+    }
+  }
+}
+
+// Log-sum-exp merge of the four waves' partials part[wave][G][D + 2] (a wave
+// without sub-chunks has l = 0): o into obuf, m and l per head.
+template <int G>
+__device__ __forceinline__ void merge_waves(const float* part, float* obuf, float (&m)[G], float (&l)[G]) {
+  const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float* px = part + (x * G + gg) * (D + 2);
+      if (px[D + 1] > 0.f) Mx = fmaxf(Mx, px[D]);
+    }
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float* px = part + (x * G + gg) * (D + 2);
+      const float f = px[D + 1] > 0.f ? exp2f(px[D] - Mx) : 0.f;
+      lsum = fmaf(px[D + 1], f, lsum);
+      o = fmaf(px[i], f, o);
+    }
+    if (hf == 0) obuf[gg * D + i] = o;
+    m[gg] = Mx;
+    l[gg] = lsum;
+  }
+}
+
 // ---------------------------------------------------------------- decode step
 
 template <int IO_BF16>
@@ -737,12 +1174,10 @@ __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
   uint16_t* vnew = knew + D;
   const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
   const int64_t row = ((int64_t)si * a.g.n_kv + h) * D;
-  float x;
-  uint16_t vb = 0;
-  if (tid < D)
-    x = load_io<IO_BF16>(a.k_new, row + tid);
-  else
-    vb = io_to_bf16<IO_BF16>(a.v_new, row + tid - D);
+  // every thread loads both (no load under a branch, whose join would wait
+  // for it and, in order, for every load issued before)
+  const float x = load_io<IO_BF16>(a.k_new, row + i);
+  const uint16_t vb = io_to_bf16<IO_BF16>(a.v_new, row + i);
   float t[64];
   const float4* tp = (const float4*)(a.tk + ((int64_t)h * D + i) * D + 64 * hf);
 #pragma unroll
@@ -753,10 +1188,10 @@ __device__ void new_entry(const DecodeArgs& a, int h, int si, uint32_t* sm) {
     t[4 * c + 2] = t4.z;
     t[4 * c + 3] = t4.w;
   }
-  if (tid < D)
-    kin[tid] = x;
+  if (hf == 0)
+    kin[i] = x;
   else
-    vnew[tid - D] = vb;
+    vnew[i] = vb;
   __syncthreads();
   double s0 = 0.0, s1 = 0.0;
 #pragma unroll
@@ -1046,7 +1481,9 @@ __global__ __launch_bounds__(256) void prep_kernel(DecodeArgs a) {
   const int h = blockIdx.x, si = blockIdx.y;
   QueryIn<G> qin;
   compensate_load<IO_BF16, G>(a, h, si, qin);
-  if (a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
+  // (G >= 4: the split kernel's window workgroup transforms the new entry,
+  // which keeps this launch's chain short)
+  if (!C::HS && a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
   compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
   uint4* dst = (uint4*)(a.prep + (int64_t)(si * a.g.n_kv + h) * prep_words(G));
   constexpr int NQ4 = (prep_words(G) - D) / 4;
@@ -1065,12 +1502,18 @@ __device__ __forceinline__ int run_start(int64_t nsub, int j, int n) {
   return (int)((nsub * (LIGHT + 16 * (int64_t)(j - 1))) / total);
 }
 
+// Waves per SIMD the register allocation must allow: three at G = 4 with the
+// query block from the prep kernel (the matrix-core path then needs 127-167
+// registers), two otherwise (G <= 2 keeps two sub-chunks of codes and the
+// query digits in registers; G = 8, and the in-workgroup query preparation
+// with two sub-chunks' loads in flight, need more than 168).
+template <int G, bool PREP>
+constexpr int split_waves() { return G == 4 && PREP ? 3 : 2; }
+
 // PREP: the query block comes from the prep kernel (else every workgroup
-// prepares the query itself).  Three waves per SIMD at G = 4 for 3- and 4-bit
-// codes; at 2 bits the head split needs more than 168 registers per lane
-// (it spilled, 40% slower), so two.
+// prepares the query itself).
 template <int IO_BF16, int BITS, int G, bool PREP>
-__global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, (split_waves<G, PREP>())) void split_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
   uint32_t* sm = (uint32_t*)smem4;
@@ -1083,8 +1526,28 @@ __global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel
   // oldest waves on their SIMDs and win issue arbitration, which keeps their
   // serial chain short), then the quantized workgroups unit by unit.
   int j, u;
+  int nsu = a.n_splits;  // this unit's quantized workgroups
   const int units = a.n_seq * a.g.n_kv;
-  if (a.contig == 2) {
+  if (a.balanced) {
+    if ((int)blockIdx.x < units) {
+      u = blockIdx.x;
+      j = a.n_splits;
+    } else {
+      // the last sequence whose range starts at or before r (sequences
+      // without quantized workgroups have empty ranges)
+      const int r = blockIdx.x - units;
+      int s0 = 0, s1 = a.n_seq;
+      while (s1 - s0 > 1) {
+        const int mid = (s0 + s1) >> 1;
+        if (a.s.wg0[mid] <= r) s0 = mid;
+        else s1 = mid;
+      }
+      nsu = (a.s.wg0[s0 + 1] - a.s.wg0[s0]) / a.g.n_kv;
+      const int rr = r - a.s.wg0[s0];
+      u = s0 * a.g.n_kv + rr / nsu;
+      j = rr % nsu;
+    }
+  } else if (a.contig == 2) {
     // One quantized workgroup per CU: the quantized workgroups first, so that
     // the dispatcher spreads them one per CU, then the window workgroups.
     // Block b < units is unit b's workgroup 0, which takes a smaller share of
@@ -1137,13 +1600,20 @@ __global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel
   const int c_end = hi > lo ? (hi + C::TW - 1) / C::TW : c_first;
   const int nw = 4 * a.n_splits;
   const int64_t nsub = c_end - c_first;
+  // matrix-core path (G >= 4): workgroup j takes the contiguous run [mr0,
+  // mr1) of the unit's 64-position sub-chunks, which its waves share out in
+  // turn (k, k + 4, ...)
+  const int mc_first = lo / C::MT, mc_end = hi > lo ? (hi + C::MT - 1) / C::MT : mc_first;
+  const int64_t mnsub = mc_end - mc_first;
+  const int nsd = nsu > 0 ? nsu : 1;
+  const int mr0 = j < nsu ? mc_first + (int)((mnsub * j) / nsd) : mc_first;
+  const int mr1 = j < nsu ? mc_first + (int)((mnsub * (j + 1)) / nsd) : mc_first;
   bool empty;
   if (j == a.n_splits) {
     const int ns = Lq < g.S ? Lq : g.S;
     empty = ns + (Lq > sq ? Lq - sq : 0) == 0;
   } else if (C::HS) {
-    empty = a.contig ? (nsub * (j + 1)) / a.n_splits == (nsub * j) / a.n_splits
-                     : c_first + j >= c_end;
+    empty = mr1 == mr0;
   } else if (a.contig == 1) {
     empty = (nsub * (4 * j + 4)) / nw == (nsub * 4 * j) / nw;
   } else if (a.contig == 2) {
@@ -1153,7 +1623,6 @@ __global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel
   }
   float m[G], l[G];
   uint16_t first_leaving = 0;
-  bool direct = false;  // head-split workgroups write their partials themselves
   if (!empty) {
     if (j == a.n_splits) {
       // a decode step's first ring entry to quantize after the attention
@@ -1170,6 +1639,8 @@ __global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel
         PrepIn<G> pin;
         prep_load<G>(a, u, pin);
         prep_store<BITS, G>(sm, pin);
+        // G >= 4: the prep kernel leaves the new entry to this workgroup
+        if (C::HS && a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
       } else {
         // the query inputs and the new entry's inputs in flight together
         QueryIn<G> qin;
@@ -1180,40 +1651,32 @@ __global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel
       window_chunk<BITS, G>(a, unit, Lq, sq, sm, m, l);
       first_leaving = first_lv;
     } else if constexpr (C::HS) {
-      // head split: the four waves walk the same sub-chunks, wave w taking
-      // query heads [w GW, w GW + GW)
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler
-      int c0, cstride, cend;
-      if (a.contig) {
-        c0 = c_first + (int)((nsub * j) / a.n_splits);
-        cend = c_first + (int)((nsub * (j + 1)) / a.n_splits);
-        cstride = 1;
-      } else {
-        c0 = c_first + j;
-        cend = c_end;
-        cstride = a.n_splits;
-      }
-      // the query inputs, then the first sub-chunk's codes, in flight together
-      SubBuf<BITS, C::GW> A, B;
+      const int c0 = mr0 + w;
+      // the query inputs, then the first two sub-chunks' codes, in flight together
+      MBuf<BITS> A, B;
+      MQuery<C::NTL> qy;
       if constexpr (PREP) {
-        PrepIn<G> pin;
-        prep_load<G>(a, u, pin);
-        load_first<BITS, C::GW, 0>(A, a, qm, c0, cend, spare);
-        load_first<BITS, C::GW, 0>(B, a, qm, c0 + cstride, cend, spare);
-        prep_store<BITS, G>(sm, pin);
+        // the lane's operands straight from the unit's query block (its
+        // scales and operand words; q' and the new entry are the window's)
+        const uint32_t* blk = a.prep + (int64_t)u * prep_words(G);
+        mquery_load<C::NTL>(qy, (const float*)(blk + (C::O_QSC - C::O_QF)), blk + (C::O_QD - C::O_QF));
+        mload<BITS>(A, a, qm, c0 < mr1 ? c0 * C::MT : -1, spare);
+        mload<BITS>(B, a, qm, c0 + 4 < mr1 ? (c0 + 4) * C::MT : -1, spare);
       } else {
         QueryIn<G> qin;
         compensate_load<IO_BF16, G>(a, h, si, qin);
-        load_first<BITS, C::GW, 0>(A, a, qm, c0, cend, spare);
-        load_first<BITS, C::GW, 0>(B, a, qm, c0 + cstride, cend, spare);
+        mload<BITS>(A, a, qm, c0 < mr1 ? c0 * C::MT : -1, spare);
+        mload<BITS>(B, a, qm, c0 + 4 < mr1 ? (c0 + 4) * C::MT : -1, spare);
         compensate_query<IO_BF16, BITS, G>(a, h, si, sm, qin);
+        mquery_load<C::NTL>(qy, (const float*)(sm + C::O_QSC), sm + C::O_QD);
       }
-      float* dst = a.wsp + ((int64_t)(qbase + w * C::GW) * nsp + j) * PS;
-      quant_wave<BITS, C::GW, 0>(a, qm, c0, cstride, cend, lo, hi,
-                              (const float*)(sm + C::O_QSC) + w * C::GW * 4,
-                              sm + C::O_QD + w * C::GW * 16 * DIGP, sm + C::O_UNION + w * C::WAVE,
-                              dst, (int64_t)nsp * PS, A, B, spare);
-      direct = true;
+      uint32_t* wbase = sm + C::O_UNION;
+      float* part = (float*)(wbase + 4 * C::WAVE);  // [4 waves][G][D + 2]
+      mquant_wave<BITS, C::NTL>(a, qm, c0, mr1, lo, hi, qy, (uint16_t*)(wbase + w * C::WAVE),
+                                part + w * G * (D + 2), A, B, spare);
+      __syncthreads();
+      merge_waves<G>(part, obuf, m, l);
     } else {
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wi = 4 * j + w;
       int c0, cstride, cend;
@@ -1252,32 +1715,11 @@ __global__ __launch_bounds__(256, G == 4 && BITS != 2 ? 3 : 2) void split_kernel
                                            wbase + w * C::WAVE, part + w * G * (D + 2), D + 2, A,
                                            B, spare);
       __syncthreads();
-      // merge the four wave partials (a wave without sub-chunks has l = 0)
-      const int i = tid & (D - 1), hf = tid >> 7;
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float* px = part + (x * G + gg) * (D + 2);
-          if (px[D + 1] > 0.f) M = fmaxf(M, px[D]);
-        }
-        float lsum = 0.f, o = 0.f;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float* px = part + (x * G + gg) * (D + 2);
-          const float f = px[D + 1] > 0.f ? exp2f(px[D] - M) : 0.f;
-          lsum = fmaf(px[D + 1], f, lsum);
-          o = fmaf(px[i], f, o);
-        }
-        if (hf == 0) obuf[gg * D + i] = o;
-        m[gg] = M;
-        l[gg] = lsum;
-      }
+      merge_waves<G>(part, obuf, m, l);
     }
   }
   __syncthreads();
-  if (!direct && tid < D) {
+  if (tid < D) {
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       float* dst = a.wsp + ((int64_t)(qbase + gg) * nsp + j) * PS;
@@ -1300,12 +1742,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   __shared__ float red[64];
   const int jq = blockIdx.x, si = blockIdx.y, tid = threadIdx.x;
   const int nsp = a.n_splits + 1;
+  // partials written: the sequence's quantized workgroups 0 .. nq - 1 and the
+  // window's, n_splits (a balanced grid gives a sequence nq <= n_splits)
+  const int nq = a.balanced ? (a.s.wg0[si + 1] - a.s.wg0[si]) / a.g.n_kv : a.n_splits;
+  auto written = [&](int y) { return y < nq || y == a.n_splits; };
   const float* src = a.wsp + ((int64_t)si * a.g.n_q + jq) * nsp * PS;
   const int d4 = (tid & 31) * 4, rsd = tid >> 5;
   // every load in flight at once: (m, l) of partial tid, and this thread's
   // four dimensions of partials rsd, rsd + 8, ... with their (m, l)
   float mt = -INFINITY, lt = 0.f;
-  if (tid < nsp) {
+  if (written(tid)) {
     mt = src[tid * PS + D];
     lt = src[tid * PS + D + 1];
   }
@@ -1317,7 +1763,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     my[k] = 0.f;
     ly[k] = 0.f;
-    if (y < nsp) {
+    if (written(y)) {
       v[k] = *(const float4*)(src + (int64_t)y * PS + d4);
       my[k] = src[y * PS + D];
       ly[k] = src[y * PS + D + 1];
@@ -1351,19 +1797,28 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 // bound in a.n_splits.
 template <int IO_BF16, int BITS, int G>
 hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
-  static int slots = 0, cus = 0;
+  // resident workgroups of the two kernel variants (in-workgroup query
+  // preparation, query block from the prep kernel)
+  static int slots = 0, slots_p = 0, cus = 0;
   const size_t lds = (size_t)SplitCfg<BITS, G>::TOTAL * 4;
   if (slots == 0) {
-    int dev = 0, per = 0;
+    int dev = 0, per = 0, per_p = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<IO_BF16, BITS, G, false>, 256,
                                                        lds);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_p, split_kernel<IO_BF16, BITS, G, true>, 256,
+                                                       lds);
     if (e != hipSuccess) return e;
+    slots_p = cus * (per_p > 0 ? per_p : 1);
     slots = cus * (per > 0 ? per : 1);
   }
-  // Three layouts, chosen per launch:
+  // Layouts, chosen per launch:
+  //  - G >= 4 (matrix-core path): one wave of workgroups, the quantized ones
+  //    shared out among the sequences in proportion to their 64-position
+  //    sub-chunks (balanced grid, below);
   //  - G <= 2 with at most half as many units as CUs: one quantized
   //    workgroup per CU (below), query preparation in every workgroup;
   //  - otherwise, for long single launches with few units: the grid fills the
@@ -1374,7 +1829,57 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
   //    window workgroup's chain stays short.
   const int units = a.n_seq * a.g.n_kv;
   bool prep = false;
-  if (!SplitCfg<BITS, G>::HS && 2 * units <= cus) {
+  int grid = 0;
+  a.balanced = 0;
+  if (SplitCfg<BITS, G>::HS) {
+    // A workgroup takes four sub-chunks at a time, so an oversubscribed grid
+    // would leave it runs too short for its fixed costs; one wave of
+    // workgroups with shares in proportion to the sequences' lengths keeps
+    // the ragged batch balanced instead (36-layer ragged batch: 2.80 ms per
+    // step with ~6x oversubscription, 2.40 with 1x).  The prep kernel
+    // prepares the query blocks of launches under 240 MB; larger ones
+    // prepare them in every workgroup, behind its first code loads (64-layer
+    // 64K batch, G = 8: 6.48 against 6.76 ms).  At least four sub-chunks (one
+    // per wave) per workgroup, at most a.n_splits per KV head.
+    prep = a.max_sub >= 16;
+    const int sl = prep ? slots_p : slots;
+    constexpr int MT = SplitCfg<BITS, G>::MT;
+    int64_t total = 0;
+    int msub[MAXSEQ];
+    for (int i = 0; i < a.n_seq; ++i) {
+      const int lo = a.g.S, hi = a.s.squant[i];
+      const int first = lo / MT, end = hi > lo ? (hi + MT - 1) / MT : first;
+      msub[i] = end - first;
+      total += (int64_t)msub[i] * a.g.n_kv;
+    }
+    // sub-chunks per workgroup: the smallest share whose rounded-up counts
+    // fit the slots left by the window workgroups (a second wave of
+    // workgroups would start only when the windows end)
+    const int qwg = sl - units > units ? sl - units : units;
+    int64_t per = (total + qwg - 1) / qwg;
+    if (per < 4) per = 4;
+    for (;;) {
+      int64_t n = 0;
+      for (int i = 0; i < a.n_seq; ++i) {
+        const int64_t ni = (msub[i] + per - 1) / per;
+        n += (ni < a.n_splits ? ni : a.n_splits) * a.g.n_kv;
+      }
+      if (n <= qwg) break;
+      per += 1 + per / 16;
+    }
+    int acc = 0, nmax = 0;
+    for (int i = 0; i < a.n_seq; ++i) {
+      int n = (int)((msub[i] + per - 1) / per);
+      if (n > a.n_splits) n = a.n_splits;
+      a.s.wg0[i] = acc;
+      acc += n * a.g.n_kv;
+      if (n > nmax) nmax = n;
+    }
+    a.s.wg0[a.n_seq] = acc;
+    a.n_splits = nmax;
+    a.balanced = 1;
+    grid = units + acc;
+  } else if (2 * units <= cus) {
     // Few units (long contexts, G <= 2): one quantized workgroup per CU, each
     // on one contiguous run of its unit's sub-chunks, with the query
     // preparation in every workgroup.  Four waves per CU keep fewer bytes in
@@ -1390,19 +1895,18 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     const double bytes = (double)a.total_sub * SplitCfg<BITS, G>::TW * (32.0 * BITS + 8.0);
     prep = a.max_sub >= 16 && (bytes < 240e6 || 9 * units > slots);
     if (prep) {
-      const int target = (6 * slots) / units - 1;
+      const int target = (6 * slots_p) / units - 1;
       if (target > fill) fill = target;
     }
     if (a.n_splits > fill) a.n_splits = fill;
   }
   a.xcd_map = a.xcd_map && units % 8 == 0;
+  if (!a.balanced) grid = (a.n_splits + 1) * units;
   if (prep) {
     hipLaunchKernelGGL((prep_kernel<IO_BF16, BITS, G>), dim3(a.g.n_kv, a.n_seq), dim3(256), lds, st, a);
-    hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G, true>), dim3((a.n_splits + 1) * units), dim3(256),
-                       lds, st, a);
+    hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G, true>), dim3(grid), dim3(256), lds, st, a);
   } else {
-    hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G, false>), dim3((a.n_splits + 1) * units),
-                       dim3(256), lds, st, a);
+    hipLaunchKernelGGL((split_kernel<IO_BF16, BITS, G, false>), dim3(grid), dim3(256), lds, st, a);
   }
   return hipGetLastError();
 }
