@@ -935,8 +935,8 @@ def main():
                    "hbm_frac": round(mm["value"] / HBM_PEAK_GBS, 4),
                    "tokens_per_s": round(Bw / (mm["ms_per_step"] * 1e-3), 1),
                    "layers": wl.n_layers, "batch": Bw, "cache_mb_read_per_step": round(cache_mb, 2),
-                   "attention": "int8 matrix cores (one-position chunk steps)"
-                   if wl.group == 8 else "split kernel (v_dot8)"}
+                   "attention": "split kernel, int8 matrix cores (groups of 4 and 8 query heads)"
+                   if wl.group >= 4 else "split kernel (v_dot8)"}
             if cache_mb * copies < 256:
                 row["residency"] = ("last-level-cache resident: the whole cache fits the 256 MB "
                                     "Infinity Cache and is re-read from it every step; not an "

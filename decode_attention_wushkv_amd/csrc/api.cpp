@@ -335,13 +335,6 @@ extern "C" wushkv_status wushkv_append(wushkv_cache* c, int32_t layer, int32_t n
   return WUSHKV_OK;
 }
 
-// Decode steps run on the split kernel at every group size (groups of 4 and
-// 8 on its int8 matrix-core path).
-static bool step_as_chunk(const wushkv_cache* c) {
-  (void)c;
-  return false;
-}
-
 // Bytes of the split partials at the start of the decode workspace; the
 // query blocks follow.
 static uint64_t split_ws_partials(const wushkv_cache* c, int32_t n_seq) {
@@ -351,21 +344,10 @@ static uint64_t split_ws_partials(const wushkv_cache* c, int32_t n_seq) {
 
 extern "C" uint64_t wushkv_decode_workspace_bytes(const wushkv_cache* c, int32_t n_seq) {
   if (!c || n_seq < 0) return 0;
-  uint64_t b = split_ws_partials(c, n_seq) +
-               align256((uint64_t)n_seq * c->cfg.n_kv_heads *
-                        prep_words(c->cfg.n_q_heads / c->cfg.n_kv_heads) * 4);
-  if (step_as_chunk(c)) {
-    const uint64_t cb = chunk_ws_layout(n_seq, c->cfg.n_kv_heads, 8, 1).total;
-    if (cb > b) b = cb;
-  }
-  return b;
+  return split_ws_partials(c, n_seq) +
+         align256((uint64_t)n_seq * c->cfg.n_kv_heads *
+                  prep_words(c->cfg.n_q_heads / c->cfg.n_kv_heads) * 4);
 }
-
-extern "C" wushkv_status wushkv_chunk_step(wushkv_cache* c, int32_t layer, int32_t n_seq,
-                                           const int32_t* slots, const int32_t* n_new,
-                                           const void* k, const void* v, const float* tk,
-                                           const void* q, const float* tq, float* out, void* ws,
-                                           uint64_t ws_bytes, void* stream);
 
 // Shared by decode_attn and decode_step: validation of the attention
 // arguments, then the per-sequence plan and the launch.  step = 1 adds the
@@ -411,14 +393,6 @@ static wushkv_status decode_common(wushkv_cache* c, int32_t layer, int32_t n_seq
     if (noalloc_scratch(&ws, &bytes) != hipSuccess) return WUSHKV_EDEVICE;
     if (bytes < wushkv_decode_workspace_bytes(c, n_seq)) return WUSHKV_EWORKSPACE;
     ws_bytes = bytes;
-  }
-  if (step) {
-    if (step_as_chunk(c)) {
-      int32_t ones[MAXSEQ];
-      for (int i = 0; i < n_seq; ++i) ones[i] = 1;
-      return wushkv_chunk_step(c, layer, n_seq, slots, ones, k, v, tk, q, tq, out, ws, ws_bytes,
-                               stream);
-    }
   }
   DecodeArgs a;
   memset(&a, 0, sizeof(a));

@@ -1005,11 +1005,14 @@ __device__ __forceinline__ void mprocess(const MBuf<BITS>& b, int pbase, int lo,
     const float wsc = wm[t] > 0.f ? (float)W8MAX * __builtin_amdgcn_rcpf(wm[t]) : 0.f;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      int wq = (int)rintf(w[t][cb] * wsc);
-      wq = wq > W8MAX ? W8MAX : wq;
+      // wq = w wsc rounded to the nearest integer (ties to even), at most
+      // W8MAX: added to 1.5 * 2^23 in one rounding, it sits in the low bits
+      // of the float (whose bits are 0x4B400000 + wq)
+      const uint32_t rb = __float_as_uint(fminf(fmaf(w[t][cb], wsc, 12582912.f), 12582912.f + (float)W8MAX));
       // balanced digits lo = ((wq + 128) & 255) - 128, hi = (wq + 128) >> 8
-      // as two's-complement bytes: the low byte is wq & 255
-      wl[((t * 4 + grp) * 4 + cb) * 16 + eb] = (uint16_t)(((wq + 128) & 0xFF00) | (wq & 0xFF));
+      // as two's-complement bytes: the low byte is wq & 255 (the 16-bit store
+      // drops the bits above)
+      wl[((t * 4 + grp) * 4 + cb) * 16 + eb] = (uint16_t)((((rb + 128u) ^ rb) & 0xFF00u) ^ rb);
     }
   }
   wave_sync();

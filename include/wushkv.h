@@ -276,9 +276,9 @@ wushkv_status wushkv_decode_attn(wushkv_cache* cache, int32_t layer, int32_t n_s
  *   q, tq, out, ws  as in wushkv_decode_attn.
  * EUNSUPPORTED if sink + recent + flush > 1024 (the window one workgroup
  * holds); ECAPACITY if any L + 1 > ctx_cap.  Updates the host lengths on
- * success; a failing call changes nothing.  With groups of 8 query heads per
- * KV head the step runs as a one-position wushkv_chunk_step (int8 matrix
- * cores), which is faster there at every bit width.
+ * success; a failing call changes nothing.  Groups of 4 and 8 query heads
+ * per KV head score and accumulate on the int8 matrix cores inside the same
+ * launch.
  */
 wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_seq,
                                  const int32_t* slots, const void* k, const void* v,
@@ -292,8 +292,8 @@ wushkv_status wushkv_decode_step(wushkv_cache* cache, int32_t layer, int32_t n_s
  * without the workspace: the library keeps it in a file-scope device array
  * of WUSHKV_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  A
  * call whose workspace (wushkv_decode_workspace_bytes) exceeds that returns
- * WUSHKV_EWORKSPACE before any launch (e.g. the G = 8 decode step of 8
- * sequences, whose chunk-step workspace is larger).  No call allocates or
+ * WUSHKV_EWORKSPACE before any launch (e.g. a step of 8 sequences with 64
+ * query heads, whose split partials take about 17.6 MB).  No call allocates or
  * frees memory.  Every call on one GPU shares its array: calls that overlap
  * on one GPU (two streams, two threads) race and must be serialized by the
  * caller.  Nothing in the array needs to start at zero.
