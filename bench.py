@@ -834,14 +834,6 @@ def main():
     traffic = stored_traffic(w.name, args.path)
     if traffic is not None:
         traffic = int(traffic)
-    # groups of 8 query heads: the library runs decode steps as one-position
-    # chunk steps (prep, int8 matrix-core attention, merge), with no split
-    # launch; the roofline then takes the whole step per layer
-    chunk_route = fused and w.n_q == 8 * w.n_kv
-    if chunk_route:
-        split_avg_ms = ms_per_step / w.n_layers
-        achieved = bytes_per_launch / (split_avg_ms * 1e-3) / 1e9
-        traffic = None
     res = {
         "metric": "2-bit KV decode attn: cache GB/s & % HBM peak; append tokens/s",
         "value": round(value, 2),
@@ -871,17 +863,14 @@ def main():
                    "note": "one-token appends per (sequence, layer) inside the timed steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("one decode layer as chunk steps (chunk_prep_kernel, "
-                                "chunk_kernel, chunk_merge_kernel), timed as the whole step "
-                                "per layer" if chunk_route else
-                                "split_kernel (split-K scan over codes + windows"
+                     "kernel": ("split_kernel (split-K scan over codes + windows"
                                 + (", fused one-token append)" if fused else ")")),
                      "bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_ms": round(split_avg_ms, 5), "launches": n_launches,
-                     "events_avg_ms": None if chunk_route else round(m["split_ev_ms"], 5),
-                     "combine_avg_ms": None if chunk_route else round(m["comb_avg_ms"], 5),
-                     "combine_events_avg_ms": None if chunk_route else round(m["comb_ev_ms"], 5),
-                     "layers_x_split_plus_combine_ms": None if chunk_route else round(
+                     "events_avg_ms": round(m["split_ev_ms"], 5),
+                     "combine_avg_ms": round(m["comb_avg_ms"], 5),
+                     "combine_events_avg_ms": round(m["comb_ev_ms"], 5),
+                     "layers_x_split_plus_combine_ms": round(
                          w.n_layers * (split_avg_ms + m["comb_avg_ms"]), 4),
                      "timing": "HIP events around every split launch and every combine launch of "
                                f"a second timed pass of {K} steps ({round(total_b_ms / K, 4)} "
