@@ -775,10 +775,12 @@ __device__ void quant_wave(const DecodeArgs& a, const QMap& qm, int c0, int stri
 //           digit sums of head `group` at position 16 cb + m16, joined in the
 //           lane, and the 16 lanes of a row group share a head.
 //   values  A = softmax-weight digits, row 4 h + k holding digit k of head h's
-//           15-bit weight codes; B = value codes, column = dimension.  Lane
-//           (m16, group) of the result holds both digit sums of head `group`
-//           at dimension 16 db + m16.
-// Per 64 positions and four heads that is 8 + 8 matrix-core instructions;
+//           15-bit weight codes (with eight heads, rows 4 h + 2 and 4 h + 3
+//           hold those of head h of the second tile); B = value codes,
+//           column = dimension.  Lane (m16, group) of the result holds both
+//           digit sums of head `group` (of each tile) at dimension 16 db + m16.
+// Per 64 positions and four heads that is 8 + 8 matrix-core instructions (8 +
+// 8 more score and no more value instructions for the second four heads);
 // the vector work left is the code unpacking (shared by the heads), one
 // softmax per (head, position) in the lanes that hold it, and the weights'
 // transposition into the A layout through 512 bytes of LDS.
@@ -1016,15 +1018,19 @@ __device__ __forceinline__ void mprocess(const MBuf<BITS>& b, int pbase, int lo,
     }
   }
   wave_sync();
-  v4i W[NTL];
-#pragma unroll
-  for (int t = 0; t < NTL; ++t) {
-    const uint4* src = (const uint4*)(wl + ((t * 4 + (m16 >> 2)) * 4 + grp) * 16);
+  static_assert(NTL == 1 || NTL == 2, "one or two tiles of four heads");
+  // One operand for both tiles at NTL = 2: row 4 h + k holds digit k % 2 of
+  // head h of tile k / 2 (one value product per dimension block for all
+  // eight heads); at NTL = 1 rows 4 h + 2, 4 h + 3 are zero.
+  v4i W;
+  {
+    const int tsel = NTL == 2 ? (m16 >> 1) & 1 : 0;
+    const uint4* src = (const uint4*)(wl + ((tsel * 4 + (m16 >> 2)) * 4 + grp) * 16);
     const uint4 x0 = src[0], x1 = src[1];
-    W[t][0] = (int)__builtin_amdgcn_perm(x0.y, x0.x, wsel);
-    W[t][1] = (int)__builtin_amdgcn_perm(x0.w, x0.z, wsel);
-    W[t][2] = (int)__builtin_amdgcn_perm(x1.y, x1.x, wsel);
-    W[t][3] = (int)__builtin_amdgcn_perm(x1.w, x1.z, wsel);
+    W[0] = (int)__builtin_amdgcn_perm(x0.y, x0.x, wsel);
+    W[1] = (int)__builtin_amdgcn_perm(x0.w, x0.z, wsel);
+    W[2] = (int)__builtin_amdgcn_perm(x1.y, x1.x, wsel);
+    W[3] = (int)__builtin_amdgcn_perm(x1.w, x1.z, wsel);
   }
   // ---- online softmax fold and o += w c
   float back[NTL];
@@ -1049,11 +1055,10 @@ __device__ __forceinline__ void mprocess(const MBuf<BITS>& b, int pbase, int lo,
     if constexpr (BITS == 2) vb = unpack2(b.vc[db][0]);
     else if constexpr (BITS == 3) vb = unpack3(b.vc[db][0], b.vh[db], 2 * (grp & 1));
     else vb = unpack4(b.vc[db][0], b.vc[db][1]);
+    const v4i pv = mfma8(W, vb, v4i{0, 0, 0, 0});
 #pragma unroll
-    for (int t = 0; t < NTL; ++t) {
-      const v4i pv = mfma8(W[t], vb, v4i{0, 0, 0, 0});
-      O[t][db] = fmaf((float)(pv[1] * 256 + pv[0]), back[t], O[t][db]);
-    }
+    for (int t = 0; t < NTL; ++t)
+      O[t][db] = fmaf((float)(pv[2 * t + 1] * 256 + pv[2 * t]), back[t], O[t][db]);
   }
 }
 
@@ -1088,7 +1093,9 @@ __device__ void mquant_wave(const DecodeArgs& a, const QMap& qm, int c0, int c_e
                             MBuf<BITS>& B, const uint8_t* spare) {
   constexpr int MT = 64;
   const int lane = threadIdx.x & 63, m16 = lane & 15, grp = lane >> 4;
-  const int wd = m16 & 3;
+  // the byte selector of this lane's weight digit: low or high byte of four
+  // 16-bit codes (NTL = 1: rows 4 h + 2, 4 h + 3 take zeros)
+  const int wd = NTL == 2 ? m16 & 1 : m16 & 3;
   const uint32_t wsel = wd == 0 ? 0x06040200u : (wd == 1 ? 0x07050301u : 0x0C0C0C0Cu);
   float M[NTL], Lp[NTL], Zp[NTL], O[NTL][8];
 #pragma unroll
