@@ -335,9 +335,9 @@ def test_quantized_range():
 def test_decode_step_noalloc_limits():
     """The no-allocation decode step checks its arguments and the size of the
     workspace it needs against its fixed scratch before touching the device:
-    a step whose workspace exceeds the scratch (groups of 8 query heads over 8
-    sequences run as chunk steps with a larger workspace) is refused with
-    EWORKSPACE, invalid arguments with EINVAL, and lengths stay unchanged."""
+    a step whose workspace exceeds the scratch (8 sequences with 64 query
+    heads: 17.6 MB of split partials) is refused with EWORKSPACE, invalid
+    arguments with EINVAL, and lengths stay unchanged."""
     P = 1 << 41
     cfg = _cfg(n_layers=1, n_q_heads=64, n_kv_heads=8, max_batch=8, ctx_cap=1000)
     lay = wk.wushkv_layout(cfg)

@@ -699,9 +699,9 @@ def test_chunk_step_same_cache_as_append(bits):
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_step_group8(bits):
-    """Groups of 8 query heads: wushkv_decode_step runs as a one-position
-    chunk step (int8 matrix cores); steps from a prefill and from an empty
-    sequence, with flush batches."""
+    """Groups of 8 query heads: wushkv_decode_step on the split kernel's int8
+    matrix-core path (two four-head tiles sharing one value product); steps
+    from a prefill and from an empty sequence, with flush batches."""
     w = _gqa_workload(2000, G=8)
     _run_steps(w, [1500, 0], 20, bits=bits, S=4, R=32, F=4, check_every=4)
 
