@@ -507,12 +507,15 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         const float wsc = wmax[r] > 0.f ? (float)W8MAX * __builtin_amdgcn_rcpf(wmax[r]) : 0.f;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-          int wq = (int)rintf(sc[cc][r] * wsc);
-          wq = wq > W8MAX ? W8MAX : wq;
+          // wq = the weight times wsc rounded to the nearest integer (ties to
+          // even), at most W8MAX: added to 1.5 * 2^23 in one rounding, it sits
+          // in the low bits of the float (whose bits are 0x4B400000 + wq)
+          const uint32_t rb = __float_as_uint(fminf(fmaf(sc[cc][r], wsc, 12582912.f), 12582912.f + (float)W8MAX));
           // balanced digits lo = ((wq + 128) & 255) - 128, hi = (wq + 128) >> 8
-          // as two's-complement bytes: lo byte = wq & 255
+          // as two's-complement bytes: lo byte = wq & 255 (the 16-bit store
+          // drops the bits above)
           const int cbl = PAIR ? 2 * cc + half : cc;
-          wl[((4 * grp + r) + 16 * cbl) * 16 + eb] = (uint16_t)(((wq + 128) & 0xFF00) | (wq & 0xFF));
+          wl[((4 * grp + r) + 16 * cbl) * 16 + eb] = (uint16_t)((((rb + 128u) ^ rb) & 0xFF00u) ^ rb);
           if constexpr (PAIR) wl[((4 * grp + r) + 16 * (2 * cc + 1 - half)) * 16 + eb] = 0;
         }
       }
@@ -522,11 +525,12 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         const uint4* src = (const uint4*)(wl + lane * 16);
         const uint4 x0 = src[0], x1 = src[1];
         const uint32_t dw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        // low (high) bytes of the four 16-bit codes in d0, d1, in order
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t d0 = dw[2 * q], d1 = dw[2 * q + 1];
-          Wl[q] = (int)((d0 & 0xFFu) | ((d0 >> 8) & 0xFF00u) | ((d1 & 0xFFu) << 16) | ((d1 << 8) & 0xFF000000u));
-          Wh[q] = (int)(((d0 >> 8) & 0xFFu) | ((d0 >> 16) & 0xFF00u) | ((d1 & 0xFF00u) << 8) | (d1 & 0xFF000000u));
+          Wl[q] = (int)__builtin_amdgcn_perm(d1, d0, 0x06040200u);
+          Wh[q] = (int)__builtin_amdgcn_perm(d1, d0, 0x07050301u);
         }
       }
       // ---- online softmax fold and o += w c (lane, r -> row 4 grp + r, dim 16 db + m16)
