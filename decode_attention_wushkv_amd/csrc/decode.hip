@@ -203,9 +203,10 @@ struct QueryIn {
 // Issues the global loads of the compensation inputs.  Callers issue their
 // first code loads after this, so that waiting for these inputs does not wait
 // for the codes as well.
+// The raw-query part of the compensation inputs.
 template <int IO_BF16, int G>
-__device__ __forceinline__ void compensate_load(const DecodeArgs& a, int h, int si, QueryIn<G>& in) {
-  const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
+__device__ __forceinline__ void compensate_load_q(const DecodeArgs& a, int h, int si, QueryIn<G>& in) {
+  const int tid = threadIdx.x;
   const int64_t q0 = ((int64_t)si * a.g.n_q + h * G) * D;
   // (every thread loads, past the end a repeat of the last element that the
   // caller ignores: a load under a branch would be waited for at the branch
@@ -215,6 +216,12 @@ __device__ __forceinline__ void compensate_load(const DecodeArgs& a, int h, int 
     const int x = tid + 256 * n;
     in.q[n] = load_io<IO_BF16>(a.q, q0 + (x < G * D ? x : G * D - 1));
   }
+}
+
+template <int IO_BF16, int G>
+__device__ __forceinline__ void compensate_load(const DecodeArgs& a, int h, int si, QueryIn<G>& in) {
+  const int tid = threadIdx.x, i = tid & (D - 1), hf = tid >> 7;
+  compensate_load_q<IO_BF16, G>(a, h, si, in);
   const float4* tp = (const float4*)(a.tq + ((int64_t)h * D + i) * D + 64 * hf);
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
@@ -1487,10 +1494,39 @@ template <int IO_BF16, int BITS, int G>
 __global__ __launch_bounds__(256) void prep_kernel(DecodeArgs a) {
   using C = SplitCfg<BITS, G>;
   extern __shared__ uint4 smem4[];
+  // T_K^{-T} of the head, rows padded to D + 4 floats (a lane's 16-byte
+  // reads of rows i, i + 1, ... then fall in different banks)
+  constexpr int TR = D + 4;
+  __shared__ __align__(16) float tl[D * TR];
   uint32_t* sm = (uint32_t*)smem4;
-  const int h = blockIdx.x, si = blockIdx.y;
+  const int h = blockIdx.x, si = blockIdx.y, tid = threadIdx.x;
   QueryIn<G> qin;
-  compensate_load<IO_BF16, G>(a, h, si, qin);
+  // The matrix in whole 16-byte chunks, chunk x = tid + 256 c (row x / 32):
+  // every load instruction of a wave reads two whole rows (compensate_load's
+  // layout has each lane read its own row, 64 rows per instruction), then
+  // each thread takes its half row from LDS.
+  {
+    const float4* tg = (const float4*)(a.tq + (int64_t)h * D * D);
+    float4 tv[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) tv[c] = tg[tid + 256 * c];
+    compensate_load_q<IO_BF16, G>(a, h, si, qin);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int x = tid + 256 * c;
+      *(float4*)(tl + (x >> 5) * TR + 4 * (x & 31)) = tv[c];
+    }
+    __syncthreads();
+    const float* tr = tl + (tid & (D - 1)) * TR + 64 * (tid >> 7);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const float4 t4 = *(const float4*)(tr + 4 * c);
+      qin.t[4 * c] = t4.x;
+      qin.t[4 * c + 1] = t4.y;
+      qin.t[4 * c + 2] = t4.z;
+      qin.t[4 * c + 3] = t4.w;
+    }
+  }
   // (G >= 4: the split kernel's window workgroup transforms the new entry,
   // which keeps this launch's chain short)
   if (!C::HS && a.k_new) new_entry<IO_BF16, BITS, G>(a, h, si, sm);
