@@ -1549,8 +1549,8 @@ __device__ __forceinline__ int run_start(int64_t nsub, int j, int n) {
 }
 
 // Waves per SIMD the register allocation must allow: three at G = 4 with the
-// query block from the prep kernel (the matrix-core path then needs 127-167
-// registers), two otherwise (G <= 2 keeps two sub-chunks of codes and the
+// query block from the prep kernel (the matrix-core path then needs 123-168
+// registers, so four fit at 2 bits), two otherwise (G <= 2 keeps two sub-chunks of codes and the
 // query digits in registers; G = 8, and the in-workgroup query preparation
 // with two sub-chunks' loads in flight, need more than 168).
 template <int G, bool PREP>
@@ -1883,10 +1883,10 @@ hipError_t launch_split(DecodeArgs& a, hipStream_t st) {
     // workgroups with shares in proportion to the sequences' lengths keeps
     // the ragged batch balanced instead (36-layer ragged batch: 2.80 ms per
     // step with ~6x oversubscription, 2.40 with 1x).  The prep kernel
-    // prepares the query blocks of launches under 240 MB; larger ones
-    // prepare them in every workgroup, behind its first code loads (64-layer
-    // 64K batch, G = 8: 6.48 against 6.76 ms).  At least four sub-chunks (one
-    // per wave) per workgroup, at most a.n_splits per KV head.
+    // prepares the query blocks whenever the longest unit has 16 or more
+    // sub-chunks (the preparation in every workgroup, behind its first code
+    // loads, measured no faster).  At least four sub-chunks (one per wave)
+    // per workgroup, at most a.n_splits per KV head.
     prep = a.max_sub >= 16;
     const int sl = prep ? slots_p : slots;
     constexpr int MT = SplitCfg<BITS, G>::MT;
