@@ -73,13 +73,33 @@ __device__ __forceinline__ float dppf(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dppf<0xB1>(x));
-  x = fmaxf(x, dppf<0x4E>(x));
-  x = fmaxf(x, dppf<0x124>(x));
-  x = fmaxf(x, dppf<0x128>(x));
-  return x;
+// Maxima and sums over the 16 lanes of a DPP row (every lane gets the result).
+
+// Max over the 16 lanes of a DPP row of a non-negative float: its bits as an
+// unsigned integer are ordered the same, and an unsigned max (identity 0)
+// takes the DPP move into the max itself (a float max needs two more
+// operations per step to canonicalize its operand).
+__device__ __forceinline__ float row16_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  return __uint_as_float(v);
+}
+
+// Max over the 16 lanes of a DPP row of non-NaN floats (-inf included),
+// through an order-preserving signed-integer key: a negative float's bits
+// other than the sign flipped (the same map takes the key back).
+__device__ __forceinline__ float row16_max_key(float x) {
+  int v = __float_as_int(x);
+  v ^= (v >> 31) & 0x7FFFFFFF;
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  v ^= (v >> 31) & 0x7FFFFFFF;
+  return __int_as_float(v);
 }
 
 __device__ __forceinline__ float row16_sum(float x) {
@@ -483,7 +503,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
         float x = sc[0][r];
 #pragma unroll
         for (int cc = 1; cc < NC; ++cc) x = fmaxf(x, sc[cc][r]);
-        m[r] = row16_max(x);
+        m[r] = row16_max_key(x);  // scores are never NaN (masked: -inf)
         if constexpr (PAIR) m[r] = cross_max(m[r]);
         float wm = 0.f;
         lsum[r] = zsum[r] = 0.f;
@@ -495,7 +515,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkArgs a) {
           zsum[r] = fmaf(pp, vz[cc], zsum[r]);
           wm = fmaxf(wm, sc[cc][r]);
         }
-        wmax[r] = row16_max(wm);
+        wmax[r] = row16_max_nonneg(wm);  // weights are >= 0
         if constexpr (PAIR) wmax[r] = cross_max(wmax[r]);
       }
       // ---- weight codes into this wave's A operand (row, position) layout:
